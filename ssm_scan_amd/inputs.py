@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the log-linear Mamba-2 forward.
+
+This module only draws random numbers and rounds them to the storage type.
+It holds none of the method's arithmetic, so both the fp64 oracle (through
+the tests) and the HIP path consume exactly the same values.
+
+Workload shapes follow the benchmark setup of the log-linear attention
+write-up (yoousoft.com, section on the Mamba-2 / gated generalisation and
+the H100 setup paragraph): group size 2, 48 heads, head dim 64, state 128,
+chunk 64, at sequence lengths 8K, 32K and 131K.  Decay follows Mamba-2's
+per-head scalar parameterisation, log a_t = -dt_t * exp(A_log[h]).
+
+Draw order is fixed: X, B, C, log_a (A_log per head first, then the dt
+noise), lambda.  Every draw uses numpy's PCG64 ``default_rng(seed)`` in
+float32; bf16 inputs are rounded to nearest-even from those float32 draws.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Config",
+    "CONFIGS",
+    "make_inputs",
+    "bf16_round",
+    "num_levels",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    ngroups: int
+    headdim: int  # P, value dim
+    dstate: int  # N, state dim
+    chunk: int
+    nlevels: int  # L = ceil(log2 T) + 1
+    dtype: str  # "fp32" or "bf16"
+    decay: str  # "softplus" (configs 1-2) or "mamba2" (configs 3-5)
+
+    def shapes(self):
+        Bt, T, H, G, P, N, L = (self.batch, self.seqlen, self.nheads,
+                                self.ngroups, self.headdim, self.dstate,
+                                self.nlevels)
+        return dict(X=(Bt, T, H, P), B=(Bt, T, G, N), C=(Bt, T, G, N),
+                    log_a=(Bt, T, H), lam=(Bt, T, H, L), out=(Bt, T, H, P))
+
+    def replace(self, **kw) -> "Config":
+        return dataclasses.replace(self, **kw)
+
+
+def num_levels(seqlen: int) -> int:
+    """Number of Fenwick levels needed for a sequence: ceil(log2 T) + 1."""
+    return (max(seqlen, 1) - 1).bit_length() + 1
+
+
+CONFIGS = {
+    "tiny_fp32": Config("tiny_fp32", 1, 256, 1, 1, 16, 16, 16, 9, "fp32",
+                        "softplus"),
+    "t2k_bf16": Config("t2k_bf16", 2, 2048, 8, 8, 64, 64, 64, 12, "bf16",
+                       "softplus"),
+    "t8k_bf16": Config("t8k_bf16", 1, 8192, 48, 24, 64, 128, 64, 14, "bf16",
+                       "mamba2"),
+    "t32k_bf16": Config("t32k_bf16", 1, 32768, 48, 24, 64, 128, 64, 16,
+                        "bf16", "mamba2"),
+    "t131k_bf16": Config("t131k_bf16", 1, 131072, 48, 24, 64, 128, 64, 18,
+                         "bf16", "mamba2"),
+}
+
+
+def bf16_round(x: np.ndarray):
+    """Round float32 values to bfloat16, nearest-even.
+
+    Returns ``(bits, values)``: the raw uint16 bf16 bit patterns and the same
+    numbers widened back to float32 (exactly representable).  Inputs are
+    finite; no NaN handling is needed for these draws.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    bits = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    vals = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return bits, vals
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    # numerically safe softplus in float32 (a distribution shape, not the method)
+    return (np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def make_inputs(cfg: Config, seed: int = 0, *, variant: str | None = None):
+    """Draw the inputs of one configuration.
+
+    Returns a dict with float32 arrays ``X, B, C, log_a, lam`` holding the
+    exact values the kernels see (bf16-rounded for bf16 configs; log_a is
+    always float32), plus ``bits`` (uint16 arrays for the bf16 tensors, or
+    None for fp32 configs).
+
+    ``variant`` modifies the draw after the fact (the draw itself is
+    unchanged), to exercise parts of the method the default draws barely
+    reach:
+      - "slow_decay": log_a scaled by 1e-3
+      - "no_decay":   log_a = 0 (a = 1)
+      - "lam_onehot_<l>": lambda = 1 on level l, 0 elsewhere
+      - "lam_intra": lambda zero on every level above log2(chunk)
+      - "lam_inter": lambda zero on levels 0..log2(chunk)
+      - "lam_ones":  lambda = 1 everywhere
+    """
+    rng = np.random.default_rng(seed)
+    sh = cfg.shapes()
+    f32 = np.float32
+    X = rng.standard_normal(sh["X"], dtype=f32)
+    inv_sqrt_n = f32(1.0 / math.sqrt(cfg.dstate))
+    B = rng.standard_normal(sh["B"], dtype=f32) * inv_sqrt_n
+    C = rng.standard_normal(sh["C"], dtype=f32) * inv_sqrt_n
+    if cfg.decay == "softplus":
+        log_a = -f32(0.5) * _softplus(rng.standard_normal(sh["log_a"], dtype=f32))
+    elif cfg.decay == "mamba2":
+        A_log = rng.uniform(0.0, math.log(16.0), size=(cfg.nheads,)).astype(f32)
+        dt = _softplus(rng.standard_normal(sh["log_a"], dtype=f32) - f32(2.0))
+        log_a = -(dt * np.exp(A_log)[None, None, :]).astype(f32)
+    else:
+        raise ValueError(cfg.decay)
+    lam = _softplus(rng.standard_normal(sh["lam"], dtype=f32))
+
+    if variant is not None:
+        c = cfg.chunk.bit_length() - 1
+        if variant == "slow_decay":
+            log_a = (log_a * f32(1e-3)).astype(f32)
+        elif variant == "no_decay":
+            log_a = np.zeros_like(log_a)
+        elif variant.startswith("lam_onehot_"):
+            lev = int(variant.rsplit("_", 1)[1])
+            lam = np.zeros_like(lam)
+            lam[..., lev] = 1.0
+        elif variant == "lam_intra":
+            lam = lam.copy()
+            lam[..., c + 1:] = 0.0
+        elif variant == "lam_inter":
+            lam = lam.copy()
+            lam[..., :c + 1] = 0.0
+        elif variant == "lam_ones":
+            lam = np.ones_like(lam)
+        else:
+            raise ValueError(f"unknown variant {variant!r}")
+
+    out = dict(log_a=np.ascontiguousarray(log_a, dtype=f32))
+    if cfg.dtype == "bf16":
+        bits = {}
+        for k, v in (("X", X), ("B", B), ("C", C), ("lam", lam)):
+            bits[k], out[k] = bf16_round(v)
+        out["bits"] = bits
+    elif cfg.dtype == "fp32":
+        for k, v in (("X", X), ("B", B), ("C", C), ("lam", lam)):
+            out[k] = np.ascontiguousarray(v, dtype=f32)
+        out["bits"] = None
+    else:
+        raise ValueError(cfg.dtype)
+    return out
