@@ -1,0 +1,159 @@
+/*
+ * loglin.h -- C ABI of the MI355X (gfx950) log-linear Mamba-2 forward.
+ *
+ * Operation (log-linear attention write-up, yoousoft.com/industry/3746,
+ * section "special structure: tree partition", matrix form; section
+ * "log-linear generalisation of Mamba-2"): for every batch b and head h,
+ *
+ *     O = (C B^T  (.)  M^H) X,
+ *     M^H[t,s] = prod_{r=s+1..t} a_r * lambda[t, level(t,s)]  for s <= t, else 0,
+ *     level(t,s) = 0 if s == t else 1 + floor(log2(t XOR s))   (Fenwick level),
+ *
+ * with C as the query, B as the key and X as the value (state space
+ * duality section of the biyoush.com article on Transformers, RNNs and
+ * Mamba-2).  Heads share B/C in consecutive groups: group(h) = h / (H/G).
+ * No skip term, no dt scaling of X, no output gate.
+ *
+ * The work is split into chunks of `chunk` tokens (efficient training
+ * algorithm section): a dense intra-chunk block for levels 0..log2(chunk),
+ * and, for every higher level, chunk states combined by a Fenwick-ordered
+ * scan and read back by one output pass fused across levels.
+ *
+ * Layouts (all row-major, innermost dimension last, densely packed):
+ *   X      [batch, seqlen, nheads,  headdim]   io dtype
+ *   B, C   [batch, seqlen, ngroups, dstate ]   io dtype
+ *   log_a  [batch, seqlen, nheads]             float32, log of the decay a_t
+ *   lambda [batch, seqlen, nheads,  nlevels]   io dtype, weight of level l
+ *                                              for query position t
+ *   out    [batch, seqlen, nheads,  headdim]   io dtype (bf16: round to
+ *                                              nearest even from fp32)
+ * Accumulation is fp32 for both io dtypes.  Levels >= ceil(log2 seqlen)+1
+ * are ignored.
+ *
+ * Ownership: every pointer argument except `dims`/`opts` is a device
+ * pointer owned by the caller.  The library keeps no pointer after a call
+ * returns, allocates no device memory and has no global mutable state; it
+ * is safe to call from several host threads on different streams.
+ *
+ * Asynchrony: loglin_fwd only enqueues kernels on `stream` (a hipStream_t,
+ * NULL = the default stream) and returns.  Device faults surface at the
+ * caller's next synchronisation.  Results are deterministic: no atomics,
+ * repeated calls on the same inputs are bit-identical.
+ *
+ * Errors: functions returning int return LOGLIN_OK (0) or a negative
+ * LOGLIN_ERR_* code.  Every argument check runs on the host before any HIP
+ * call, so an invalid call touches no device state.
+ */
+#ifndef LOGLIN_H_
+#define LOGLIN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOGLIN_VERSION 1
+
+typedef enum {
+  LOGLIN_F32 = 0,
+  LOGLIN_BF16 = 1
+} loglin_dtype;
+
+enum {
+  LOGLIN_OK = 0,
+  LOGLIN_ERR_NULL = -1,        /* a required pointer is NULL */
+  LOGLIN_ERR_DIM = -2,         /* a dimension is <= 0 or too large */
+  LOGLIN_ERR_CHUNK = -3,       /* chunk is not 16, 32 or 64 */
+  LOGLIN_ERR_SEQ_CHUNK = -4,   /* seqlen is not a multiple of chunk */
+  LOGLIN_ERR_GROUPS = -5,      /* nheads is not a multiple of ngroups */
+  LOGLIN_ERR_LEVELS = -6,      /* nlevels < ceil(log2 seqlen) + 1 */
+  LOGLIN_ERR_DTYPE = -7,       /* io_dtype is not a loglin_dtype */
+  LOGLIN_ERR_WORKSPACE = -8,   /* workspace NULL or smaller than required */
+  LOGLIN_ERR_ALIGN = -9,       /* a pointer is not 16-byte aligned */
+  LOGLIN_ERR_SHAPE = -10,      /* (headdim, dstate) not supported */
+  LOGLIN_ERR_HIP = -11,        /* a HIP call failed */
+  LOGLIN_ERR_OPTS = -12        /* an option is out of range */
+};
+
+/* Problem sizes.  headdim = P (value dim), dstate = N (state dim),
+ * nlevels = L (weights per token and head).  Supported: headdim in
+ * {16, 32, 64}; dstate in {32, 64, 128}, plus 16 for LOGLIN_F32. */
+typedef struct {
+  int64_t batch;
+  int64_t seqlen;
+  int64_t nheads;
+  int64_t ngroups;
+  int64_t headdim;
+  int64_t dstate;
+  int64_t nlevels;
+  int32_t io_dtype; /* loglin_dtype */
+  int32_t reserved; /* must be 0 */
+} loglin_dims;
+
+/* Number of timing points loglin_fwd_ex records when opts->stage_events is
+ * set: before the chunk-state pass, before the level scan, before the
+ * output pass, and after it. */
+#define LOGLIN_NUM_STAGES 3
+
+/* Optional knobs; pass NULL for defaults. */
+typedef struct {
+  /* log2 of the chunks per segment the state pass reduces into one state;
+   * -1 lets the library choose.  0 <= seg_log2 <= log2(seqlen/chunk). */
+  int32_t seg_log2;
+  int32_t reserved; /* must be 0 */
+  /* NULL, or LOGLIN_NUM_STAGES + 1 events (hipEvent_t) recorded on
+   * `stream` at the stage boundaries, for per-pass timing. */
+  void* const* stage_events;
+} loglin_opts;
+
+/* Bytes of device workspace loglin_fwd needs for these sizes (may be 0).
+ * Returns 0 as well when the arguments are invalid; loglin_fwd then
+ * reports the error. */
+size_t loglin_workspace_bytes(const loglin_dims* dims, int chunk);
+size_t loglin_workspace_bytes_ex(const loglin_dims* dims, int chunk,
+                                 const loglin_opts* opts);
+
+/* Enqueue the forward pass.  X, B, C, log_a, lambda, out and workspace are
+ * device pointers, 16-byte aligned; `out` must not alias an input.  The
+ * workspace (at least loglin_workspace_bytes bytes, contents ignored on
+ * entry) must not be used by other work until the call's kernels finish. */
+int loglin_fwd(const void* X, const void* B, const void* C,
+               const float* log_a, const void* lambda, int chunk, void* out,
+               const loglin_dims* dims, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+int loglin_fwd_ex(const void* X, const void* B, const void* C,
+                  const float* log_a, const void* lambda, int chunk,
+                  void* out, const loglin_dims* dims, void* workspace,
+                  size_t workspace_bytes, void* stream,
+                  const loglin_opts* opts);
+
+/* Host-only argument check: the same checks loglin_fwd runs first.
+ * Pointers are only tested for NULL and alignment, never dereferenced. */
+int loglin_validate(const void* X, const void* B, const void* C,
+                    const float* log_a, const void* lambda, int chunk,
+                    const void* out, const loglin_dims* dims,
+                    const void* workspace, size_t workspace_bytes,
+                    const loglin_opts* opts);
+
+/* Static description of an error code (never NULL). */
+const char* loglin_strerror(int code);
+
+/* Segment depth (log2 chunks per segment) the library would use; negative
+ * error code on invalid arguments.  Host only. */
+int loglin_plan_seg_log2(const loglin_dims* dims, int chunk,
+                         const loglin_opts* opts);
+
+/* Event helpers for callers that time stages without linking HIP
+ * themselves.  *event receives a hipEvent_t with timing enabled. */
+int loglin_event_create(void** event);
+int loglin_event_destroy(void* event);
+int loglin_event_elapsed_ms(void* start, void* stop, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGLIN_H_ */

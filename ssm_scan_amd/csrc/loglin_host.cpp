@@ -1,0 +1,244 @@
+// Host side of the C ABI declared in include/loglin.h: argument checks,
+// workspace plan and dispatch to the (io type, chunk, P, N) instantiation.
+// Every check runs before the first HIP call.
+#include "loglin.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "loglin_launch.hpp"
+
+namespace {
+
+using loglin::Params;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_log2(int64_t x) {
+  int k = 0;
+  while ((int64_t(1) << k) < x) ++k;
+  return k;
+}
+
+bool supported_shape(int dtype, int64_t P, int64_t N) {
+  const bool p_ok = P == 16 || P == 32 || P == 64;
+  const bool n_ok = N == 32 || N == 64 || N == 128 || (dtype == LOGLIN_F32 && N == 16);
+  return p_ok && n_ok;
+}
+
+struct Plan {
+  int nc, kc, m, ns, ks, ll;
+  size_t off_state, off_decay, off_slots, off_gap, bytes;
+};
+
+int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) {
+  if (!d) return LOGLIN_ERR_NULL;
+  if (d->reserved != 0) return LOGLIN_ERR_DIM;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->ngroups <= 0 ||
+      d->headdim <= 0 || d->dstate <= 0 || d->nlevels <= 0)
+    return LOGLIN_ERR_DIM;
+  if (d->io_dtype != LOGLIN_F32 && d->io_dtype != LOGLIN_BF16) return LOGLIN_ERR_DTYPE;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return LOGLIN_ERR_CHUNK;
+  if (d->seqlen % chunk) return LOGLIN_ERR_SEQ_CHUNK;
+  if (d->nheads % d->ngroups) return LOGLIN_ERR_GROUPS;
+  // Limits of the int32 index math and of the launch grids.
+  if (d->seqlen > (int64_t(1) << 30) || d->nheads > 4096 || d->nlevels > 64 ||
+      d->batch * d->nheads > 65535)
+    return LOGLIN_ERR_DIM;
+  const int64_t nc = d->seqlen / chunk;
+  if (d->batch * nc * d->nheads > (int64_t(1) << 30)) return LOGLIN_ERR_DIM;
+  if (d->nlevels < ceil_log2(d->seqlen) + 1) return LOGLIN_ERR_LEVELS;
+  if (!supported_shape(d->io_dtype, d->headdim, d->dstate)) return LOGLIN_ERR_SHAPE;
+
+  // A chunk count that is not a power of two needs no special case: every
+  // block a chunk reads lies before it.
+  const int kc = ceil_log2(nc);
+  int m = 0;
+  if (o) {
+    if (o->reserved != 0) return LOGLIN_ERR_OPTS;
+    if (o->seg_log2 < -1) return LOGLIN_ERR_OPTS;
+    if (o->seg_log2 > 0) return LOGLIN_ERR_OPTS;  // segments of one chunk only
+    if (o->seg_log2 >= 0) m = o->seg_log2;
+  }
+  const int64_t ns = (nc + (int64_t(1) << m) - 1) >> m;
+  const int ks = ceil_log2(ns);
+  if (ks > loglin::MAX_DEPTH) return LOGLIN_ERR_DIM;
+
+  pl->nc = (int)nc;
+  pl->kc = kc;
+  pl->m = m;
+  pl->ns = (int)ns;
+  pl->ks = ks;
+  pl->ll = ceil_log2(d->seqlen) + 1;
+  const size_t bh = (size_t)(d->batch * d->nheads);
+  const size_t pn = (size_t)(d->headdim * d->dstate);
+  const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;
+  size_t off = 0;
+  if (kc > 0) {
+    pl->off_state = off;
+    off = round_up(off + bh * ns * pn * sizeof(float));
+    pl->off_decay = off;
+    off = round_up(off + bh * ns * sizeof(float));
+    pl->off_slots = off;
+    off = round_up(off + bh * ns * pn * esz);
+    pl->off_gap = off;
+    off = round_up(off + bh * ns * (ks + 1) * sizeof(float));
+  } else {
+    pl->off_state = pl->off_decay = pl->off_slots = pl->off_gap = 0;
+  }
+  pl->bytes = off;
+  return LOGLIN_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+int check_all(const void* X, const void* B, const void* C, const float* log_a,
+              const void* lambda, int chunk, const void* out, const loglin_dims* dims,
+              const void* ws, size_t ws_bytes, const loglin_opts* opts, Plan* pl) {
+  int rc = check_dims(dims, chunk, opts, pl);
+  if (rc) return rc;
+  if (!X || !B || !C || !log_a || !lambda || !out) return LOGLIN_ERR_NULL;
+  if (misaligned(X) || misaligned(B) || misaligned(C) || misaligned(log_a) ||
+      misaligned(lambda) || misaligned(out))
+    return LOGLIN_ERR_ALIGN;
+  if (pl->bytes > 0) {
+    if (!ws || ws_bytes < pl->bytes) return LOGLIN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return LOGLIN_ERR_ALIGN;
+  }
+  return LOGLIN_OK;
+}
+
+loglin::LaunchFn pick(int dtype, int chunk, int P, int N) {
+  using namespace loglin;
+  if (dtype == LOGLIN_BF16) {
+    if (chunk == 16) return lookup_bf16_16(P, N);
+    if (chunk == 32) return lookup_bf16_32(P, N);
+    if (chunk == 64) return lookup_bf16_64(P, N);
+  } else {
+    if (chunk == 16) return lookup_f32_16(P, N);
+    if (chunk == 32) return lookup_f32_32(P, N);
+    if (chunk == 64) return lookup_f32_64(P, N);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t loglin_workspace_bytes_ex(const loglin_dims* dims, int chunk, const loglin_opts* opts) {
+  Plan pl;
+  return check_dims(dims, chunk, opts, &pl) ? 0 : pl.bytes;
+}
+
+size_t loglin_workspace_bytes(const loglin_dims* dims, int chunk) {
+  return loglin_workspace_bytes_ex(dims, chunk, nullptr);
+}
+
+int loglin_plan_seg_log2(const loglin_dims* dims, int chunk, const loglin_opts* opts) {
+  Plan pl;
+  int rc = check_dims(dims, chunk, opts, &pl);
+  return rc ? rc : pl.m;
+}
+
+int loglin_validate(const void* X, const void* B, const void* C, const float* log_a,
+                    const void* lambda, int chunk, const void* out, const loglin_dims* dims,
+                    const void* workspace, size_t workspace_bytes, const loglin_opts* opts) {
+  Plan pl;
+  return check_all(X, B, C, log_a, lambda, chunk, out, dims, workspace, workspace_bytes,
+                   opts, &pl);
+}
+
+int loglin_fwd_ex(const void* X, const void* B, const void* C, const float* log_a,
+                  const void* lambda, int chunk, void* out, const loglin_dims* dims,
+                  void* workspace, size_t workspace_bytes, void* stream,
+                  const loglin_opts* opts) {
+  Plan pl;
+  int rc = check_all(X, B, C, log_a, lambda, chunk, out, dims, workspace, workspace_bytes,
+                     opts, &pl);
+  if (rc) return rc;
+  loglin::LaunchFn fn = pick(dims->io_dtype, chunk, (int)dims->headdim, (int)dims->dstate);
+  if (!fn) return LOGLIN_ERR_SHAPE;
+
+  Params pr{};
+  pr.X = X;
+  pr.Bm = B;
+  pr.Cm = C;
+  pr.log_a = log_a;
+  pr.lam = lambda;
+  pr.out = out;
+  char* ws = static_cast<char*>(workspace);
+  if (pl.bytes > 0) {
+    pr.seg_state = reinterpret_cast<float*>(ws + pl.off_state);
+    pr.seg_decay = reinterpret_cast<float*>(ws + pl.off_decay);
+    pr.slots = ws + pl.off_slots;
+    pr.gap_decay = reinterpret_cast<float*>(ws + pl.off_gap);
+  }
+  pr.batch = (int)dims->batch;
+  pr.seqlen = (int)dims->seqlen;
+  pr.nheads = (int)dims->nheads;
+  pr.ngroups = (int)dims->ngroups;
+  pr.nlevels = (int)dims->nlevels;
+  pr.nc = pl.nc;
+  pr.kc = pl.kc;
+  pr.m = pl.m;
+  pr.ns = pl.ns;
+  pr.ks = pl.ks;
+  pr.ll = pl.ll;
+  void* const* ev = opts ? opts->stage_events : nullptr;
+  int herr = fn(pr, static_cast<hipStream_t>(stream), ev);
+  return herr ? LOGLIN_ERR_HIP : LOGLIN_OK;
+}
+
+int loglin_fwd(const void* X, const void* B, const void* C, const float* log_a,
+               const void* lambda, int chunk, void* out, const loglin_dims* dims,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return loglin_fwd_ex(X, B, C, log_a, lambda, chunk, out, dims, workspace, workspace_bytes,
+                       stream, nullptr);
+}
+
+const char* loglin_strerror(int code) {
+  switch (code) {
+    case LOGLIN_OK: return "success";
+    case LOGLIN_ERR_NULL: return "a required pointer is NULL";
+    case LOGLIN_ERR_DIM: return "a dimension is non-positive or too large";
+    case LOGLIN_ERR_CHUNK: return "chunk must be 16, 32 or 64";
+    case LOGLIN_ERR_SEQ_CHUNK: return "seqlen must be a multiple of chunk";
+    case LOGLIN_ERR_GROUPS: return "nheads must be a multiple of ngroups";
+    case LOGLIN_ERR_LEVELS: return "nlevels must be at least ceil(log2 seqlen) + 1";
+    case LOGLIN_ERR_DTYPE: return "io_dtype must be LOGLIN_F32 or LOGLIN_BF16";
+    case LOGLIN_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case LOGLIN_ERR_ALIGN: return "a pointer is not 16-byte aligned (workspace: 256)";
+    case LOGLIN_ERR_SHAPE: return "unsupported (headdim, dstate) for this dtype";
+    case LOGLIN_ERR_HIP: return "a HIP launch failed";
+    case LOGLIN_ERR_OPTS: return "an option is out of range";
+    default: return "unknown error code";
+  }
+}
+
+int loglin_event_create(void** event) {
+  if (!event) return LOGLIN_ERR_NULL;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return LOGLIN_ERR_HIP;
+  *event = e;
+  return LOGLIN_OK;
+}
+
+int loglin_event_destroy(void* event) {
+  if (!event) return LOGLIN_ERR_NULL;
+  return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? LOGLIN_OK
+                                                                        : LOGLIN_ERR_HIP;
+}
+
+int loglin_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return LOGLIN_ERR_NULL;
+  return hipEventElapsedTime(ms, static_cast<hipEvent_t>(start),
+                             static_cast<hipEvent_t>(stop)) == hipSuccess
+             ? LOGLIN_OK
+             : LOGLIN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Kernel launch sequence for one (io type, chunk, P, N) instantiation.
+#pragma once
+
+#include "loglin_device.hpp"
+
+namespace loglin {
+
+using LaunchFn = int (*)(const Params&, hipStream_t, void* const*);
+
+inline int pad8(int n) { return (n + 7) & ~7; }
+
+inline void record(void* const* ev, int i, hipStream_t st) {
+  if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+}
+
+// Returns 0 or hipError_t of the first failing launch (caller maps it).
+template <class T, int C, int P, int N>
+int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
+  using Tl = Tiles<T, C, P, N>;
+  Params pr = base;
+  record(ev, 0, st);
+  if (pr.kc > 0) {
+    pr.total = pr.batch * pr.nheads * pr.ns;
+    hipLaunchKernelGGL((state_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), 0, st, pr);
+    record(ev, 1, st);
+    dim3 g2((P * N + 255) / 256, pr.batch * pr.nheads);
+    hipLaunchKernelGGL((scan_kernel<T>), g2, dim3(256), 0, st, pr, P * N);
+  } else {
+    record(ev, 1, st);
+  }
+  record(ev, 2, st);
+  pr.total = pr.batch * pr.nc * pr.nheads;
+  const size_t shm = (size_t)C * pr.ll * sizeof(float);
+  hipLaunchKernelGGL((output_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), shm, st, pr);
+  record(ev, 3, st);
+  return (int)hipGetLastError();
+}
+
+template <class T, int C>
+LaunchFn lookup(int P, int N) {
+#define LOGLIN_CASE(PP, NN) \
+  if (P == PP && N == NN) return &launch_forward<T, C, PP, NN>;
+  LOGLIN_CASE(16, 32) LOGLIN_CASE(16, 64) LOGLIN_CASE(16, 128)
+  LOGLIN_CASE(32, 32) LOGLIN_CASE(32, 64) LOGLIN_CASE(32, 128)
+  LOGLIN_CASE(64, 32) LOGLIN_CASE(64, 64) LOGLIN_CASE(64, 128)
+  if constexpr (sizeof(T) == 4) {
+    LOGLIN_CASE(16, 16) LOGLIN_CASE(32, 16) LOGLIN_CASE(64, 16)
+  }
+#undef LOGLIN_CASE
+  return nullptr;
+}
+
+// Defined in one translation unit per (io type, chunk).
+LaunchFn lookup_bf16_16(int P, int N);
+LaunchFn lookup_bf16_32(int P, int N);
+LaunchFn lookup_bf16_64(int P, int N);
+LaunchFn lookup_f32_16(int P, int N);
+LaunchFn lookup_f32_32(int P, int N);
+LaunchFn lookup_f32_64(int P, int N);
+
+}  // namespace loglin

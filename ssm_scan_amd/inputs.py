@@ -10,14 +10,18 @@ the H100 setup paragraph): group size 2, 48 heads, head dim 64, state 128,
 chunk 64, at sequence lengths 8K, 32K and 131K.  Decay follows Mamba-2's
 per-head scalar parameterisation, log a_t = -dt_t * exp(A_log[h]).
 
-Draw order is fixed: X, B, C, log_a (A_log per head first, then the dt
-noise), lambda.  Every draw uses numpy's PCG64 ``default_rng(seed)`` in
-float32; bf16 inputs are rounded to nearest-even from those float32 draws.
+Every tensor is drawn in float32 from numpy PCG64 streams, in flat blocks
+of BLOCK elements; block i of tensor k uses its own stream seeded with
+SeedSequence([seed, k, i]) (k: 0 X, 1 B, 2 C, 3 dt noise, 4 lambda, 5 A_log).
+The values therefore do not depend on how many threads fill the blocks.
+bf16 inputs are rounded to nearest-even from those float32 draws.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -74,6 +78,13 @@ CONFIGS = {
 }
 
 
+def _bf16_round_flat(x, bits, vals):
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    bits[:] = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    vals.view(np.uint32)[:] = bits.astype(np.uint32) << np.uint32(16)
+
+
 def bf16_round(x: np.ndarray):
     """Round float32 values to bfloat16, nearest-even.
 
@@ -82,11 +93,46 @@ def bf16_round(x: np.ndarray):
     finite; no NaN handling is needed for these draws.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    bits = ((u + bias) >> np.uint32(16)).astype(np.uint16)
-    vals = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
-    return bits, vals
+    flat = x.reshape(-1)
+    bits = np.empty(flat.size, dtype=np.uint16)
+    vals = np.empty(flat.size, dtype=np.float32)
+    nblk = (flat.size + BLOCK - 1) // BLOCK
+
+    def run(i):
+        sl = slice(i * BLOCK, min(flat.size, (i + 1) * BLOCK))
+        _bf16_round_flat(flat[sl], bits[sl], vals[sl])
+
+    if nblk <= 1:
+        for i in range(nblk):
+            run(i)
+    else:
+        with cf.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(run, range(nblk)))
+    return bits.reshape(x.shape), vals.reshape(x.shape)
+
+
+BLOCK = 1 << 22
+_THREADS = min(16, os.cpu_count() or 1)
+
+
+def _normal(seed: int, tensor_id: int, shape) -> np.ndarray:
+    """Standard normal float32 draws, filled block by block in threads."""
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+
+    def fill(i):
+        lo = i * BLOCK
+        hi = min(out.size, lo + BLOCK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id, i])))
+        rng.standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
+
+    nblk = (out.size + BLOCK - 1) // BLOCK
+    if nblk <= 1:
+        for i in range(nblk):
+            fill(i)
+    else:
+        with cf.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
 
 
 def _softplus(x: np.ndarray) -> np.ndarray:
@@ -112,22 +158,24 @@ def make_inputs(cfg: Config, seed: int = 0, *, variant: str | None = None):
       - "lam_inter": lambda zero on levels 0..log2(chunk)
       - "lam_ones":  lambda = 1 everywhere
     """
-    rng = np.random.default_rng(seed)
     sh = cfg.shapes()
     f32 = np.float32
-    X = rng.standard_normal(sh["X"], dtype=f32)
+    X = _normal(seed, 0, sh["X"])
     inv_sqrt_n = f32(1.0 / math.sqrt(cfg.dstate))
-    B = rng.standard_normal(sh["B"], dtype=f32) * inv_sqrt_n
-    C = rng.standard_normal(sh["C"], dtype=f32) * inv_sqrt_n
+    B = _normal(seed, 1, sh["B"])
+    B *= inv_sqrt_n
+    C = _normal(seed, 2, sh["C"])
+    C *= inv_sqrt_n
     if cfg.decay == "softplus":
-        log_a = -f32(0.5) * _softplus(rng.standard_normal(sh["log_a"], dtype=f32))
+        log_a = -f32(0.5) * _softplus(_normal(seed, 3, sh["log_a"]))
     elif cfg.decay == "mamba2":
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5, 0])))
         A_log = rng.uniform(0.0, math.log(16.0), size=(cfg.nheads,)).astype(f32)
-        dt = _softplus(rng.standard_normal(sh["log_a"], dtype=f32) - f32(2.0))
+        dt = _softplus(_normal(seed, 3, sh["log_a"]) - f32(2.0))
         log_a = -(dt * np.exp(A_log)[None, None, :]).astype(f32)
     else:
         raise ValueError(cfg.decay)
-    lam = _softplus(rng.standard_normal(sh["lam"], dtype=f32))
+    lam = _softplus(_normal(seed, 4, sh["lam"]))
 
     if variant is not None:
         c = cfg.chunk.bit_length() - 1

@@ -1,0 +1,129 @@
+"""C ABI of libloglin.so on the CPU: the library loads, exports every
+function include/loglin.h declares, and every argument check fires on the
+host.  No test here reaches a HIP call: each call is invalid on purpose and
+the library validates before touching the device, or only plans."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ssm_scan_amd import loglin as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loglin.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libloglin.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loglin_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert "loglin_fwd" in names and "loglin_workspace_bytes" in names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def good_dims(**kw):
+    d = dict(batch=1, seqlen=32768, nheads=48, ngroups=24, headdim=64, dstate=128,
+             nlevels=16, io_dtype=L.LOGLIN_BF16)
+    d.update(kw)
+    return L.make_dims(**d)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation
+
+
+def validate(dims, chunk=64, ws_bytes=None, ptrs=None, opts=None, ws=FAKE):
+    p = dict(X=FAKE, B=FAKE, C=FAKE, log_a=FAKE, lam=FAKE, out=FAKE)
+    p.update(ptrs or {})
+    need = L.loglin_workspace_bytes(dims, chunk) if ws_bytes is None else ws_bytes
+    o = ctypes.byref(opts) if opts is not None else None
+    return L.lib().loglin_validate(p["X"], p["B"], p["C"], p["log_a"], p["lam"], chunk,
+                                   p["out"], ctypes.byref(dims), ws, need, o)
+
+
+def test_valid_arguments_pass_validation():
+    assert validate(good_dims()) == 0
+    assert validate(good_dims(io_dtype=L.LOGLIN_F32, seqlen=256, nheads=1, ngroups=1,
+                              headdim=16, dstate=16, nlevels=9), chunk=16) == 0
+
+
+@pytest.mark.parametrize("kw,chunk,code", [
+    (dict(batch=0), 64, -2), (dict(seqlen=-64), 64, -2), (dict(nheads=0), 64, -2),
+    (dict(headdim=0), 64, -2), (dict(nlevels=0), 64, -2),
+    (dict(), 48, -3), (dict(), 128, -3), (dict(), 0, -3),
+    (dict(seqlen=32768 + 16), 64, -4),
+    (dict(ngroups=5), 64, -5),
+    (dict(nlevels=15), 64, -6),
+    (dict(io_dtype=7), 64, -7),
+    (dict(headdim=48), 64, -10), (dict(dstate=96), 64, -10),
+    (dict(dstate=16), 64, -10),
+])
+def test_dimension_errors(kw, chunk, code):
+    assert validate(good_dims(**kw), chunk=chunk, ws_bytes=1 << 40) == code
+    assert L.loglin_strerror(code) != "unknown error code"
+
+
+@pytest.mark.parametrize("name", ["X", "B", "C", "log_a", "lam", "out"])
+def test_null_and_misaligned_pointers(name):
+    assert validate(good_dims(), ptrs={name: None}) == -1
+    assert validate(good_dims(), ptrs={name: FAKE + 8}) == -9
+
+
+def test_workspace_errors():
+    d = good_dims()
+    need = L.loglin_workspace_bytes(d, 64)
+    assert need > 0
+    assert validate(d, ws_bytes=need - 1) == -8
+    assert validate(d, ws=None) == -8
+    assert validate(d, ws=FAKE + 16) == -9
+
+
+def test_options_errors():
+    o = L.loglin_opts()
+    o.seg_log2, o.reserved = -2, 0
+    assert validate(good_dims(), opts=o) == -12
+    o.seg_log2, o.reserved = 0, 1
+    assert validate(good_dims(), opts=o) == -12
+
+
+def test_null_dims():
+    assert L.lib().loglin_validate(FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, FAKE,
+                                   1 << 40, None) == -1
+    assert L.lib().loglin_workspace_bytes(None, 64) == 0
+
+
+def test_fwd_rejects_before_any_device_call():
+    """loglin_fwd runs the same checks first: an invalid call returns its
+    code without a HIP call (this container has no GPU)."""
+    d = good_dims(nlevels=3)
+    rc = L.lib().loglin_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, ctypes.byref(d),
+                            FAKE, 1 << 40, None)
+    assert rc == -6
+
+
+def test_workspace_size_formula():
+    """Workspace: fp32 segment states + io-typed slots per (batch, head,
+    segment), plus small decay arrays; zero when there is a single chunk."""
+    d = good_dims()
+    need = L.loglin_workspace_bytes(d, 64)
+    ns = 32768 // 64
+    core = 48 * ns * 64 * 128 * (4 + 2)
+    assert core <= need <= core + 48 * ns * 4 * 32 + 4 * 256
+    assert L.loglin_workspace_bytes(good_dims(seqlen=64, nlevels=7), 64) == 0
+    assert L.loglin_plan_seg_log2(d, 64) == 0
+
+
+def test_strerror_all_codes():
+    for code in L.ERRORS:
+        assert isinstance(L.loglin_strerror(code), str)
+    assert L.loglin_strerror(-99) == "unknown error code"

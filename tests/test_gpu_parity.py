@@ -1,0 +1,140 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Sizes here are ones the oracle finishes in seconds while spanning several
+chunks, a ragged number of chunks and every level.  Full-size workloads are
+in test_gpu_full.py.  Bar: max relative error (per batch-head slice, max
+|out - ref| / max |ref|) <= 2e-2 for bf16 inputs, <= 1e-4 for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import loglin_ref
+from ssm_scan_amd import inputs
+
+from .gpu_helpers import (max_rel_err, run_gpu, say, small_cfg, to_device, tol_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def check(cfg, seed=0, variant=None, chunk=None, seg_log2=None):
+    say(f"[parity] {cfg.name} seed={seed} variant={variant} chunk={chunk} seg={seg_log2}")
+    d = inputs.make_inputs(cfg, seed, variant=variant)
+    t = to_device(d, cfg)
+    out = run_gpu(cfg, t, chunk=chunk, seg_log2=seg_log2)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"])
+    err = max_rel_err(got, ref)
+    say(f"         max_rel_err={err:.3e} (tol {tol_of(cfg):.0e})")
+    assert np.isfinite(got).all()
+    assert err <= tol_of(cfg), err
+    return got, ref
+
+
+def test_tiny_fp32_config():
+    """256 tokens, 1 head, P=N=16, chunk 16, fp32 (1e-4 bar)."""
+    check(inputs.CONFIGS["tiny_fp32"])
+
+
+def test_t2k_bf16_config():
+    """2 x 2048 tokens, 8 heads, P=N=64, chunk 64, bf16."""
+    check(inputs.CONFIGS["t2k_bf16"])
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_t2k_bf16_other_seeds(seed):
+    cfg = inputs.CONFIGS["t2k_bf16"].replace(batch=1, nheads=4, ngroups=4)
+    check(cfg, seed=seed)
+
+
+@pytest.mark.parametrize("T", [64, 128, 320, 1344, 2048])
+def test_headline_shape_lengths(T):
+    """Headline head shape (P=64, N=128, groups of 2), Mamba-2 decay; T=64 is
+    one chunk (no inter levels, no workspace); 320 and 1344 are ragged chunk
+    counts (5, 21)."""
+    check(small_cfg(T=T))
+
+
+@pytest.mark.parametrize("dtype,P,N,C", [
+    ("bf16", 16, 32, 16), ("bf16", 32, 64, 32), ("bf16", 64, 32, 64),
+    ("bf16", 16, 128, 32), ("fp32", 16, 16, 16), ("fp32", 64, 128, 64),
+    ("fp32", 32, 64, 32), ("fp32", 64, 16, 16),
+])
+def test_shapes_and_chunks(dtype, P, N, C):
+    check(small_cfg(dtype=dtype, T=C * 11, H=2, G=1, P=P, N=N, C=C, decay="softplus"))
+
+
+def test_batch_gt_one():
+    check(small_cfg(T=512, H=4, G=2, Bt=3))
+
+
+@pytest.mark.parametrize("variant", ["slow_decay", "no_decay", "lam_intra", "lam_inter",
+                                     "lam_ones"])
+def test_variants(variant):
+    """Slow / no decay reach the deep levels; lambda zeroed on inter (or
+    intra) levels isolates the intra-chunk kernel (or the inter path)."""
+    check(small_cfg(T=1024, H=2, G=1), variant=variant)
+
+
+@pytest.mark.parametrize("level", range(0, 12))
+def test_onehot_levels(level):
+    """lambda one-hot on each level: every Fenwick level in isolation
+    (levels 0..6 intra-chunk, 7..11 inter-chunk at chunk 64, T = 2048)."""
+    check(small_cfg(T=2048, H=2, G=1), variant=f"lam_onehot_{level}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_invariance(chunk):
+    """The result does not depend on the chunk size (up to rounding)."""
+    check(small_cfg(T=1024, H=2, G=1), chunk=chunk, variant="slow_decay")
+
+
+def test_fp32_chunk_invariance_tight():
+    cfg = small_cfg(dtype="fp32", T=512, H=2, G=1, P=32, N=32, C=16, decay="softplus")
+    d = inputs.make_inputs(cfg, 3, variant="slow_decay")
+    t = to_device(d, cfg)
+    outs = [run_gpu(cfg, t, chunk=c).cpu().numpy() for c in (16, 32, 64)]
+    ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"])
+    for o in outs:
+        assert max_rel_err(o, ref) <= 1e-4
+
+
+def test_determinism():
+    """Two runs on the same inputs are bit-identical (no atomics)."""
+    cfg = small_cfg(T=2048, H=4, G=2)
+    d = inputs.make_inputs(cfg, 0)
+    t = to_device(d, cfg)
+    a = run_gpu(cfg, t).clone()
+    b = run_gpu(cfg, t).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_causality():
+    """Perturbing tokens >= t0 leaves every output row < t0 bit-identical."""
+    cfg = small_cfg(T=1024, H=2, G=1)
+    d = inputs.make_inputs(cfg, 0)
+    t = to_device(d, cfg)
+    a = run_gpu(cfg, t).clone()
+    t0 = 700
+    for k in ("X", "B", "C", "lam"):
+        t[k][:, t0:] = t[k][:, t0:] * 2 + 1
+    t["log_a"][:, t0:] -= 0.3
+    b = run_gpu(cfg, t)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :t0], b[:, :t0])
+    assert not torch.equal(a[:, t0:], b[:, t0:])
+
+
+def test_extra_levels_ignored():
+    """lambda with more levels than ceil(log2 T) + 1: extra ones unused."""
+    cfg = small_cfg(T=512, H=2, G=1)
+    d = inputs.make_inputs(cfg, 0)
+    t = to_device(d, cfg)
+    a = run_gpu(cfg, t).clone()
+    lam2 = torch.cat([t["lam"], torch.full_like(t["lam"][..., :3], 7.0)], dim=-1).contiguous()
+    t2 = dict(t, lam=lam2)
+    b = run_gpu(cfg, t2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
