@@ -99,8 +99,10 @@ typedef struct {
 
 /* Optional knobs; pass NULL for defaults. */
 typedef struct {
-  /* log2 of the chunks per segment the state pass reduces into one state;
-   * -1 lets the library choose.  0 <= seg_log2 <= log2(seqlen/chunk). */
+  /* log2 of the chunks per segment: the state pass reduces each segment to
+   * one state and the output pass keeps the levels inside a segment on
+   * chip.  -1 lets the library choose (min(3, ceil(log2(seqlen/chunk)))).
+   * Valid: 0 <= seg_log2 <= min(3, ceil(log2(seqlen/chunk))). */
   int32_t seg_log2;
   int32_t reserved; /* must be 0 */
   /* NULL, or LOGLIN_NUM_STAGES + 1 events (hipEvent_t) recorded on

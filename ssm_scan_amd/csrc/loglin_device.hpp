@@ -86,6 +86,10 @@ struct Mfma<bf16> {
   __host__ __device__ static constexpr int state_pos(int n) {
     return 32 * (n >> 5) + 8 * ((n & 15) >> 2) + 4 * ((n & 31) >> 4) + (n & 3);
   }
+  // Fragment element (kk, j) of a lane is row state_row(kk, g, j) = element
+  // s_i of 16-row tile s_nb of the state MFMA result held by the same lane.
+  __host__ __device__ static constexpr int s_nb(int kk, int j) { return 2 * kk + (j >> 2); }
+  __host__ __device__ static constexpr int s_i(int, int j) { return j & 3; }
   __device__ static inline float ex(float x) { return __expf(x); }
 };
 
@@ -103,6 +107,8 @@ struct Mfma<float> {
   __host__ __device__ static constexpr int state_pos(int n) {
     return 16 * (n >> 4) + 4 * (n & 3) + ((n & 15) >> 2);
   }
+  __host__ __device__ static constexpr int s_nb(int kk, int) { return kk >> 2; }
+  __host__ __device__ static constexpr int s_i(int kk, int) { return kk & 3; }
   __device__ static inline float ex(float x) { return expf(x); }
 };
 
@@ -120,6 +126,19 @@ struct alignas(16) Vec16 {
   static constexpr int n = 16 / sizeof(T);
   T e[n];
 };
+
+template <class T>
+__device__ inline T frag_elem(const typename Mfma<T>::frag& f, int j);
+template <>
+__device__ inline bf16 frag_elem<bf16>(const bf16x8& f, int j) { return f[j]; }
+template <>
+__device__ inline float frag_elem<float>(const float& f, int) { return f; }
+template <class T>
+__device__ inline void set_frag_elem(typename Mfma<T>::frag& f, int j, T v);
+template <>
+__device__ inline void set_frag_elem<bf16>(bf16x8& f, int j, bf16 v) { f[j] = v; }
+template <>
+__device__ inline void set_frag_elem<float>(float& f, int, float v) { f = v; }
 
 template <class T>
 __device__ inline typename Mfma<T>::frag load_frag(const T* p) {
@@ -320,39 +339,74 @@ __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
   float stk[MAX_DEPTH], stka[MAX_DEPTH];
 #pragma unroll
   for (int i = 0; i < MAX_DEPTH; ++i) stk[i] = stka[i] = 0.f;
-  for (int q = 0; q + 1 < pr.ns; ++q) {
-    float v = valid ? src[(int64_t)q * pn + e] : 0.f;
-    float acur = dec[q];
-    const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q
+  constexpr int U = 8;  // segments whose loads are in flight together
+  const int nq = pr.ns - 1;  // the last segment is never read
+  for (int q0 = 0; q0 < nq; q0 += U) {
+    float vb[U], db[U];
 #pragma unroll
-    for (int i = 0; i < MAX_DEPTH; ++i) {
-      if (i < z) {
-        v = M::ex(acur) * stk[i] + v;
-        acur += stka[i];
-      }
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u;
+      vb[u] = (valid && q < nq) ? src[(int64_t)q * pn + e] : 0.f;
+      db[u] = q < nq ? dec[q] : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < MAX_DEPTH; ++i) {
-      if (i == z) {
-        stk[i] = v;
-        stka[i] = acur;
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u;
+      if (q >= nq) break;
+      float v = vb[u];
+      float acur = db[u];
+      const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q
+#pragma unroll
+      for (int i = 0; i < MAX_DEPTH; ++i) {
+        if (i < z) {
+          v = M::ex(acur) * stk[i] + v;
+          acur += stka[i];
+        }
       }
+#pragma unroll
+      for (int i = 0; i < MAX_DEPTH; ++i) {
+        if (i == z) {
+          stk[i] = v;
+          stka[i] = acur;
+        }
+      }
+      if (valid) dst[(int64_t)q * pn + e] = from_f<T>(v);
     }
-    if (valid) dst[(int64_t)q * pn + e] = from_f<T>(v);
   }
 }
 
 // ------------------------------------------------------------- pass 3
 
-// One work-group per (batch, chunk, head); wave w owns output columns
-// [16w, 16w+16) of the head and all C tokens of the chunk, as TB tiles of
-// Y^T (16 values of P by 16 tokens).
+// Largest segment depth m (chunks per segment 2^m) the output pass keeps a
+// register stack for.
+constexpr int MAX_SEG_LOG2 = 3;
+
+// One work-group per (batch, segment of 2^m chunks, head); the chunks of the
+// segment are processed in order.  Wave w owns output columns [16w, 16w+16)
+// of the head for all C tokens of a chunk (TB tiles of Y^T), and the same
+// columns of every chunk state it builds.
+//
+// Inter-chunk level k of chunk j reads the lower half of j's 2^k-chunk
+// block.  For k > m that block is a run of whole segments: its sum is slot
+// ((q >> ks) << ks) + 2^(ks-1) - 1 of pass 2 (ks = k - m), shared by every
+// chunk of the segment.  For k <= m it lies inside the segment: the wave
+// keeps a Fenwick stack of those block sums, entry e holding the block of
+// 2^e chunks that ends just before the current chunk, as MFMA A-operand
+// fragments.  The state MFMA leaves a lane exactly the rows its own
+// fragments need, so the stack never crosses lanes.
 template <class T, int C, int P, int N>
-__global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void output_kernel(Params pr) {
+__global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Params pr) {
   using Tl = Tiles<T, C, P, N>;
   using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int RS = N + Tl::VEC;  // row stride of the staged B and C rows
+  constexpr int NBU = C * N / Tl::VEC;  // 16-byte units of a chunk of B or C
+  constexpr int MM = MAX_SEG_LOG2;
   __shared__ __attribute__((aligned(16))) T xt[P * Tl::XS];
   __shared__ __attribute__((aligned(16))) T wt[C * Tl::XS];
+  __shared__ __attribute__((aligned(16))) T bsh[C * RS];  // B rows
+  __shared__ __attribute__((aligned(16))) T csh[C * RS];  // C rows
+  __shared__ __attribute__((aligned(16))) T bwt[N * Tl::XS];  // (B w)^T
   __shared__ float cum[C];
   extern __shared__ float lam_s[];  // [C][ll]
 
@@ -362,99 +416,203 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void output_kernel(Params 
   const int g = lane >> 4, r = lane & 15;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels, LL = pr.ll;
   const int h = tile % H;
-  const int j = (tile / H) % pr.nc;
-  const int b = tile / (H * pr.nc);
+  const int q = (tile / H) % pr.ns;
+  const int b = tile / (H * pr.ns);
   const int grp = h / (H / G);
   const int bh = b * H + h;
   const int c_log = __builtin_ctz(C);
+  const int m = pr.m;
+  const int seg = 1 << m;
+  const int j0 = q * seg;
+  const int nch = min(seg, pr.nc - j0);
   const T* X = static_cast<const T*>(pr.X);
   const T* Bm = static_cast<const T*>(pr.Bm);
   const T* Cm = static_cast<const T*>(pr.Cm);
   const T* lam = static_cast<const T*>(pr.lam);
-  const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+  const T* slots = static_cast<const T*>(pr.slots);
+  T* out = static_cast<T*>(pr.out);
 
-  if (Tl::KC > C) {
-    for (int idx = tid; idx < (C + P) * (Tl::KC - C); idx += Tl::NT) {
+  if (Tl::KC > C) {  // contraction padding of X^T, W and (B w)^T stays zero
+    for (int idx = tid; idx < (C + P + N) * (Tl::KC - C); idx += Tl::NT) {
       int row = idx / (Tl::KC - C), col = C + idx % (Tl::KC - C);
       if (row < C) wt[row * Tl::XS + col] = from_f<T>(0.f);
-      else xt[(row - C) * Tl::XS + col] = from_f<T>(0.f);
+      else if (row < C + P) xt[(row - C) * Tl::XS + col] = from_f<T>(0.f);
+      else bwt[(row - C - P) * Tl::XS + col] = from_f<T>(0.f);
     }
   }
-  chunk_cumsum<C>(pr.log_a, cum, row0, H, h, tid);
-  for (int idx = tid; idx < C * LL; idx += Tl::NT) {
-    int tau = idx / LL, l = idx - tau * LL;
-    lam_s[idx] = to_f(lam[((row0 + tau) * H + h) * L + l]);
-  }
-  load_xt<T, C, P, N>(X, xt, row0, H, h, tid);
-  __syncthreads();
 
-  // Intra-chunk weights W[t][s] = (C_t . B_s) exp(cum_t - cum_s) lambda[t,
-  // bitlen(t^s)] for s <= t, from the transposed scores C B^T computed as
-  // B C^T so that each lane holds 4 consecutive s of one t.
-  for (int u = wave; u < Tl::TB * Tl::TB; u += Tl::NW) {
-    const int tb = u / Tl::TB, sb = u - tb * Tl::TB;
-    const int t = 16 * tb + r;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (sb <= tb) {
-      const T* brow = Bm + ((row0 + 16 * sb + r) * G + grp) * N + g * Tl::KPL;
-      const T* crow = Cm + ((row0 + t) * G + grp) * N + g * Tl::KPL;
+  frag zl[MM][Tl::NKN];  // local Fenwick stack (entry e: 2^e chunks)
+  float zla[MM];         // total log-decay of each entry's block
+  float dloc[MM + 1];    // log-decay from a local block's end to the chunk
 #pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk)
-        acc = M::mma(load_frag<T>(brow + kk * Tl::KB), load_frag<T>(crow + kk * Tl::KB), acc);
-    }
-    f32x4 wv;
+  for (int e = 0; e < MM; ++e) zla[e] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 16 * sb + 4 * g + i;
-      wv[i] = (s <= t) ? acc[i] * M::ex(cum[t] - cum[s]) * lam_s[t * LL + bit_length(t ^ s)]
-                       : 0.f;
-    }
-    store4(wt + t * Tl::XS + 16 * sb + 4 * g, wv);
-  }
-  __syncthreads();
+  for (int k = 0; k <= MM; ++k) dloc[k] = 0.f;
+  float accseg = 0.f;  // log-decay from the segment start to the chunk
+  const float* gap = pr.ks > 0 ? pr.gap_decay + ((int64_t)bh * pr.ns + q) * (pr.ks + 1) : nullptr;
 
-  f32x4 Y[Tl::TB];
+  for (int jl = 0; jl < nch; ++jl) {
+    const int j = j0 + jl;
+    const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    const bool need_state = jl + 1 < nch;
+
+    // ---- stage the chunk: cumulative log-decay, lambda, X^T, B and C rows
+    chunk_cumsum<C>(pr.log_a, cum, row0, H, h, tid);
+    for (int idx = tid; idx < C * LL; idx += Tl::NT) {
+      int tau = idx / LL, l = idx - tau * LL;
+      lam_s[idx] = to_f(lam[((row0 + tau) * H + h) * L + l]);
+    }
+    load_xt<T, C, P, N>(X, xt, row0, H, h, tid);
+    constexpr int NV = N / Tl::VEC;
+    for (int idx = tid; idx < NBU; idx += Tl::NT) {
+      const int tau = idx / NV, nv = idx - tau * NV;
+      const int64_t go = ((row0 + tau) * G + grp) * N + nv * Tl::VEC;
+      *reinterpret_cast<Vec16<T>*>(bsh + tau * RS + nv * Tl::VEC) =
+          *reinterpret_cast<const Vec16<T>*>(Bm + go);
+      *reinterpret_cast<Vec16<T>*>(csh + tau * RS + nv * Tl::VEC) =
+          *reinterpret_cast<const Vec16<T>*>(Cm + go);
+    }
+    __syncthreads();
+    const float atot = cum[C - 1];
+
+    // ---- (B w)^T for this chunk's state, w_s = exp(atot - cum_s)
+    if (need_state) {
+      for (int idx = tid; idx < NBU; idx += Tl::NT) {
+        const int tau = idx / NV, nv = idx - tau * NV;
+        const Vec16<T> v = *reinterpret_cast<const Vec16<T>*>(bsh + tau * RS + nv * Tl::VEC);
+        const float w = M::ex(atot - cum[tau]);
 #pragma unroll
-  for (int tb = 0; tb < Tl::TB; ++tb) {
-    Y[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < Tl::NKT; ++kt) {
-      if (kt * Tl::KB < 16 * (tb + 1)) {
-        auto af = load_frag<T>(xt + (16 * wave + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-        auto bf = load_frag<T>(wt + (16 * tb + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-        Y[tb] = M::mma(af, bf, Y[tb]);
+        for (int e = 0; e < Tl::VEC; ++e)
+          bwt[(nv * Tl::VEC + e) * Tl::XS + tau] = from_f<T>(to_f(v.e[e]) * w);
       }
     }
-  }
 
-  // Inter-chunk levels: level c_log + k is active for chunk j when bit k-1
-  // of j is set; its source is the lower half of j's 2^k-chunk block.
-  const T* slots = static_cast<const T*>(pr.slots);
-  for (int k = 1; k <= pr.kc; ++k) {
-    if (!((j >> (k - 1)) & 1)) continue;
-    const int qk = ((j >> k) << k) + (1 << (k - 1)) - 1;
-    const float D = pr.gap_decay[((int64_t)bh * pr.ns + j) * (pr.ks + 1) + k];
-    const T* zrow = slots + (((int64_t)bh * pr.ns + qk) * P + 16 * wave + r) * N + g * Tl::KPL;
-    typename M::frag zf[Tl::NKN];
+    // ---- intra-chunk weights W[t][s], from the transposed scores B C^T
+    for (int u = wave; u < Tl::TB * Tl::TB; u += Tl::NW) {
+      const int tb = u / Tl::TB, sb = u - tb * Tl::TB;
+      const int t = 16 * tb + r;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (sb <= tb) {
+        const T* brow = bsh + (16 * sb + r) * RS + g * Tl::KPL;
+        const T* crow = csh + t * RS + g * Tl::KPL;
 #pragma unroll
-    for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = load_frag<T>(zrow + kk * Tl::KB);
+        for (int kk = 0; kk < Tl::NKN; ++kk)
+          acc = M::mma(load_frag<T>(brow + kk * Tl::KB), load_frag<T>(crow + kk * Tl::KB), acc);
+      }
+      f32x4 wv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * sb + 4 * g + i;
+        wv[i] = (s <= t) ? acc[i] * M::ex(cum[t] - cum[s]) * lam_s[t * LL + bit_length(t ^ s)]
+                         : 0.f;
+      }
+      store4(wt + t * Tl::XS + 16 * sb + 4 * g, wv);
+    }
+    __syncthreads();
+
+    // ---- output tiles: intra block, then every active inter-chunk level
+    f32x4 Y[Tl::TB];
+#pragma unroll
+    for (int tb = 0; tb < Tl::TB; ++tb) {
+      Y[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < Tl::NKT; ++kt) {
+        if (kt * Tl::KB < 16 * (tb + 1)) {
+          auto af = load_frag<T>(xt + (16 * wave + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
+          auto bf = load_frag<T>(wt + (16 * tb + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
+          Y[tb] = M::mma(af, bf, Y[tb]);
+        }
+      }
+    }
+    frag cf[Tl::TB][Tl::NKN];  // C^T fragments in state order
+#pragma unroll
+    for (int tb = 0; tb < Tl::TB; ++tb)
+#pragma unroll
+      for (int kk = 0; kk < Tl::NKN; ++kk)
+        cf[tb][kk] = load_state_frag(csh + (16 * tb + r) * RS, kk, g);
+
+    auto add_level = [&](const frag* zf, int level, float D) {
+#pragma unroll
+      for (int tb = 0; tb < Tl::TB; ++tb) {
+        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[tb][kk], tmp);
+        const int t = 16 * tb + r;
+        const float sc = lam_s[t * LL + level] * M::ex(cum[t] + D);
+        Y[tb] += sc * tmp;
+      }
+    };
+
+    for (int ks = 1; ks <= pr.ks; ++ks) {  // levels above the segment
+      if (!((q >> (ks - 1)) & 1)) continue;
+      const int qs = ((q >> ks) << ks) + (1 << (ks - 1)) - 1;
+      const T* zrow = slots + (((int64_t)bh * pr.ns + qs) * P + 16 * wave + r) * N + g * Tl::KPL;
+      frag zf[Tl::NKN];
+#pragma unroll
+      for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = load_frag<T>(zrow + kk * Tl::KB);
+      add_level(zf, c_log + m + ks, gap[ks] + accseg);
+    }
+#pragma unroll
+    for (int e = 0; e < MM; ++e) {  // levels inside the segment
+      if (e < m && ((jl >> e) & 1)) add_level(zl[e], c_log + e + 1, dloc[e + 1]);
+    }
+
 #pragma unroll
     for (int tb = 0; tb < Tl::TB; ++tb) {
       const int t = 16 * tb + r;
-      const T* crow = Cm + ((row0 + t) * G + grp) * N;
-      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], load_state_frag(crow, kk, g), tmp);
-      const float sc = lam_s[t * LL + c_log + k] * M::ex(cum[t] + D);
-      Y[tb] += sc * tmp;
+      store4(out + ((row0 + t) * H + h) * P + 16 * wave + 4 * g, Y[tb]);
     }
-  }
 
-  T* out = static_cast<T*>(pr.out);
+    // ---- this chunk's state, pushed on the local Fenwick stack
+    if (need_state) {
+      f32x4 S[Tl::NB];
 #pragma unroll
-  for (int tb = 0; tb < Tl::TB; ++tb) {
-    const int t = 16 * tb + r;
-    store4(out + ((row0 + t) * H + h) * P + 16 * wave + 4 * g, Y[tb]);
+      for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < Tl::NKT; ++kt) {
+        auto bf = load_frag<T>(xt + (16 * wave + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
+#pragma unroll
+        for (int nb = 0; nb < Tl::NB; ++nb) {
+          auto af = load_frag<T>(bwt + (16 * nb + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
+          S[nb] = M::mma(af, bf, S[nb]);
+        }
+      }
+      // merge with the entries of the blocks this chunk completes
+      const int z = __builtin_ctz(~(unsigned)jl);  // trailing ones of jl
+      float cur_a = atot;
+#pragma unroll
+      for (int e = 0; e < MM; ++e) {
+        if (e < z) {
+          const float dec = M::ex(cur_a);
+#pragma unroll
+          for (int kk = 0; kk < Tl::NKN; ++kk)
+#pragma unroll
+            for (int jj = 0; jj < Tl::KPL; ++jj)
+              S[M::s_nb(kk, jj)][M::s_i(kk, jj)] += dec * to_f(frag_elem<T>(zl[e][kk], jj));
+          cur_a += zla[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < MM; ++e) {
+        if (e == z) {
+#pragma unroll
+          for (int kk = 0; kk < Tl::NKN; ++kk)
+#pragma unroll
+            for (int jj = 0; jj < Tl::KPL; ++jj)
+              set_frag_elem<T>(zl[e][kk], jj, from_f<T>(S[M::s_nb(kk, jj)][M::s_i(kk, jj)]));
+          zla[e] = cur_a;
+        }
+      }
+    }
+
+    // ---- running log-decays for the next chunk
+    accseg += atot;
+#pragma unroll
+    for (int k = 1; k <= MM; ++k) {
+      dloc[k] += atot;
+      if (((jl + 1) & ((1 << (k - 1)) - 1)) == 0) dloc[k] = 0.f;
+    }
+    __syncthreads();  // LDS is restaged by the next chunk
   }
 }
 

@@ -56,11 +56,11 @@ int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) 
   // A chunk count that is not a power of two needs no special case: every
   // block a chunk reads lies before it.
   const int kc = ceil_log2(nc);
-  int m = 0;
+  int m = kc < loglin::MAX_SEG_LOG2 ? kc : loglin::MAX_SEG_LOG2;
   if (o) {
     if (o->reserved != 0) return LOGLIN_ERR_OPTS;
-    if (o->seg_log2 < -1) return LOGLIN_ERR_OPTS;
-    if (o->seg_log2 > 0) return LOGLIN_ERR_OPTS;  // segments of one chunk only
+    if (o->seg_log2 < -1 || o->seg_log2 > loglin::MAX_SEG_LOG2) return LOGLIN_ERR_OPTS;
+    if (o->seg_log2 > kc) return LOGLIN_ERR_OPTS;
     if (o->seg_log2 >= 0) m = o->seg_log2;
   }
   const int64_t ns = (nc + (int64_t(1) << m) - 1) >> m;
@@ -77,7 +77,7 @@ int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) 
   const size_t pn = (size_t)(d->headdim * d->dstate);
   const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;
   size_t off = 0;
-  if (kc > 0) {
+  if (ns > 1) {  // levels above one segment exist
     pl->off_state = off;
     off = round_up(off + bh * ns * pn * sizeof(float));
     pl->off_decay = off;

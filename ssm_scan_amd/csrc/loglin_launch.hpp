@@ -19,7 +19,7 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   using Tl = Tiles<T, C, P, N>;
   Params pr = base;
   record(ev, 0, st);
-  if (pr.kc > 0) {
+  if (pr.ns > 1) {
     pr.total = pr.batch * pr.nheads * pr.ns;
     hipLaunchKernelGGL((state_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), 0, st, pr);
     record(ev, 1, st);
@@ -29,7 +29,7 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
     record(ev, 1, st);
   }
   record(ev, 2, st);
-  pr.total = pr.batch * pr.nc * pr.nheads;
+  pr.total = pr.batch * pr.ns * pr.nheads;
   const size_t shm = (size_t)C * pr.ll * sizeof(float);
   hipLaunchKernelGGL((output_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), shm, st, pr);
   record(ev, 3, st);

@@ -94,6 +94,12 @@ def test_options_errors():
     assert validate(good_dims(), opts=o) == -12
     o.seg_log2, o.reserved = 0, 1
     assert validate(good_dims(), opts=o) == -12
+    o.seg_log2, o.reserved = 4, 0  # deeper than the on-chip stack
+    assert validate(good_dims(), opts=o) == -12
+    o.seg_log2 = 2  # deeper than log2 of the chunk count (2 chunks)
+    assert validate(good_dims(seqlen=128, nlevels=8), opts=o) == -12
+    o.seg_log2 = 1
+    assert validate(good_dims(seqlen=128, nlevels=8), opts=o) == 0
 
 
 def test_null_dims():
@@ -115,12 +121,18 @@ def test_workspace_size_formula():
     """Workspace: fp32 segment states + io-typed slots per (batch, head,
     segment), plus small decay arrays; zero when there is a single chunk."""
     d = good_dims()
-    need = L.loglin_workspace_bytes(d, 64)
-    ns = 32768 // 64
-    core = 48 * ns * 64 * 128 * (4 + 2)
-    assert core <= need <= core + 48 * ns * 4 * 32 + 4 * 256
+    assert L.loglin_plan_seg_log2(d, 64) == 3
+    for seg in (None, 0, 1, 2, 3):
+        m = 3 if seg is None else seg
+        need = L.loglin_workspace_bytes(d, 64, seg)
+        ns = 32768 // 64 >> m
+        core = 48 * ns * 64 * 128 * (4 + 2)
+        assert core <= need <= core + 48 * ns * 4 * 32 + 4 * 256, (seg, need, core)
+    # one chunk, or one segment: no level above a segment, no workspace
     assert L.loglin_workspace_bytes(good_dims(seqlen=64, nlevels=7), 64) == 0
-    assert L.loglin_plan_seg_log2(d, 64) == 0
+    assert L.loglin_workspace_bytes(good_dims(seqlen=512, nlevels=10), 64) == 0
+    assert L.loglin_workspace_bytes(good_dims(seqlen=512, nlevels=10), 64, 0) > 0
+    assert L.loglin_plan_seg_log2(good_dims(seqlen=128, nlevels=8), 64) == 1
 
 
 def test_strerror_all_codes():

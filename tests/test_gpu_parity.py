@@ -84,6 +84,20 @@ def test_onehot_levels(level):
     check(small_cfg(T=2048, H=2, G=1), variant=f"lam_onehot_{level}")
 
 
+@pytest.mark.parametrize("seg", [0, 1, 2, 3])
+@pytest.mark.parametrize("T", [1344, 2048])
+def test_segment_depths(seg, T):
+    """Chunks per segment 1..8: levels move between the on-chip Fenwick
+    stack of the output pass and the slots of the level scan."""
+    check(small_cfg(T=T, H=2, G=1), seg_log2=seg, variant="slow_decay")
+
+
+@pytest.mark.parametrize("seg", [0, 1, 2, 3])
+def test_segment_depths_fp32(seg):
+    cfg = small_cfg(dtype="fp32", T=16 * 37, H=2, G=1, P=16, N=32, C=16, decay="softplus")
+    check(cfg, seg_log2=seg)
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_chunk_invariance(chunk):
     """The result does not depend on the chunk size (up to rounding)."""
