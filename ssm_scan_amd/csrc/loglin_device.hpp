@@ -121,11 +121,40 @@ __device__ inline bf16 from_f<bf16>(float x) { return (bf16)x; }
 template <>
 __device__ inline float from_f<float>(float x) { return x; }
 
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 16 bytes of T as a register vector.
 template <class T>
-struct alignas(16) Vec16 {
-  static constexpr int n = 16 / sizeof(T);
-  T e[n];
+struct Vec;
+template <>
+struct Vec<bf16> {
+  using v16 = bf16x8;
+  using v2 = bf16x2;
 };
+template <>
+struct Vec<float> {
+  using v16 = f32x4;
+  using v2 = f32x2;
+};
+template <class T>
+using vec16_t = typename Vec<T>::v16;
+template <class T>
+using vec2_t = typename Vec<T>::v2;
+
+template <class T>
+__device__ inline vec16_t<T> load16(const T* p) {
+  return *reinterpret_cast<const vec16_t<T>*>(p);
+}
+template <class T>
+__device__ inline void store16(T* p, vec16_t<T> v) {
+  *reinterpret_cast<vec16_t<T>*>(p) = v;
+}
+template <class T>
+__device__ inline void store_pair(T* p, T a, T b) {
+  vec2_t<T> v = {a, b};
+  *reinterpret_cast<vec2_t<T>*>(p) = v;
+}
 
 template <class T>
 __device__ inline T frag_elem(const typename Mfma<T>::frag& f, int j);
@@ -143,17 +172,6 @@ __device__ inline void set_frag_elem<float>(float& f, int, float v) { f = v; }
 template <class T>
 __device__ inline typename Mfma<T>::frag load_frag(const T* p) {
   return *reinterpret_cast<const typename Mfma<T>::frag*>(p);
-}
-
-// B operand over the state dimension, read from a token row of C in state
-// order (see Mfma::state_row).
-__device__ inline bf16x8 load_state_frag(const bf16* row, int kk, int g) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * kk + 4 * g);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * kk + 16 + 4 * g);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ inline float load_state_frag(const float* row, int kk, int g) {
-  return row[Mfma<float>::state_row(kk, g, 0)];
 }
 
 __device__ inline void store4(bf16* p, f32x4 v) {
@@ -186,59 +204,195 @@ struct Tiles {
   static constexpr int KC = C < KB ? KB : C;  // token contraction, padded
   static constexpr int NKT = KC / KB;
   static constexpr int NKN = N / KB;
-  static constexpr int XS = KC + 16 / (int)sizeof(T);  // LDS row stride
   static constexpr int VEC = 16 / (int)sizeof(T);
+  // LDS arrays indexed [row][token] (X^T, W, (B w)^T): for bf16 with 64
+  // tokens the rows are unpadded and the 16-byte blocks of a row are XOR-
+  // swizzled by ((row >> 3) ^ row) & 7, which keeps both the token-pair
+  // transposing stores and the MFMA operand loads free of bank conflicts;
+  // other shapes use a 16-byte row pad.
+  static constexpr bool SWZ = sizeof(T) == 2 && KC == 64;
+  static constexpr int XS = SWZ ? KC : KC + VEC;  // LDS row stride
+  __device__ static inline int col(int row, int c) {
+    if constexpr (SWZ) return (((c >> 3) ^ (row >> 3) ^ row) & 7) << 3 | (c & 7);
+    else return c;
+  }
+  __device__ static inline int at(int row, int c) { return row * XS + col(row, c); }
   static_assert(C % 16 == 0 && P % 16 == 0 && N % KB == 0, "tile sizes");
   static_assert(C <= 64, "one wave scans a chunk");
 };
 
-// Inclusive prefix sum of log_a over one chunk into cum[0..C), staged in LDS.
-template <int C>
-__device__ inline void chunk_cumsum(const float* log_a, float* cum, int64_t row0,
-                                    int H, int h, int tid) {
+// Per-token quantities of one chunk, staged in LDS by wave 0:
+//   cum[t]  inclusive prefix sum of log a over the chunk (fp32),
+//   ecum[t] = exp(cum[t])            (decay from the chunk start to t),
+//   wst[t]  = exp(cum[C-1] - cum[t]) (decay from t to the chunk end).
+template <class T, int C>
+__device__ inline void chunk_decays(float la, float* cum, float* ecum, float* wst, int tid) {
   if (tid < 64) {
-    float v = tid < C ? log_a[(row0 + tid) * H + h] : 0.f;
+    float v = la;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       float o = __shfl_up(v, d, 64);
       if (tid >= d) v += o;
     }
-    if (tid < C) cum[tid] = v;
+    const float tot = __shfl(v, C - 1, 64);
+    if (tid < C) {
+      cum[tid] = v;
+      ecum[tid] = Mfma<T>::ex(v);
+      wst[tid] = Mfma<T>::ex(tot - v);
+    }
   }
 }
 
-// X rows of one chunk -> xt[p][tau] (transposed), bf16/fp32 as stored.
-template <class T, int C, int P, int N>
-__device__ inline void load_xt(const T* X, T* xt, int64_t row0, int H, int h,
-                               int tid) {
-  using Tl = Tiles<T, C, P, N>;
-  constexpr int PV = P / Tl::VEC;
-  for (int idx = tid; idx < C * PV; idx += Tl::NT) {
-    int tau = idx / PV, pv = idx - tau * PV;
-    Vec16<T> v = *reinterpret_cast<const Vec16<T>*>(
-        X + ((row0 + tau) * H + h) * P + pv * Tl::VEC);
+// A tile of token rows (B, C or X of one chunk) staged in LDS unpadded, W
+// elements per row; the 16-byte blocks of row t are XOR-swizzled by
+// t mod (blocks per row).  This keeps the MFMA operand loads (16 rows x one
+// block, the state-order 8-byte halves, and the transposing 8-byte reads of
+// four consecutive rows) free of bank conflicts.
+template <class T, int W>
+struct Rows {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int NBLK = W / VEC;
+  __device__ static inline int at(int row, int c) {
+    return row * W + ((((c / VEC) ^ row) & (NBLK - 1)) * VEC) + (c % VEC);
+  }
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* global_ptr_t;
+
+// Copy R token rows of W elements (global row stride `grs` elements) into
+// LDS in the Rows layout with global_load_lds_dwordx4: lane i of an
+// instruction writes the 16 bytes at M0 + 16 i, so each instruction fills
+// 1 KB of LDS and every lane fetches the global block that belongs there.
+// The copy is asynchronous: s_waitcnt and a barrier precede any read.
+template <class T, int R, int W, int NW>
+__device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, int lane) {
+  using L = Rows<T, W>;
+  constexpr int PIECES = R * L::NBLK;  // 16-byte pieces of the tile
+  constexpr int INSTS = (PIECES + 63) / 64;
+  constexpr int PER_INST = 1024 / (int)sizeof(T);  // elements per instruction
 #pragma unroll
-    for (int e = 0; e < Tl::VEC; ++e) xt[(pv * Tl::VEC + e) * Tl::XS + tau] = v.e[e];
+  for (int k = 0; k < (INSTS + NW - 1) / NW; ++k) {
+    const int inst = wave + k * NW;
+    const int piece = inst * 64 + lane;
+    if (inst < INSTS && piece < PIECES) {  // lanes past a short tile write nothing
+      const int row = piece / L::NBLK, pb = piece % L::NBLK;
+      const int lb = (pb ^ row) & (L::NBLK - 1);
+      const T* src = g + (int64_t)row * grs + lb * L::VEC;
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(void*)src,
+                                       (lds_ptr_t)(void*)(lds + inst * PER_INST), 16, 0, 0);
+    }
+  }
+}
+
+// ---- MFMA operand fragments from LDS tiles (lane = 16 g + r)
+
+// Contraction along a row: elements [k0 + KPL g, k0 + KPL g + KPL) of row
+// `row` (one 16-byte read for bf16).
+template <class T, class Lay>
+__device__ inline typename Mfma<T>::frag frag_along(const T* tile, int row, int k0, int g) {
+  return load_frag<T>(tile + Lay::at(row, k0 + g * Mfma<T>::KPL));
+}
+
+// Contraction down the rows: lane (g, r) receives tile[k0 + KPL g + j][c0 + r]
+// for j < KPL.  For bf16 this is two ds_read_b64_tr_b16: within each group
+// of 16 lanes, lane i = 4q + p receives element p of the 8-byte pieces that
+// lanes q, q+4, q+8, q+12 address; lane s addresses row kb + s/4 at column
+// c0 + 4 (s mod 4), so lane i gets rows kb..kb+3 of column c0 + i.
+template <class Lay>
+__device__ inline bf16x8 frag_down_bf16(const bf16* tile, int k0, int c0, int g, int r) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16* lp;
+  const int kb = k0 + 8 * g + (r >> 2), c = c0 + 4 * (r & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(void*)(tile + Lay::at(kb, c)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(void*)(tile + Lay::at(kb + 4, c)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <class T, class Lay>
+__device__ inline typename Mfma<T>::frag frag_down(const T* tile, int k0, int c0, int g, int r) {
+  if constexpr (sizeof(T) == 2) return frag_down_bf16<Lay>(tile, k0, c0, g, r);
+  else return tile[Lay::at(k0 + g, c0 + r)];
+}
+
+// frag_down of a token-row tile with row k scaled by w[k] (fp32 math).
+template <class T, class Lay>
+__device__ inline typename Mfma<T>::frag frag_down_scaled(const T* tile, const float* w, int k0,
+                                                          int c0, int g, int r) {
+  auto f = frag_down<T, Lay>(tile, k0, c0, g, r);
+  if constexpr (sizeof(T) == 2) {
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + k0 + 8 * g);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + k0 + 8 * g + 4);
+    bf16x8 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = (bf16)((float)f[j] * w0[j]);
+      o[j + 4] = (bf16)((float)f[j + 4] * w1[j]);
+    }
+    return o;
+  } else {
+    return f * w[k0 + g];
+  }
+}
+
+// State-order B-operand fragment (see Mfma::state_row) of token row `row`.
+template <class T, int N>
+__device__ inline typename Mfma<T>::frag rows_state_frag(const T* tile, int row, int kk, int g) {
+  using L = Rows<T, N>;
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(tile + L::at(row, 32 * kk + 4 * g));
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(tile + L::at(row, 32 * kk + 16 + 4 * g));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    return tile[L::at(row, Mfma<float>::state_row(kk, g, 0))];
+  }
+}
+
+// One chunk's state S[n][p] = sum_t B[t][n] w[t] X[t][p] for this wave's 16
+// columns of X (all N rows of S), accumulated into S (NB tiles of 16x16).
+template <class T, int C, int P, int N>
+__device__ inline void chunk_state_mma(const T* bs, const T* xs, const float* w, f32x4* S,
+                                       int wave, int g, int r) {
+  using Tl = Tiles<T, C, P, N>;
+  using M = Mfma<T>;
+#pragma unroll
+  for (int kt = 0; kt < Tl::NKT; ++kt) {  // rows C..KC-1 of the tiles are zero
+    const auto bf = frag_down_scaled<T, Rows<T, P>>(xs, w, kt * Tl::KB, 16 * wave, g, r);
+#pragma unroll
+    for (int nb = 0; nb < Tl::NB; ++nb) {
+      const auto af = frag_down<T, Rows<T, N>>(bs, kt * Tl::KB, 16 * nb, g, r);
+      S[nb] = M::mma(af, bf, S[nb]);
+    }
   }
 }
 
 // ------------------------------------------------------------- pass 1
 
 // One work-group per (batch, head, segment).  Wave w owns state columns
-// [16w, 16w+16) and all N rows, as NB 16x16 fp32 tiles.
+// [16w, 16w+16) and all N rows, as NB 16x16 fp32 tiles.  B and X rows go
+// straight to LDS, double-buffered: the next chunk's rows are requested as
+// soon as the current chunk's have landed.
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params pr) {
   using Tl = Tiles<T, C, P, N>;
   using M = Mfma<T>;
-  __shared__ __attribute__((aligned(16))) T bwt[N * Tl::XS];
-  __shared__ __attribute__((aligned(16))) T xt[P * Tl::XS];
-  __shared__ float cum[C];
+  constexpr int KC = Tl::KC;  // token rows of a tile; rows C..KC-1 stay zero
+  __shared__ __attribute__((aligned(1024))) T bsh[2][KC * N];
+  __shared__ __attribute__((aligned(1024))) T xsh[2][KC * P];
+  __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int H = pr.nheads, G = pr.ngroups;
+  if (KC > C) {
+    for (int i = tid; i < (KC - C) * (N + P); i += Tl::NT) {
+      const int rr = C + i / (N + P), c = i % (N + P);
+      if (c < N) bsh[0][rr * N + c] = bsh[1][rr * N + c] = from_f<T>(0.f);
+      else xsh[0][rr * P + c - N] = xsh[1][rr * P + c - N] = from_f<T>(0.f);
+    }
+    for (int i = C + tid; i < KC; i += Tl::NT) wst[i] = 0.f;
+  }
   const int q = tile % pr.ns;
   const int bh = tile / pr.ns;
   const int h = bh % H, b = bh / H;
@@ -246,53 +400,38 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
   const T* X = static_cast<const T*>(pr.X);
   const T* Bm = static_cast<const T*>(pr.Bm);
   const int seg = 1 << pr.m;
-
-  if (Tl::KC > C) {  // zero the contraction padding once
-    for (int idx = tid; idx < (N + P) * (Tl::KC - C); idx += Tl::NT) {
-      int row = idx / (Tl::KC - C), col = C + idx % (Tl::KC - C);
-      if (row < N) bwt[row * Tl::XS + col] = from_f<T>(0.f);
-      else xt[(row - N) * Tl::XS + col] = from_f<T>(0.f);
-    }
-  }
+  const int j0 = q * seg;
+  const int nch = min(seg, pr.nc - j0);
 
   f32x4 S[Tl::NB];
 #pragma unroll
   for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float seg_sum = 0.f;
 
-  for (int jl = 0; jl < seg; ++jl) {
-    const int j = q * seg + jl;
-    if (j >= pr.nc) break;  // last segment of a ragged chunk count
+  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    chunk_cumsum<C>(pr.log_a, cum, row0, H, h, tid);
+    rows_to_lds<T, C, N, Tl::NW>(Bm + (row0 * G + grp) * N, (int64_t)G * N, bsh[buf], wave, lane);
+    rows_to_lds<T, C, P, Tl::NW>(X + (row0 * H + h) * P, (int64_t)H * P, xsh[buf], wave, lane);
+  };
+  float la = tid < C ? pr.log_a[((int64_t)b * pr.seqlen + (int64_t)j0 * C + tid) * H + h] : 0.f;
+  issue(j0, 0);
+  for (int jl = 0; jl < nch; ++jl) {
+    const int cur = jl & 1;
+    chunk_decays<T, C>(la, cum, ecum, wst, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     __syncthreads();
-    const float atot = cum[C - 1];
-    constexpr int NV = N / Tl::VEC;
-    for (int idx = tid; idx < C * NV; idx += Tl::NT) {
-      int tau = idx / NV, nv = idx - tau * NV;
-      Vec16<T> v = *reinterpret_cast<const Vec16<T>*>(
-          Bm + ((row0 + tau) * G + grp) * N + nv * Tl::VEC);
-      float w = M::ex(atot - cum[tau]);
-#pragma unroll
-      for (int e = 0; e < Tl::VEC; ++e)
-        bwt[(nv * Tl::VEC + e) * Tl::XS + tau] = from_f<T>(to_f(v.e[e]) * w);
+    if (jl + 1 < nch) {  // the other buffer was released by the previous barrier
+      issue(j0 + jl + 1, cur ^ 1);
+      const int64_t rn = (int64_t)b * pr.seqlen + (int64_t)(j0 + jl + 1) * C;
+      la = tid < C ? pr.log_a[(rn + tid) * H + h] : 0.f;
     }
-    load_xt<T, C, P, N>(X, xt, row0, H, h, tid);
-    __syncthreads();
+    const float atot = cum[C - 1];
     if (jl > 0) {
       const float dec = M::ex(atot);
 #pragma unroll
       for (int nb = 0; nb < Tl::NB; ++nb) S[nb] *= dec;
     }
-#pragma unroll
-    for (int kt = 0; kt < Tl::NKT; ++kt) {
-      auto bf = load_frag<T>(xt + (16 * wave + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-#pragma unroll
-      for (int nb = 0; nb < Tl::NB; ++nb) {
-        auto af = load_frag<T>(bwt + (16 * nb + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-        S[nb] = M::mma(af, bf, S[nb]);
-      }
-    }
+    chunk_state_mma<T, C, P, N>(bsh[cur], xsh[cur], wst, S, wave, g, r);
     seg_sum += atot;
     __syncthreads();
   }
@@ -381,6 +520,26 @@ __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
 // register stack for.
 constexpr int MAX_SEG_LOG2 = 3;
 
+// Score tiles of the intra-chunk block, causal ones (sb <= tb) first so that
+// dealing them round-robin to the waves balances the MFMA work.
+template <int TB>
+__device__ inline void score_tile(int u, int& tb, int& sb) {
+  constexpr int NCAUSAL = TB * (TB + 1) / 2;
+  if (u < NCAUSAL) {
+    tb = 0;
+    while ((tb + 1) * (tb + 2) / 2 <= u) ++tb;
+    sb = u - tb * (tb + 1) / 2;
+  } else {
+    int k = u - NCAUSAL;  // strictly upper tiles, row-major
+    tb = 0;
+    while (k >= TB - 1 - tb) {
+      k -= TB - 1 - tb;
+      ++tb;
+    }
+    sb = tb + 1 + k;
+  }
+}
+
 // One work-group per (batch, segment of 2^m chunks, head); the chunks of the
 // segment are processed in order.  Wave w owns output columns [16w, 16w+16)
 // of the head for all C tokens of a chunk (TB tiles of Y^T), and the same
@@ -394,27 +553,44 @@ constexpr int MAX_SEG_LOG2 = 3;
 // 2^e chunks that ends just before the current chunk, as MFMA A-operand
 // fragments.  The state MFMA leaves a lane exactly the rows its own
 // fragments need, so the stack never crosses lanes.
+//
+// B and X rows are double-buffered in LDS (bf16): the next chunk's rows are
+// requested right after the current chunk's first barrier.  C rows are
+// single-buffered and refilled once the output tiles have read them.
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Params pr) {
   using Tl = Tiles<T, C, P, N>;
   using M = Mfma<T>;
   using frag = typename M::frag;
-  constexpr int RS = N + Tl::VEC;  // row stride of the staged B and C rows
-  constexpr int NBU = C * N / Tl::VEC;  // 16-byte units of a chunk of B or C
+  using RB = Rows<T, N>;
+  using RX = Rows<T, P>;
   constexpr int MM = MAX_SEG_LOG2;
-  __shared__ __attribute__((aligned(16))) T xt[P * Tl::XS];
-  __shared__ __attribute__((aligned(16))) T wt[C * Tl::XS];
-  __shared__ __attribute__((aligned(16))) T bsh[C * RS];  // B rows
-  __shared__ __attribute__((aligned(16))) T csh[C * RS];  // C rows
-  __shared__ __attribute__((aligned(16))) T bwt[N * Tl::XS];  // (B w)^T
-  __shared__ float cum[C];
-  extern __shared__ float lam_s[];  // [C][ll]
+  constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;
+  constexpr int KC = Tl::KC;  // token rows of the B / X tiles; rows C..KC-1 stay zero
+  __shared__ __attribute__((aligned(1024))) T bsh[NBUF][KC * N];  // B rows
+  __shared__ __attribute__((aligned(1024))) T xsh[NBUF][KC * P];  // X rows
+  __shared__ __attribute__((aligned(1024))) T csh[C * N];         // C rows
+  __shared__ __attribute__((aligned(16))) T wt[C * Tl::XS];       // W[t][s]
+  __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
+  extern __shared__ float lam_s[];  // [C][ll | 1]
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r = lane & 15;
+  const int tid0 = threadIdx.x, wave = tid0 >> 6;
+  if (KC > C) {  // contraction padding of the token tiles and of W stays zero
+    for (int i = tid0; i < (KC - C) * (N + P); i += Tl::NT) {
+      const int rr = C + i / (N + P), c = i % (N + P);
+#pragma unroll
+      for (int bf = 0; bf < NBUF; ++bf) {
+        if (c < N) bsh[bf][rr * N + c] = from_f<T>(0.f);
+        else xsh[bf][rr * P + c - N] = from_f<T>(0.f);
+      }
+    }
+    for (int i = tid0; i < C * (KC - C); i += Tl::NT) wt[(i / (KC - C)) * Tl::XS + C + i % (KC - C)] = from_f<T>(0.f);
+    for (int i = C + tid0; i < KC; i += Tl::NT) wst[i] = 0.f;
+  }
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels, LL = pr.ll;
+  const int LLP = LL | 1;  // odd row stride: lambda lookups of 16 rows spread over banks
   const int h = tile % H;
   const int q = (tile / H) % pr.ns;
   const int b = tile / (H * pr.ns);
@@ -432,15 +608,6 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   const T* slots = static_cast<const T*>(pr.slots);
   T* out = static_cast<T*>(pr.out);
 
-  if (Tl::KC > C) {  // contraction padding of X^T, W and (B w)^T stays zero
-    for (int idx = tid; idx < (C + P + N) * (Tl::KC - C); idx += Tl::NT) {
-      int row = idx / (Tl::KC - C), col = C + idx % (Tl::KC - C);
-      if (row < C) wt[row * Tl::XS + col] = from_f<T>(0.f);
-      else if (row < C + P) xt[(row - C) * Tl::XS + col] = from_f<T>(0.f);
-      else bwt[(row - C - P) * Tl::XS + col] = from_f<T>(0.f);
-    }
-  }
-
   frag zl[MM][Tl::NKN];  // local Fenwick stack (entry e: 2^e chunks)
   float zla[MM];         // total log-decay of each entry's block
   float dloc[MM + 1];    // log-decay from a local block's end to the chunk
@@ -450,133 +617,185 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   for (int k = 0; k <= MM; ++k) dloc[k] = 0.f;
   float accseg = 0.f;  // log-decay from the segment start to the chunk
   const float* gap = pr.ks > 0 ? pr.gap_decay + ((int64_t)bh * pr.ns + q) * (pr.ks + 1) : nullptr;
+  const unsigned ext_mask = (unsigned)q & ((1u << pr.ks) - 1u);  // active levels above
+  auto slot_row = [&](int ks, int r, int g) __attribute__((always_inline)) {
+    const int qs = ((q >> ks) << ks) + (1 << (ks - 1)) - 1;
+    return slots + (((int64_t)bh * pr.ns + qs) * P + 16 * wave + r) * N + g * Tl::KPL;
+  };
+
+  constexpr int LPF = (C * 32 + Tl::NT - 1) / Tl::NT;  // lambda values per thread (<= 32 levels)
+  constexpr bool LAM_PREFETCH = LPF <= 8;
+  float la = 0.f;
+  T lv[LAM_PREFETCH ? LPF : 1];
+  frag zfirst[Tl::NKN];  // slot of the lowest level above the segment
+  auto issue_bx = [&](int j, int buf, int lane) __attribute__((always_inline)) {
+    const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    rows_to_lds<T, C, N, Tl::NW>(Bm + (r0 * G + grp) * N, (int64_t)G * N, bsh[buf], wave, lane);
+    rows_to_lds<T, C, P, Tl::NW>(X + (r0 * H + h) * P, (int64_t)H * P, xsh[buf], wave, lane);
+  };
+  auto issue_c = [&](int j, int lane) __attribute__((always_inline)) {
+    const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    rows_to_lds<T, C, N, Tl::NW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, csh, wave, lane);
+  };
+  auto issue_regs = [&](int j, int tid) __attribute__((always_inline)) {
+    const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    const int r = tid & 15, g = (tid >> 4) & 3;
+    if (ext_mask) {
+      const T* zr = slot_row(__builtin_ctz(ext_mask) + 1, r, g);
+#pragma unroll
+      for (int kk = 0; kk < Tl::NKN; ++kk) zfirst[kk] = load_frag<T>(zr + kk * Tl::KB);
+    }
+    la = tid < C ? pr.log_a[(r0 + tid) * H + h] : 0.f;
+    if constexpr (LAM_PREFETCH) {
+#pragma unroll
+      for (int k = 0; k < LPF; ++k) {
+        const int idx = tid + k * Tl::NT;
+        if (idx < C * LL) {
+          const int tau = idx / LL, l = idx - tau * LL;
+          lv[k] = lam[((r0 + tau) * H + h) * L + l];
+        }
+      }
+    }
+  };
+  issue_bx(j0, 0, tid0 & 63);
+  issue_c(j0, tid0 & 63);
+  issue_regs(j0, tid0);
 
   for (int jl = 0; jl < nch; ++jl) {
     const int j = j0 + jl;
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const bool need_state = jl + 1 < nch;
+    const int cur = NBUF == 2 ? (jl & 1) : 0;
+    const T* bs = bsh[cur];
+    const T* xs = xsh[cur];
+    // Recompute lane-dependent LDS addresses inside the loop instead of
+    // keeping dozens of them live across it (they would be spilled).
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, g = lane >> 4, r = lane & 15;
 
-    // ---- stage the chunk: cumulative log-decay, lambda, X^T, B and C rows
-    chunk_cumsum<C>(pr.log_a, cum, row0, H, h, tid);
-    for (int idx = tid; idx < C * LL; idx += Tl::NT) {
-      int tau = idx / LL, l = idx - tau * LL;
-      lam_s[idx] = to_f(lam[((row0 + tau) * H + h) * L + l]);
-    }
-    load_xt<T, C, P, N>(X, xt, row0, H, h, tid);
-    constexpr int NV = N / Tl::VEC;
-    for (int idx = tid; idx < NBU; idx += Tl::NT) {
-      const int tau = idx / NV, nv = idx - tau * NV;
-      const int64_t go = ((row0 + tau) * G + grp) * N + nv * Tl::VEC;
-      *reinterpret_cast<Vec16<T>*>(bsh + tau * RS + nv * Tl::VEC) =
-          *reinterpret_cast<const Vec16<T>*>(Bm + go);
-      *reinterpret_cast<Vec16<T>*>(csh + tau * RS + nv * Tl::VEC) =
-          *reinterpret_cast<const Vec16<T>*>(Cm + go);
-    }
-    __syncthreads();
-    const float atot = cum[C - 1];
-
-    // ---- (B w)^T for this chunk's state, w_s = exp(atot - cum_s)
-    if (need_state) {
-      for (int idx = tid; idx < NBU; idx += Tl::NT) {
-        const int tau = idx / NV, nv = idx - tau * NV;
-        const Vec16<T> v = *reinterpret_cast<const Vec16<T>*>(bsh + tau * RS + nv * Tl::VEC);
-        const float w = M::ex(atot - cum[tau]);
+    // ---- stage lambda and the per-token decays
+    if constexpr (LAM_PREFETCH) {
 #pragma unroll
-        for (int e = 0; e < Tl::VEC; ++e)
-          bwt[(nv * Tl::VEC + e) * Tl::XS + tau] = from_f<T>(to_f(v.e[e]) * w);
+      for (int k = 0; k < LPF; ++k) {
+        const int idx = tid + k * Tl::NT;
+        if (idx < C * LL) {
+          const int tau = idx / LL, l = idx - tau * LL;
+          lam_s[tau * LLP + l] = to_f(lv[k]);
+        }
+      }
+    } else {
+      for (int idx = tid; idx < C * LL; idx += Tl::NT) {
+        const int tau = idx / LL, l = idx - tau * LL;
+        lam_s[tau * LLP + l] = to_f(lam[((row0 + tau) * H + h) * L + l]);
       }
     }
+    chunk_decays<T, C>(la, cum, ecum, wst, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
+    __syncthreads();
+    if (NBUF == 2 && need_state) issue_bx(j + 1, cur ^ 1, lane);  // other buffer is free
+    const float atot = cum[C - 1];
 
     // ---- intra-chunk weights W[t][s], from the transposed scores B C^T
     for (int u = wave; u < Tl::TB * Tl::TB; u += Tl::NW) {
-      const int tb = u / Tl::TB, sb = u - tb * Tl::TB;
+      int tb, sb;
+      score_tile<Tl::TB>(u, tb, sb);
       const int t = 16 * tb + r;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 wv = {0.f, 0.f, 0.f, 0.f};
       if (sb <= tb) {
-        const T* brow = bsh + (16 * sb + r) * RS + g * Tl::KPL;
-        const T* crow = csh + t * RS + g * Tl::KPL;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < Tl::NKN; ++kk)
-          acc = M::mma(load_frag<T>(brow + kk * Tl::KB), load_frag<T>(crow + kk * Tl::KB), acc);
-      }
-      f32x4 wv;
+          acc = M::mma(frag_along<T, RB>(bs, 16 * sb + r, kk * Tl::KB, g),
+                       frag_along<T, RB>(csh, t, kk * Tl::KB, g), acc);
+        const float ct_ = cum[t];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 16 * sb + 4 * g + i;
-        wv[i] = (s <= t) ? acc[i] * M::ex(cum[t] - cum[s]) * lam_s[t * LL + bit_length(t ^ s)]
-                         : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * sb + 4 * g + i;
+          wv[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[s]) * lam_s[t * LLP + bit_length(t ^ s)]
+                           : 0.f;
+        }
       }
-      store4(wt + t * Tl::XS + 16 * sb + 4 * g, wv);
+      store4(wt + Tl::at(t, 16 * sb + 4 * g), wv);
     }
     __syncthreads();
 
-    // ---- output tiles: intra block, then every active inter-chunk level
-    f32x4 Y[Tl::TB];
+    // ---- output tiles, TH t-blocks at a time: intra block, then every
+    // active inter-chunk level
+    constexpr int TH = Tl::TB < 2 ? Tl::TB : 2;
 #pragma unroll
-    for (int tb = 0; tb < Tl::TB; ++tb) {
-      Y[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < Tl::TB; t0 += TH) {
+      f32x4 Y[TH];
+      frag cf[TH][Tl::NKN];  // C^T fragments in state order
 #pragma unroll
-      for (int kt = 0; kt < Tl::NKT; ++kt) {
-        if (kt * Tl::KB < 16 * (tb + 1)) {
-          auto af = load_frag<T>(xt + (16 * wave + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-          auto bf = load_frag<T>(wt + (16 * tb + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-          Y[tb] = M::mma(af, bf, Y[tb]);
+      for (int i = 0; i < TH; ++i) {
+        const int tb = t0 + i;
+        Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < Tl::NKT; ++kt) {
+          if (kt * Tl::KB < 16 * (tb + 1)) {
+            auto af = frag_down<T, RX>(xs, kt * Tl::KB, 16 * wave, g, r);
+            auto bf = load_frag<T>(wt + Tl::at(16 * tb + r, kt * Tl::KB + g * Tl::KPL));
+            Y[i] = M::mma(af, bf, Y[i]);
+          }
         }
+#pragma unroll
+        for (int kk = 0; kk < Tl::NKN; ++kk) cf[i][kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
+      }
+
+      auto add_level = [&](const frag* zf, int level, float D) __attribute__((always_inline)) {
+        const float eD = M::ex(D);
+#pragma unroll
+        for (int i = 0; i < TH; ++i) {
+          f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[i][kk], tmp);
+          const int t = 16 * (t0 + i) + r;
+          const float sc = lam_s[t * LLP + level] * ecum[t] * eD;
+          Y[i] += sc * tmp;
+        }
+      };
+
+      // levels above the segment; the first slot is in registers already,
+      // the others are loaded one level ahead
+      unsigned mask = ext_mask;
+      frag zcur[Tl::NKN];
+#pragma unroll
+      for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = zfirst[kk];
+      while (mask) {
+        const int ks = __builtin_ctz(mask) + 1;
+        mask &= mask - 1;
+        frag znext[Tl::NKN];
+        if (mask) {
+          const T* zr = slot_row(__builtin_ctz(mask) + 1, r, g);
+#pragma unroll
+          for (int kk = 0; kk < Tl::NKN; ++kk) znext[kk] = load_frag<T>(zr + kk * Tl::KB);
+        }
+        add_level(zcur, c_log + m + ks, gap[ks] + accseg);
+#pragma unroll
+        for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = znext[kk];
+      }
+#pragma unroll
+      for (int e = 0; e < MM; ++e) {  // levels inside the segment
+        if (e < m && ((jl >> e) & 1)) add_level(zl[e], c_log + e + 1, dloc[e + 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < TH; ++i) {
+        const int t = 16 * (t0 + i) + r;
+        store4(out + ((row0 + t) * H + h) * P + 16 * wave + 4 * g, Y[i]);
       }
     }
-    frag cf[Tl::TB][Tl::NKN];  // C^T fragments in state order
-#pragma unroll
-    for (int tb = 0; tb < Tl::TB; ++tb)
-#pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk)
-        cf[tb][kk] = load_state_frag(csh + (16 * tb + r) * RS, kk, g);
 
-    auto add_level = [&](const frag* zf, int level, float D) {
-#pragma unroll
-      for (int tb = 0; tb < Tl::TB; ++tb) {
-        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[tb][kk], tmp);
-        const int t = 16 * tb + r;
-        const float sc = lam_s[t * LL + level] * M::ex(cum[t] + D);
-        Y[tb] += sc * tmp;
-      }
-    };
-
-    for (int ks = 1; ks <= pr.ks; ++ks) {  // levels above the segment
-      if (!((q >> (ks - 1)) & 1)) continue;
-      const int qs = ((q >> ks) << ks) + (1 << (ks - 1)) - 1;
-      const T* zrow = slots + (((int64_t)bh * pr.ns + qs) * P + 16 * wave + r) * N + g * Tl::KPL;
-      frag zf[Tl::NKN];
-#pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = load_frag<T>(zrow + kk * Tl::KB);
-      add_level(zf, c_log + m + ks, gap[ks] + accseg);
-    }
-#pragma unroll
-    for (int e = 0; e < MM; ++e) {  // levels inside the segment
-      if (e < m && ((jl >> e) & 1)) add_level(zl[e], c_log + e + 1, dloc[e + 1]);
-    }
-
-#pragma unroll
-    for (int tb = 0; tb < Tl::TB; ++tb) {
-      const int t = 16 * tb + r;
-      store4(out + ((row0 + t) * H + h) * P + 16 * wave + 4 * g, Y[tb]);
-    }
-
-    // ---- this chunk's state, pushed on the local Fenwick stack
     if (need_state) {
+      __syncthreads();  // every wave has read its C^T fragments
+      issue_c(j + 1, lane);
+      issue_regs(j + 1, tid);  // land during the state MFMAs
+
+      // ---- this chunk's state, pushed on the local Fenwick stack
       f32x4 S[Tl::NB];
 #pragma unroll
       for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < Tl::NKT; ++kt) {
-        auto bf = load_frag<T>(xt + (16 * wave + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-#pragma unroll
-        for (int nb = 0; nb < Tl::NB; ++nb) {
-          auto af = load_frag<T>(bwt + (16 * nb + r) * Tl::XS + kt * Tl::KB + g * Tl::KPL);
-          S[nb] = M::mma(af, bf, S[nb]);
-        }
-      }
+      chunk_state_mma<T, C, P, N>(bs, xs, wst, S, wave, g, r);
       // merge with the entries of the blocks this chunk completes
       const int z = __builtin_ctz(~(unsigned)jl);  // trailing ones of jl
       float cur_a = atot;
@@ -613,6 +832,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
       if (((jl + 1) & ((1 << (k - 1)) - 1)) == 0) dloc[k] = 0.f;
     }
     __syncthreads();  // LDS is restaged by the next chunk
+    if (NBUF == 1 && need_state) issue_bx(j + 1, 0, lane);
   }
 }
 
