@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace loglin {
 
 typedef __bf16 bf16;
@@ -182,6 +184,16 @@ __device__ inline void store4(float* p, f32x4 v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Work-group barrier for LDS producer / consumer hand-offs.  It waits for
+// this wave's LDS operations only: __syncthreads() also waits for every
+// outstanding global load (its fence is not address-space aware), which
+// would stall on the asynchronous global->LDS prefetch of the next chunk.
+// Tiles filled by global_load_lds are published with an explicit
+// s_waitcnt before the barrier that precedes their first read.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ inline int bit_length(unsigned x) {
   return x ? 32 - __builtin_clz(x) : 0;
 }
@@ -260,6 +272,21 @@ struct Rows {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* global_ptr_t;
 
+// One global_load_lds_dwordx4: lane i copies 16 bytes from its own global
+// address to LDS address lds_base + 16 i.  Issued from inline assembly so
+// that the compiler does not track it: its wait analysis cannot tell LDS
+// arrays apart for these copies and would otherwise stall every later LDS
+// read on the copy in flight.  Callers publish the data with s_waitcnt
+// vmcnt(0) and a barrier before the first read of the destination.
+__device__ inline void dma_16x64(const void* src, const void* lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(lds_ptr_t)const_cast<void*>(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
 // Copy R token rows of W elements (global row stride `grs` elements) into
 // LDS in the Rows layout with global_load_lds_dwordx4: lane i of an
 // instruction writes the 16 bytes at M0 + 16 i, so each instruction fills
@@ -279,8 +306,7 @@ __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, in
       const int row = piece / L::NBLK, pb = piece % L::NBLK;
       const int lb = (pb ^ row) & (L::NBLK - 1);
       const T* src = g + (int64_t)row * grs + lb * L::VEC;
-      __builtin_amdgcn_global_load_lds((global_ptr_t)(void*)src,
-                                       (lds_ptr_t)(void*)(lds + inst * PER_INST), 16, 0, 0);
+      dma_16x64(src, lds + inst * PER_INST);
     }
   }
 }
@@ -376,8 +402,12 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
   using Tl = Tiles<T, C, P, N>;
   using M = Mfma<T>;
   constexpr int KC = Tl::KC;  // token rows of a tile; rows C..KC-1 stay zero
-  __shared__ __attribute__((aligned(1024))) T bsh[2][KC * N];
-  __shared__ __attribute__((aligned(1024))) T xsh[2][KC * P];
+  // Two named buffers (not one 2-D array) so that the compiler can tell the
+  // asynchronous fill of one from reads of the other and does not wait.
+  __shared__ __attribute__((aligned(1024))) T bsh0[KC * N];
+  __shared__ __attribute__((aligned(1024))) T bsh1[KC * N];
+  __shared__ __attribute__((aligned(1024))) T xsh0[KC * P];
+  __shared__ __attribute__((aligned(1024))) T xsh1[KC * P];
   __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -388,8 +418,8 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
   if (KC > C) {
     for (int i = tid; i < (KC - C) * (N + P); i += Tl::NT) {
       const int rr = C + i / (N + P), c = i % (N + P);
-      if (c < N) bsh[0][rr * N + c] = bsh[1][rr * N + c] = from_f<T>(0.f);
-      else xsh[0][rr * P + c - N] = xsh[1][rr * P + c - N] = from_f<T>(0.f);
+      if (c < N) bsh0[rr * N + c] = bsh1[rr * N + c] = from_f<T>(0.f);
+      else xsh0[rr * P + c - N] = xsh1[rr * P + c - N] = from_f<T>(0.f);
     }
     for (int i = C + tid; i < KC; i += Tl::NT) wst[i] = 0.f;
   }
@@ -408,20 +438,23 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
   for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float seg_sum = 0.f;
 
-  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+  auto issue = [&](int j, T* bs, T* xs) __attribute__((always_inline)) {
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, Tl::NW>(Bm + (row0 * G + grp) * N, (int64_t)G * N, bsh[buf], wave, lane);
-    rows_to_lds<T, C, P, Tl::NW>(X + (row0 * H + h) * P, (int64_t)H * P, xsh[buf], wave, lane);
+    rows_to_lds<T, C, N, Tl::NW>(Bm + (row0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
+    rows_to_lds<T, C, P, Tl::NW>(X + (row0 * H + h) * P, (int64_t)H * P, xs, wave, lane);
   };
   float la = tid < C ? pr.log_a[((int64_t)b * pr.seqlen + (int64_t)j0 * C + tid) * H + h] : 0.f;
-  issue(j0, 0);
-  for (int jl = 0; jl < nch; ++jl) {
-    const int cur = jl & 1;
+  issue(j0, bsh0, xsh0);
+  // one chunk per call; CUR selects the buffer pair at compile time
+  auto step = [&](auto cur_c, int jl) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
+    T* bs = CUR ? bsh1 : bsh0;
+    T* xs = CUR ? xsh1 : xsh0;
     chunk_decays<T, C>(la, cum, ecum, wst, tid);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
-    __syncthreads();
+    lds_barrier();
     if (jl + 1 < nch) {  // the other buffer was released by the previous barrier
-      issue(j0 + jl + 1, cur ^ 1);
+      issue(j0 + jl + 1, CUR ? bsh0 : bsh1, CUR ? xsh0 : xsh1);
       const int64_t rn = (int64_t)b * pr.seqlen + (int64_t)(j0 + jl + 1) * C;
       la = tid < C ? pr.log_a[(rn + tid) * H + h] : 0.f;
     }
@@ -431,9 +464,13 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
 #pragma unroll
       for (int nb = 0; nb < Tl::NB; ++nb) S[nb] *= dec;
     }
-    chunk_state_mma<T, C, P, N>(bsh[cur], xsh[cur], wst, S, wave, g, r);
+    chunk_state_mma<T, C, P, N>(bs, xs, wst, S, wave, g, r);
     seg_sum += atot;
-    __syncthreads();
+    lds_barrier();
+  };
+  for (int jl = 0; jl < nch; jl += 2) {
+    step(std::integral_constant<int, 0>{}, jl);
+    if (jl + 1 < nch) step(std::integral_constant<int, 1>{}, jl + 1);
   }
 
   float* dst = pr.seg_state + ((int64_t)bh * pr.ns + q) * (P * N) + (16 * wave + r) * N;
@@ -567,12 +604,18 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   constexpr int MM = MAX_SEG_LOG2;
   constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;
   constexpr int KC = Tl::KC;  // token rows of the B / X tiles; rows C..KC-1 stay zero
-  __shared__ __attribute__((aligned(1024))) T bsh[NBUF][KC * N];  // B rows
-  __shared__ __attribute__((aligned(1024))) T xsh[NBUF][KC * P];  // X rows
+  // B and X rows, two named buffers each (bf16; fp32 uses only the first)
+  // so that the compiler can tell the asynchronous fill of one from reads
+  // of the other and does not wait for it.
+  __shared__ __attribute__((aligned(1024))) T bsh0[KC * N];
+  __shared__ __attribute__((aligned(1024))) T bsh1[NBUF == 2 ? KC * N : 1];
+  __shared__ __attribute__((aligned(1024))) T xsh0[KC * P];
+  __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? KC * P : 1];
   __shared__ __attribute__((aligned(1024))) T csh[C * N];         // C rows
   __shared__ __attribute__((aligned(16))) T wt[C * Tl::XS];       // W[t][s]
   __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
-  extern __shared__ float lam_s[];  // [C][ll | 1]
+  __shared__ float gap_s[MAX_DEPTH + 1];  // gap log-decays of this segment
+  extern __shared__ float lam_s[];        // [C][ll | 1]
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
@@ -580,10 +623,12 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   if (KC > C) {  // contraction padding of the token tiles and of W stays zero
     for (int i = tid0; i < (KC - C) * (N + P); i += Tl::NT) {
       const int rr = C + i / (N + P), c = i % (N + P);
-#pragma unroll
-      for (int bf = 0; bf < NBUF; ++bf) {
-        if (c < N) bsh[bf][rr * N + c] = from_f<T>(0.f);
-        else xsh[bf][rr * P + c - N] = from_f<T>(0.f);
+      if (c < N) {
+        bsh0[rr * N + c] = from_f<T>(0.f);
+        if constexpr (NBUF == 2) bsh1[rr * N + c] = from_f<T>(0.f);
+      } else {
+        xsh0[rr * P + c - N] = from_f<T>(0.f);
+        if constexpr (NBUF == 2) xsh1[rr * P + c - N] = from_f<T>(0.f);
       }
     }
     for (int i = tid0; i < C * (KC - C); i += Tl::NT) wt[(i / (KC - C)) * Tl::XS + C + i % (KC - C)] = from_f<T>(0.f);
@@ -616,7 +661,8 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
 #pragma unroll
   for (int k = 0; k <= MM; ++k) dloc[k] = 0.f;
   float accseg = 0.f;  // log-decay from the segment start to the chunk
-  const float* gap = pr.ks > 0 ? pr.gap_decay + ((int64_t)bh * pr.ns + q) * (pr.ks + 1) : nullptr;
+  if (tid0 <= pr.ks && pr.ks > 0)  // read after the first barrier
+    gap_s[tid0] = pr.gap_decay[((int64_t)bh * pr.ns + q) * (pr.ks + 1) + tid0];
   const unsigned ext_mask = (unsigned)q & ((1u << pr.ks) - 1u);  // active levels above
   auto slot_row = [&](int ks, int r, int g) __attribute__((always_inline)) {
     const int qs = ((q >> ks) << ks) + (1 << (ks - 1)) - 1;
@@ -628,10 +674,10 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   float la = 0.f;
   T lv[LAM_PREFETCH ? LPF : 1];
   frag zfirst[Tl::NKN];  // slot of the lowest level above the segment
-  auto issue_bx = [&](int j, int buf, int lane) __attribute__((always_inline)) {
+  auto issue_bx = [&](int j, T* bs, T* xs, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, Tl::NW>(Bm + (r0 * G + grp) * N, (int64_t)G * N, bsh[buf], wave, lane);
-    rows_to_lds<T, C, P, Tl::NW>(X + (r0 * H + h) * P, (int64_t)H * P, xsh[buf], wave, lane);
+    rows_to_lds<T, C, N, Tl::NW>(Bm + (r0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
+    rows_to_lds<T, C, P, Tl::NW>(X + (r0 * H + h) * P, (int64_t)H * P, xs, wave, lane);
   };
   auto issue_c = [&](int j, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
@@ -657,17 +703,20 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
       }
     }
   };
-  issue_bx(j0, 0, tid0 & 63);
+  issue_bx(j0, bsh0, xsh0, tid0 & 63);
   issue_c(j0, tid0 & 63);
   issue_regs(j0, tid0);
 
-  for (int jl = 0; jl < nch; ++jl) {
+  // one chunk per call; CUR selects the B / X buffer pair at compile time
+  auto step = [&](auto cur_c, int jl) __attribute__((always_inline)) {
+    constexpr int CUR = NBUF == 2 ? decltype(cur_c)::value : 0;
+    T* bs = CUR ? bsh1 : bsh0;
+    T* xs = CUR ? xsh1 : xsh0;
+    T* bs_next = NBUF == 2 ? (CUR ? bsh0 : bsh1) : bsh0;
+    T* xs_next = NBUF == 2 ? (CUR ? xsh0 : xsh1) : xsh0;
     const int j = j0 + jl;
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const bool need_state = jl + 1 < nch;
-    const int cur = NBUF == 2 ? (jl & 1) : 0;
-    const T* bs = bsh[cur];
-    const T* xs = xsh[cur];
     // Recompute lane-dependent LDS addresses inside the loop instead of
     // keeping dozens of them live across it (they would be spilled).
     int tid = tid0;
@@ -692,8 +741,8 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     }
     chunk_decays<T, C>(la, cum, ecum, wst, tid);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
-    __syncthreads();
-    if (NBUF == 2 && need_state) issue_bx(j + 1, cur ^ 1, lane);  // other buffer is free
+    lds_barrier();
+    if (NBUF == 2 && need_state) issue_bx(j + 1, bs_next, xs_next, lane);  // other pair is free
     const float atot = cum[C - 1];
 
     // ---- intra-chunk weights W[t][s], from the transposed scores B C^T
@@ -718,7 +767,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
       }
       store4(wt + Tl::at(t, 16 * sb + 4 * g), wv);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- output tiles, TH t-blocks at a time: intra block, then every
     // active inter-chunk level
@@ -771,7 +820,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
 #pragma unroll
           for (int kk = 0; kk < Tl::NKN; ++kk) znext[kk] = load_frag<T>(zr + kk * Tl::KB);
         }
-        add_level(zcur, c_log + m + ks, gap[ks] + accseg);
+        add_level(zcur, c_log + m + ks, gap_s[ks] + accseg);
 #pragma unroll
         for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = znext[kk];
       }
@@ -787,7 +836,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     }
 
     if (need_state) {
-      __syncthreads();  // every wave has read its C^T fragments
+      lds_barrier();  // every wave has read its C^T fragments
       issue_c(j + 1, lane);
       issue_regs(j + 1, tid);  // land during the state MFMAs
 
@@ -831,8 +880,12 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
       dloc[k] += atot;
       if (((jl + 1) & ((1 << (k - 1)) - 1)) == 0) dloc[k] = 0.f;
     }
-    __syncthreads();  // LDS is restaged by the next chunk
-    if (NBUF == 1 && need_state) issue_bx(j + 1, 0, lane);
+    lds_barrier();  // LDS is restaged by the next chunk
+    if (NBUF == 1 && need_state) issue_bx(j + 1, bs_next, xs_next, lane);
+  };
+  for (int jl = 0; jl < nch; jl += 2) {
+    step(std::integral_constant<int, 0>{}, jl);
+    if (jl + 1 < nch) step(std::integral_constant<int, 1>{}, jl + 1);
   }
 }
 
