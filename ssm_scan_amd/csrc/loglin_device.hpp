@@ -42,6 +42,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Upper bound on Fenwick depth over segments (supports 2^16 segments).
 constexpr int MAX_DEPTH = 16;
 
+// Level weights of one chunk sit in LDS as 32-bit words copied straight
+// from the lambda tensor: token t owns words [t W, t W + W) starting at the
+// word that holds its first weight.  W is odd, so 16 consecutive tokens read
+// 16 different banks.  bf16 rows may start in the upper half of a word.
+__host__ __device__ inline int lam_words(int ll, int esize) {
+  return esize == 4 ? (ll | 1) : (((ll + 1) / 2 + 1) | 1);
+}
+
 struct Params {
   const void* X;
   const void* Bm;
@@ -278,13 +286,26 @@ typedef __attribute__((address_space(1))) void* global_ptr_t;
 // arrays apart for these copies and would otherwise stall every later LDS
 // read on the copy in flight.  Callers publish the data with s_waitcnt
 // vmcnt(0) and a barrier before the first read of the destination.
-__device__ inline void dma_16x64(const void* src, const void* lds_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(lds_ptr_t)const_cast<void*>(lds_base));
+__device__ inline void dma_16x64(const void* src, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(m0)
                : "memory", "m0");
+}
+
+// Same with global_load_lds_dword: lane i copies 4 bytes to lds_byte + 4 i.
+__device__ inline void dma_4x64(const void* src, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+// Byte address of an LDS array element in the LDS aperture (32 bits).
+__device__ inline unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(lds_ptr_t)const_cast<void*>(p);
 }
 
 // Copy R token rows of W elements (global row stride `grs` elements) into
@@ -297,16 +318,16 @@ __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, in
   using L = Rows<T, W>;
   constexpr int PIECES = R * L::NBLK;  // 16-byte pieces of the tile
   constexpr int INSTS = (PIECES + 63) / 64;
-  constexpr int PER_INST = 1024 / (int)sizeof(T);  // elements per instruction
+  const int ws = __builtin_amdgcn_readfirstlane(wave);  // uniform: keep it scalar
 #pragma unroll
   for (int k = 0; k < (INSTS + NW - 1) / NW; ++k) {
-    const int inst = wave + k * NW;
+    const int inst = ws + k * NW;
     const int piece = inst * 64 + lane;
     if (inst < INSTS && piece < PIECES) {  // lanes past a short tile write nothing
       const int row = piece / L::NBLK, pb = piece % L::NBLK;
       const int lb = (pb ^ row) & (L::NBLK - 1);
       const T* src = g + (int64_t)row * grs + lb * L::VEC;
-      dma_16x64(src, lds + inst * PER_INST);
+      dma_16x64(src, lds_addr(lds) + inst * 1024u);
     }
   }
 }
@@ -615,7 +636,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   __shared__ __attribute__((aligned(16))) T wt[C * Tl::XS];       // W[t][s]
   __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
   __shared__ float gap_s[MAX_DEPTH + 1];  // gap log-decays of this segment
-  extern __shared__ float lam_s[];        // [C][ll | 1]
+  extern __shared__ unsigned lam_w[];     // [C][lam_words]: level weights
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
@@ -635,7 +656,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     for (int i = C + tid0; i < KC; i += Tl::NT) wst[i] = 0.f;
   }
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels, LL = pr.ll;
-  const int LLP = LL | 1;  // odd row stride: lambda lookups of 16 rows spread over banks
+  const int LW = lam_words(LL, (int)sizeof(T));
   const int h = tile % H;
   const int q = (tile / H) % pr.ns;
   const int b = tile / (H * pr.ns);
@@ -649,7 +670,6 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   const T* X = static_cast<const T*>(pr.X);
   const T* Bm = static_cast<const T*>(pr.Bm);
   const T* Cm = static_cast<const T*>(pr.Cm);
-  const T* lam = static_cast<const T*>(pr.lam);
   const T* slots = static_cast<const T*>(pr.slots);
   T* out = static_cast<T*>(pr.out);
 
@@ -669,10 +689,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     return slots + (((int64_t)bh * pr.ns + qs) * P + 16 * wave + r) * N + g * Tl::KPL;
   };
 
-  constexpr int LPF = (C * 32 + Tl::NT - 1) / Tl::NT;  // lambda values per thread (<= 32 levels)
-  constexpr bool LAM_PREFETCH = LPF <= 8;
   float la = 0.f;
-  T lv[LAM_PREFETCH ? LPF : 1];
   frag zfirst[Tl::NKN];  // slot of the lowest level above the segment
   auto issue_bx = [&](int j, T* bs, T* xs, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
@@ -692,19 +709,38 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
       for (int kk = 0; kk < Tl::NKN; ++kk) zfirst[kk] = load_frag<T>(zr + kk * Tl::KB);
     }
     la = tid < C ? pr.log_a[(r0 + tid) * H + h] : 0.f;
-    if constexpr (LAM_PREFETCH) {
-#pragma unroll
-      for (int k = 0; k < LPF; ++k) {
-        const int idx = tid + k * Tl::NT;
-        if (idx < C * LL) {
-          const int tau = idx / LL, l = idx - tau * LL;
-          lv[k] = lam[((r0 + tau) * H + h) * L + l];
-        }
+  };
+  // level weights of chunk j into lam_w (the last word of the tensor bounds
+  // the copy: a row's padding words may run past the end)
+  const int64_t lam_last_word = ((int64_t)pr.batch * pr.seqlen * H * L * (int64_t)sizeof(T) - 4) / 4;
+  auto issue_lam = [&](int j, int lane) __attribute__((always_inline)) {
+    const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    const int words = C * LW;
+    for (int inst = __builtin_amdgcn_readfirstlane(wave); inst * 64 < words; inst += Tl::NW) {
+      const int idx = inst * 64 + lane;
+      if (idx < words) {
+        const int t = idx / LW, w = idx - t * LW;
+        const int64_t e0 = ((r0 + t) * H + h) * L;
+        int64_t gw = (sizeof(T) == 4 ? e0 : (e0 >> 1)) + w;
+        gw = gw < lam_last_word ? gw : lam_last_word;
+        dma_4x64(static_cast<const unsigned*>(pr.lam) + gw, lds_addr(lam_w) + inst * 256u);
       }
     }
   };
+  // weight of level lvl for token t of the current chunk; par: t's row
+  // starts in the upper half of its first word (bf16, odd level count)
+  auto lam_at = [&](int t, int lvl, int par) __attribute__((always_inline)) -> float {
+    if constexpr (sizeof(T) == 4) {
+      return __uint_as_float(lam_w[t * LW + lvl]);
+    } else {
+      const unsigned short* hw = reinterpret_cast<const unsigned short*>(lam_w);
+      return __uint_as_float((unsigned)hw[2 * t * LW + par + lvl] << 16);
+    }
+  };
+  const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
   issue_c(j0, tid0 & 63);
+  issue_lam(j0, tid0 & 63);
   issue_regs(j0, tid0);
 
   // one chunk per call; CUR selects the B / X buffer pair at compile time
@@ -723,22 +759,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, g = lane >> 4, r = lane & 15;
 
-    // ---- stage lambda and the per-token decays
-    if constexpr (LAM_PREFETCH) {
-#pragma unroll
-      for (int k = 0; k < LPF; ++k) {
-        const int idx = tid + k * Tl::NT;
-        if (idx < C * LL) {
-          const int tau = idx / LL, l = idx - tau * LL;
-          lam_s[tau * LLP + l] = to_f(lv[k]);
-        }
-      }
-    } else {
-      for (int idx = tid; idx < C * LL; idx += Tl::NT) {
-        const int tau = idx / LL, l = idx - tau * LL;
-        lam_s[tau * LLP + l] = to_f(lam[((row0 + tau) * H + h) * L + l]);
-      }
-    }
+    // ---- per-token decays of the chunk
     chunk_decays<T, C>(la, cum, ecum, wst, tid);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     lds_barrier();
@@ -758,10 +779,11 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
           acc = M::mma(frag_along<T, RB>(bs, 16 * sb + r, kk * Tl::KB, g),
                        frag_along<T, RB>(csh, t, kk * Tl::KB, g), acc);
         const float ct_ = cum[t];
+        const int par = lpar & (((int)row0 + t) * H + h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * sb + 4 * g + i;
-          wv[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[s]) * lam_s[t * LLP + bit_length(t ^ s)]
+          wv[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[s]) * lam_at(t, bit_length(t ^ s), par)
                            : 0.f;
         }
       }
@@ -771,7 +793,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
 
     // ---- output tiles, TH t-blocks at a time: intra block, then every
     // active inter-chunk level
-    constexpr int TH = Tl::TB < 2 ? Tl::TB : 2;
+    constexpr int TH = Tl::TB;
 #pragma unroll
     for (int t0 = 0; t0 < Tl::TB; t0 += TH) {
       f32x4 Y[TH];
@@ -800,7 +822,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
 #pragma unroll
           for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[i][kk], tmp);
           const int t = 16 * (t0 + i) + r;
-          const float sc = lam_s[t * LLP + level] * ecum[t] * eD;
+          const float sc = lam_at(t, level, lpar & (((int)row0 + t) * H + h)) * ecum[t] * eD;
           Y[i] += sc * tmp;
         }
       };
@@ -838,6 +860,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     if (need_state) {
       lds_barrier();  // every wave has read its C^T fragments
       issue_c(j + 1, lane);
+      issue_lam(j + 1, lane);
       issue_regs(j + 1, tid);  // land during the state MFMAs
 
       // ---- this chunk's state, pushed on the local Fenwick stack

@@ -30,7 +30,7 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   }
   record(ev, 2, st);
   pr.total = pr.batch * pr.ns * pr.nheads;
-  const size_t shm = (size_t)C * (pr.ll | 1) * sizeof(float);
+  const size_t shm = (size_t)C * lam_words(pr.ll, (int)sizeof(T)) * 4;
   hipLaunchKernelGGL((output_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), shm, st, pr);
   record(ev, 3, st);
   return (int)hipGetLastError();
