@@ -68,6 +68,7 @@ struct Params {
   int ns;     // segments
   int ks;     // log2(ns)
   int ll;     // levels used: log2(seqlen) + 1
+  int hp;     // heads per work-group of the output pass (1 or 2)
   int total;  // logical work-groups of the kernel being launched
 };
 
@@ -598,69 +599,113 @@ __device__ inline void score_tile(int u, int& tb, int& sb) {
   }
 }
 
-// One work-group per (batch, segment of 2^m chunks, head); the chunks of the
-// segment are processed in order.  Wave w owns output columns [16w, 16w+16)
-// of the head for all C tokens of a chunk (TB tiles of Y^T), and the same
-// columns of every chunk state it builds.
+// One work-group per (batch, segment of 2^m chunks, HP heads of one group);
+// the chunks of the segment are processed in order.  The HP heads share
+// the group's B and C rows and the scores C B^T; wave w serves head
+// w / (P/16) and owns its output columns [16 (w mod P/16), +16) for all C
+// tokens of a chunk (TB tiles of Y^T), and the same columns of every chunk
+// state it builds.
 //
 // Inter-chunk level k of chunk j reads the lower half of j's 2^k-chunk
 // block.  For k > m that block is a run of whole segments: its sum is slot
 // ((q >> ks) << ks) + 2^(ks-1) - 1 of pass 2 (ks = k - m), shared by every
-// chunk of the segment.  For k <= m it lies inside the segment: the wave
-// keeps a Fenwick stack of those block sums, entry e holding the block of
-// 2^e chunks that ends just before the current chunk, as MFMA A-operand
-// fragments.  The state MFMA leaves a lane exactly the rows its own
-// fragments need, so the stack never crosses lanes.
+// chunk of the segment.  The first NR of those slots stay in LDS for the
+// whole segment; the others are fetched per chunk.  For k <= m the block
+// lies inside the segment: the wave keeps a Fenwick stack of those block
+// sums, entry e holding the block of 2^e chunks that ends just before the
+// current chunk, as MFMA A-operand fragments.  The state MFMA leaves a lane
+// exactly the rows its own fragments need, so the stack never crosses
+// lanes.
 //
 // B and X rows are double-buffered in LDS (bf16): the next chunk's rows are
 // requested right after the current chunk's first barrier.  C rows are
 // single-buffered and refilled once the output tiles have read them.
-template <class T, int C, int P, int N>
-__global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Params pr) {
+template <class T, int C, int P, int N, int HP>
+struct OutCfg {
+  using Tl = Tiles<T, C, P, N>;
+  static constexpr int NWH = Tl::NW;    // waves per head
+  static constexpr int NTW = HP * NWH;  // waves per work-group
+  static constexpr int NT = NTW * 64;
+  static constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int KC = Tl::KC;
+  static constexpr int LAM_MAX = HP * C * (sizeof(T) == 2 ? 17 : 33) * 4;  // <= 32 levels
+  static constexpr int STATIC_LDS =
+      (int)sizeof(T) * (NBUF * KC * N + C * N + HP * NBUF * KC * P + HP * C * Tl::XS) +
+      4 * (HP * (2 * C + KC) + HP * (MAX_DEPTH + 1));
+  static constexpr int SLOT_BYTES = HP * P * N * (int)sizeof(T);
+  // resident slots only where a work-group holds the whole CU anyway
+  static constexpr int NR_FIT = (160 * 1024 - STATIC_LDS - LAM_MAX - 2048) / SLOT_BYTES;
+  static constexpr int NR = HP == 1 ? 0 : (NR_FIT > MAX_DEPTH ? MAX_DEPTH : NR_FIT);
+  static constexpr int MIN_BLOCKS = HP == 1 ? 2 : 1;
+};
+
+template <class T, int C, int P, int N, int HP>
+__global__ __launch_bounds__((OutCfg<T, C, P, N, HP>::NT), (OutCfg<T, C, P, N, HP>::MIN_BLOCKS))
+void output_kernel(Params pr) {
+  using Cfg = OutCfg<T, C, P, N, HP>;
   using Tl = Tiles<T, C, P, N>;
   using M = Mfma<T>;
   using frag = typename M::frag;
   using RB = Rows<T, N>;
   using RX = Rows<T, P>;
   constexpr int MM = MAX_SEG_LOG2;
-  constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;
+  constexpr int NBUF = Cfg::NBUF;
+  constexpr int NR = Cfg::NR;
+  constexpr int NTW = Cfg::NTW;
   constexpr int KC = Tl::KC;  // token rows of the B / X tiles; rows C..KC-1 stay zero
+  constexpr int GS = MAX_DEPTH + 1;
   // B and X rows, two named buffers each (bf16; fp32 uses only the first)
   // so that the compiler can tell the asynchronous fill of one from reads
-  // of the other and does not wait for it.
+  // of the other and does not wait for it.  X, W and the per-token arrays
+  // hold HP heads back to back.
   __shared__ __attribute__((aligned(1024))) T bsh0[KC * N];
   __shared__ __attribute__((aligned(1024))) T bsh1[NBUF == 2 ? KC * N : 1];
-  __shared__ __attribute__((aligned(1024))) T xsh0[KC * P];
-  __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? KC * P : 1];
-  __shared__ __attribute__((aligned(1024))) T csh[C * N];         // C rows
-  __shared__ __attribute__((aligned(16))) T wt[C * Tl::XS];       // W[t][s]
-  __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
-  __shared__ float gap_s[MAX_DEPTH + 1];  // gap log-decays of this segment
-  extern __shared__ unsigned lam_w[];     // [C][lam_words]: level weights
+  __shared__ __attribute__((aligned(1024))) T xsh0[HP * KC * P];
+  __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? HP * KC * P : 1];
+  __shared__ __attribute__((aligned(1024))) T csh[C * N];          // C rows
+  __shared__ __attribute__((aligned(1024))) T zres[NR ? HP * NR * P * N : 1];  // resident slots
+  __shared__ __attribute__((aligned(16))) T wt[HP * C * Tl::XS];   // W[t][s]
+  __shared__ __attribute__((aligned(16))) float cum[HP * C], ecum[HP * C], wst[HP * KC];
+  __shared__ float gap_s[HP * GS];     // gap log-decays of this segment
+  extern __shared__ unsigned lam_w[];  // [HP][C][lam_words]: level weights
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
-  const int tid0 = threadIdx.x, wave = tid0 >> 6;
+  const int tid0 = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // uniform: keep it scalar
+  const int hh = wave / Cfg::NWH;  // head of this wave within the work-group
+  const int wv = wave % Cfg::NWH;  // its 16-column block
   if (KC > C) {  // contraction padding of the token tiles and of W stays zero
-    for (int i = tid0; i < (KC - C) * (N + P); i += Tl::NT) {
-      const int rr = C + i / (N + P), c = i % (N + P);
+    for (int i = tid0; i < (KC - C) * (N + HP * P); i += Cfg::NT) {
+      const int rr = C + i / (N + HP * P), c = i % (N + HP * P);
       if (c < N) {
         bsh0[rr * N + c] = from_f<T>(0.f);
         if constexpr (NBUF == 2) bsh1[rr * N + c] = from_f<T>(0.f);
       } else {
-        xsh0[rr * P + c - N] = from_f<T>(0.f);
-        if constexpr (NBUF == 2) xsh1[rr * P + c - N] = from_f<T>(0.f);
+        const int x = c - N, o = (x / P) * KC * P + rr * P + x % P;
+        xsh0[o] = from_f<T>(0.f);
+        if constexpr (NBUF == 2) xsh1[o] = from_f<T>(0.f);
       }
     }
-    for (int i = tid0; i < C * (KC - C); i += Tl::NT) wt[(i / (KC - C)) * Tl::XS + C + i % (KC - C)] = from_f<T>(0.f);
-    for (int i = C + tid0; i < KC; i += Tl::NT) wst[i] = 0.f;
+    for (int i = tid0; i < HP * C * (KC - C); i += Cfg::NT) {
+      const int row = i / (KC - C);  // head-major rows of W
+      wt[row * Tl::XS + C + i % (KC - C)] = from_f<T>(0.f);
+    }
+    for (int i = tid0; i < HP * (KC - C); i += Cfg::NT) wst[(i / (KC - C)) * KC + C + i % (KC - C)] = 0.f;
   }
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels, LL = pr.ll;
   const int LW = lam_words(LL, (int)sizeof(T));
-  const int h = tile % H;
-  const int q = (tile / H) % pr.ns;
-  const int b = tile / (H * pr.ns);
-  const int grp = h / (H / G);
+  // Heads of one group next to each other (they share B and C), then
+  // segments, then groups: the work-groups resident on one XCD at a time
+  // cover few heads and many segments, so the level slots they read stay
+  // in that XCD's L2.
+  const int hpg = H / G, npair = hpg / HP;
+  const int pi = tile % npair;
+  const int q = (tile / npair) % pr.ns;
+  const int grp = (tile / (npair * pr.ns)) % G;
+  const int b = tile / (npair * pr.ns * G);
+  const int h0 = grp * hpg + pi * HP;  // first head of the work-group
+  const int h = h0 + hh;               // head of this wave
   const int bh = b * H + h;
   const int c_log = __builtin_ctz(C);
   const int m = pr.m;
@@ -672,6 +717,10 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   const T* Cm = static_cast<const T*>(pr.Cm);
   const T* slots = static_cast<const T*>(pr.slots);
   T* out = static_cast<T*>(pr.out);
+  float* cum_h = cum + hh * C;
+  float* ecum_h = ecum + hh * C;
+  float* wst_h = wst + hh * KC;
+  const float* gap_h = gap_s + hh * GS;
 
   frag zl[MM][Tl::NKN];  // local Fenwick stack (entry e: 2^e chunks)
   float zla[MM];         // total log-decay of each entry's block
@@ -681,63 +730,89 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
 #pragma unroll
   for (int k = 0; k <= MM; ++k) dloc[k] = 0.f;
   float accseg = 0.f;  // log-decay from the segment start to the chunk
-  if (tid0 <= pr.ks && pr.ks > 0)  // read after the first barrier
-    gap_s[tid0] = pr.gap_decay[((int64_t)bh * pr.ns + q) * (pr.ks + 1) + tid0];
+  if (pr.ks > 0) {     // read after the first barrier
+    for (int i = tid0; i < HP * (pr.ks + 1); i += Cfg::NT) {
+      const int k = i / (pr.ks + 1), l = i % (pr.ks + 1);
+      gap_s[k * GS + l] = pr.gap_decay[((int64_t)(b * H + h0 + k) * pr.ns + q) * (pr.ks + 1) + l];
+    }
+  }
   const unsigned ext_mask = (unsigned)q & ((1u << pr.ks) - 1u);  // active levels above
-  auto slot_row = [&](int ks, int r, int g) __attribute__((always_inline)) {
+  auto slot_of = [&](int hd, int ks) __attribute__((always_inline)) {
     const int qs = ((q >> ks) << ks) + (1 << (ks - 1)) - 1;
-    return slots + (((int64_t)bh * pr.ns + qs) * P + 16 * wave + r) * N + g * Tl::KPL;
+    return slots + ((int64_t)(b * H + hd) * pr.ns + qs) * P * N;
   };
+  // levels past the resident ones are fetched per chunk
+  unsigned stream_mask = ext_mask;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) stream_mask &= stream_mask - 1;
 
   float la = 0.f;
-  frag zfirst[Tl::NKN];  // slot of the lowest level above the segment
+  frag zfirst[Tl::NKN];  // first streamed level slot
   auto issue_bx = [&](int j, T* bs, T* xs, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, Tl::NW>(Bm + (r0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
-    rows_to_lds<T, C, P, Tl::NW>(X + (r0 * H + h) * P, (int64_t)H * P, xs, wave, lane);
+    rows_to_lds<T, C, N, NTW>(Bm + (r0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
+#pragma unroll
+    for (int k = 0; k < HP; ++k)
+      rows_to_lds<T, C, P, NTW>(X + (r0 * H + h0 + k) * P, (int64_t)H * P, xs + k * KC * P, wave, lane);
   };
   auto issue_c = [&](int j, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, Tl::NW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, csh, wave, lane);
+    rows_to_lds<T, C, N, NTW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, csh, wave, lane);
   };
   auto issue_regs = [&](int j, int tid) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    const int r = tid & 15, g = (tid >> 4) & 3;
-    if (ext_mask) {
-      const T* zr = slot_row(__builtin_ctz(ext_mask) + 1, r, g);
+    const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+    if (stream_mask) {
+      const T* zr = slot_of(h, __builtin_ctz(stream_mask) + 1) + (16 * wv + r) * N + g * Tl::KPL;
 #pragma unroll
       for (int kk = 0; kk < Tl::NKN; ++kk) zfirst[kk] = load_frag<T>(zr + kk * Tl::KB);
     }
-    la = tid < C ? pr.log_a[(r0 + tid) * H + h] : 0.f;
+    la = (wv == 0 && lane < C) ? pr.log_a[(r0 + lane) * H + h] : 0.f;
   };
   // level weights of chunk j into lam_w (the last word of the tensor bounds
   // the copy: a row's padding words may run past the end)
   const int64_t lam_last_word = ((int64_t)pr.batch * pr.seqlen * H * L * (int64_t)sizeof(T) - 4) / 4;
   auto issue_lam = [&](int j, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    const int words = C * LW;
-    for (int inst = __builtin_amdgcn_readfirstlane(wave); inst * 64 < words; inst += Tl::NW) {
+    const int words = HP * C * LW;
+    for (int inst = __builtin_amdgcn_readfirstlane(wave); inst * 64 < words; inst += NTW) {
       const int idx = inst * 64 + lane;
       if (idx < words) {
-        const int t = idx / LW, w = idx - t * LW;
-        const int64_t e0 = ((r0 + t) * H + h) * L;
+        const int tw = idx / LW, w = idx - tw * LW;  // tw = head * C + token
+        const int k = tw / C, t = tw - k * C;
+        const int64_t e0 = ((r0 + t) * H + h0 + k) * L;
         int64_t gw = (sizeof(T) == 4 ? e0 : (e0 >> 1)) + w;
         gw = gw < lam_last_word ? gw : lam_last_word;
         dma_4x64(static_cast<const unsigned*>(pr.lam) + gw, lds_addr(lam_w) + inst * 256u);
       }
     }
   };
-  // weight of level lvl for token t of the current chunk; par: t's row
-  // starts in the upper half of its first word (bf16, odd level count)
-  auto lam_at = [&](int t, int lvl, int par) __attribute__((always_inline)) -> float {
+  // weight of level lvl for token t of head h0 + k in the current chunk;
+  // par: the row starts in the upper half of its first word (bf16, odd
+  // level count)
+  auto lam_at = [&](int k, int t, int lvl, int par) __attribute__((always_inline)) -> float {
+    const int row = k * C + t;
     if constexpr (sizeof(T) == 4) {
-      return __uint_as_float(lam_w[t * LW + lvl]);
+      return __uint_as_float(lam_w[row * LW + lvl]);
     } else {
       const unsigned short* hw = reinterpret_cast<const unsigned short*>(lam_w);
-      return __uint_as_float((unsigned)hw[2 * t * LW + par + lvl] << 16);
+      return __uint_as_float((unsigned)hw[2 * row * LW + par + lvl] << 16);
     }
   };
   const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
+  if constexpr (NR > 0) {  // resident slots, published by the first barrier
+    unsigned mk = ext_mask;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (mk) {
+        const int ks = __builtin_ctz(mk) + 1;
+        mk &= mk - 1;
+#pragma unroll
+        for (int k = 0; k < HP; ++k)
+          rows_to_lds<T, P, N, NTW>(slot_of(h0 + k, ks), N, zres + (k * NR + i) * P * N, wave, tid0 & 63);
+      }
+    }
+  }
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
   issue_c(j0, tid0 & 63);
   issue_lam(j0, tid0 & 63);
@@ -747,7 +822,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
   auto step = [&](auto cur_c, int jl) __attribute__((always_inline)) {
     constexpr int CUR = NBUF == 2 ? decltype(cur_c)::value : 0;
     T* bs = CUR ? bsh1 : bsh0;
-    T* xs = CUR ? xsh1 : xsh0;
+    T* xsb = CUR ? xsh1 : xsh0;
     T* bs_next = NBUF == 2 ? (CUR ? bsh0 : bsh1) : bsh0;
     T* xs_next = NBUF == 2 ? (CUR ? xsh0 : xsh1) : xsh0;
     const int j = j0 + jl;
@@ -758,78 +833,98 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
     int tid = tid0;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const T* xs = xsb + hh * KC * P;
 
-    // ---- per-token decays of the chunk
-    chunk_decays<T, C>(la, cum, ecum, wst, tid);
+    // ---- per-token decays of the chunk (first wave of each head)
+    if (wv == 0) chunk_decays<T, C>(la, cum_h, ecum_h, wst_h, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     lds_barrier();
     if (NBUF == 2 && need_state) issue_bx(j + 1, bs_next, xs_next, lane);  // other pair is free
-    const float atot = cum[C - 1];
+    const float atot = cum_h[C - 1];
 
-    // ---- intra-chunk weights W[t][s], from the transposed scores B C^T
-    for (int u = wave; u < Tl::TB * Tl::TB; u += Tl::NW) {
+    // ---- intra-chunk weights W[t][s] of every head, from the shared
+    // transposed scores B C^T
+    for (int u = wave; u < Tl::TB * Tl::TB; u += NTW) {
       int tb, sb;
       score_tile<Tl::TB>(u, tb, sb);
       const int t = 16 * tb + r;
-      f32x4 wv = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (sb <= tb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < Tl::NKN; ++kk)
           acc = M::mma(frag_along<T, RB>(bs, 16 * sb + r, kk * Tl::KB, g),
                        frag_along<T, RB>(csh, t, kk * Tl::KB, g), acc);
-        const float ct_ = cum[t];
-        const int par = lpar & (((int)row0 + t) * H + h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * sb + 4 * g + i;
-          wv[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[s]) * lam_at(t, bit_length(t ^ s), par)
-                           : 0.f;
-        }
       }
-      store4(wt + Tl::at(t, 16 * sb + 4 * g), wv);
+#pragma unroll
+      for (int k = 0; k < HP; ++k) {
+        f32x4 wv4 = {0.f, 0.f, 0.f, 0.f};
+        if (sb <= tb) {
+          const float ct_ = cum[k * C + t];
+          const int par = lpar & (((int)row0 + t) * H + h0 + k);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = 16 * sb + 4 * g + i;
+            wv4[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[k * C + s]) *
+                                    lam_at(k, t, bit_length(t ^ s), par)
+                              : 0.f;
+          }
+        }
+        store4(wt + k * C * Tl::XS + Tl::at(t, 16 * sb + 4 * g), wv4);
+      }
     }
     lds_barrier();
 
-    // ---- output tiles, TH t-blocks at a time: intra block, then every
-    // active inter-chunk level
-    constexpr int TH = Tl::TB;
+    // ---- output tiles: intra block, then every active inter-chunk level
+    {
+      const T* wth = wt + hh * C * Tl::XS;
+      const int par_r = lpar & (((int)row0 + r) * H + h);  // parity of token 16 tb + r
+      f32x4 Y[Tl::TB];
+      frag cf[Tl::TB][Tl::NKN];  // C^T fragments in state order
 #pragma unroll
-    for (int t0 = 0; t0 < Tl::TB; t0 += TH) {
-      f32x4 Y[TH];
-      frag cf[TH][Tl::NKN];  // C^T fragments in state order
-#pragma unroll
-      for (int i = 0; i < TH; ++i) {
-        const int tb = t0 + i;
-        Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < Tl::TB; ++tb) {
+        Y[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < Tl::NKT; ++kt) {
           if (kt * Tl::KB < 16 * (tb + 1)) {
-            auto af = frag_down<T, RX>(xs, kt * Tl::KB, 16 * wave, g, r);
-            auto bf = load_frag<T>(wt + Tl::at(16 * tb + r, kt * Tl::KB + g * Tl::KPL));
-            Y[i] = M::mma(af, bf, Y[i]);
+            auto af = frag_down<T, RX>(xs, kt * Tl::KB, 16 * wv, g, r);
+            auto bf = load_frag<T>(wth + Tl::at(16 * tb + r, kt * Tl::KB + g * Tl::KPL));
+            Y[tb] = M::mma(af, bf, Y[tb]);
           }
         }
 #pragma unroll
-        for (int kk = 0; kk < Tl::NKN; ++kk) cf[i][kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
+        for (int kk = 0; kk < Tl::NKN; ++kk) cf[tb][kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
       }
 
       auto add_level = [&](const frag* zf, int level, float D) __attribute__((always_inline)) {
         const float eD = M::ex(D);
 #pragma unroll
-        for (int i = 0; i < TH; ++i) {
+        for (int tb = 0; tb < Tl::TB; ++tb) {
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[i][kk], tmp);
-          const int t = 16 * (t0 + i) + r;
-          const float sc = lam_at(t, level, lpar & (((int)row0 + t) * H + h)) * ecum[t] * eD;
-          Y[i] += sc * tmp;
+          for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[tb][kk], tmp);
+          const int t = 16 * tb + r;
+          // 16 tb keeps the parity of the row start: H * 16 tb is even
+          const float sc = lam_at(hh, t, level, par_r) * ecum_h[t] * eD;
+          Y[tb] += sc * tmp;
         }
       };
 
-      // levels above the segment; the first slot is in registers already,
-      // the others are loaded one level ahead
+      // levels above the segment: resident slots from LDS, then the others
+      // from memory (the first one is in registers already, the rest are
+      // loaded one level ahead)
       unsigned mask = ext_mask;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (mask) {
+          const int ks = __builtin_ctz(mask) + 1;
+          mask &= mask - 1;
+          frag zf[Tl::NKN];
+          const T* zt = zres + (hh * NR + i) * P * N;
+#pragma unroll
+          for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = frag_along<T, RB>(zt, 16 * wv + r, kk * Tl::KB, g);
+          add_level(zf, c_log + m + ks, gap_h[ks] + accseg);
+        }
+      }
       frag zcur[Tl::NKN];
 #pragma unroll
       for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = zfirst[kk];
@@ -838,11 +933,11 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
         mask &= mask - 1;
         frag znext[Tl::NKN];
         if (mask) {
-          const T* zr = slot_row(__builtin_ctz(mask) + 1, r, g);
+          const T* zr = slot_of(h, __builtin_ctz(mask) + 1) + (16 * wv + r) * N + g * Tl::KPL;
 #pragma unroll
           for (int kk = 0; kk < Tl::NKN; ++kk) znext[kk] = load_frag<T>(zr + kk * Tl::KB);
         }
-        add_level(zcur, c_log + m + ks, gap_s[ks] + accseg);
+        add_level(zcur, c_log + m + ks, gap_h[ks] + accseg);
 #pragma unroll
         for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = znext[kk];
       }
@@ -851,9 +946,9 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
         if (e < m && ((jl >> e) & 1)) add_level(zl[e], c_log + e + 1, dloc[e + 1]);
       }
 #pragma unroll
-      for (int i = 0; i < TH; ++i) {
-        const int t = 16 * (t0 + i) + r;
-        store4(out + ((row0 + t) * H + h) * P + 16 * wave + 4 * g, Y[i]);
+      for (int tb = 0; tb < Tl::TB; ++tb) {
+        const int t = 16 * tb + r;
+        store4(out + ((row0 + t) * H + h) * P + 16 * wv + 4 * g, Y[tb]);
       }
     }
 
@@ -867,7 +962,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT), 2) void output_kernel(Para
       f32x4 S[Tl::NB];
 #pragma unroll
       for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      chunk_state_mma<T, C, P, N>(bs, xs, wst, S, wave, g, r);
+      chunk_state_mma<T, C, P, N>(bs, xs, wst_h, S, wv, g, r);
       // merge with the entries of the blocks this chunk completes
       const int z = __builtin_ctz(~(unsigned)jl);  // trailing ones of jl
       float cur_a = atot;

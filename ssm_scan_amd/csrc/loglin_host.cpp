@@ -30,7 +30,7 @@ bool supported_shape(int dtype, int64_t P, int64_t N) {
 }
 
 struct Plan {
-  int nc, kc, m, ns, ks, ll;
+  int nc, kc, m, ns, ks, ll, hp;
   size_t off_state, off_decay, off_slots, off_gap, bytes;
 };
 
@@ -57,8 +57,14 @@ int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) 
   // block a chunk reads lies before it.
   const int kc = ceil_log2(nc);
   int m = kc < loglin::MAX_SEG_LOG2 ? kc : loglin::MAX_SEG_LOG2;
+  int hp = 1;
   if (o) {
-    if (o->reserved != 0) return LOGLIN_ERR_OPTS;
+    if (o->heads_per_block < 0 || o->heads_per_block > 2) return LOGLIN_ERR_OPTS;
+    if (o->heads_per_block == 2) {
+      if (d->io_dtype != LOGLIN_BF16 || d->headdim != 64 || (d->nheads / d->ngroups) % 2)
+        return LOGLIN_ERR_OPTS;
+      hp = 2;
+    }
     if (o->seg_log2 < -1 || o->seg_log2 > loglin::MAX_SEG_LOG2) return LOGLIN_ERR_OPTS;
     if (o->seg_log2 > kc) return LOGLIN_ERR_OPTS;
     if (o->seg_log2 >= 0) m = o->seg_log2;
@@ -73,6 +79,7 @@ int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) 
   pl->ns = (int)ns;
   pl->ks = ks;
   pl->ll = ceil_log2(d->seqlen) + 1;
+  pl->hp = hp;
   const size_t bh = (size_t)(d->batch * d->nheads);
   const size_t pn = (size_t)(d->headdim * d->dstate);
   const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;
@@ -188,6 +195,7 @@ int loglin_fwd_ex(const void* X, const void* B, const void* C, const float* log_
   pr.ns = pl.ns;
   pr.ks = pl.ks;
   pr.ll = pl.ll;
+  pr.hp = pl.hp;
   void* const* ev = opts ? opts->stage_events : nullptr;
   int herr = fn(pr, static_cast<hipStream_t>(stream), ev);
   return herr ? LOGLIN_ERR_HIP : LOGLIN_OK;

@@ -13,6 +13,14 @@ inline void record(void* const* ev, int i, hipStream_t st) {
   if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
 }
 
+template <class T, int C, int P, int N, int HP>
+void launch_output(Params pr, hipStream_t st) {
+  using Cfg = OutCfg<T, C, P, N, HP>;
+  pr.total = pr.batch * pr.ns * (pr.nheads / HP);
+  const size_t shm = (size_t)HP * C * lam_words(pr.ll, (int)sizeof(T)) * 4;
+  hipLaunchKernelGGL((output_kernel<T, C, P, N, HP>), dim3(pad8(pr.total)), dim3(Cfg::NT), shm, st, pr);
+}
+
 // Returns 0 or hipError_t of the first failing launch (caller maps it).
 template <class T, int C, int P, int N>
 int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
@@ -29,9 +37,13 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
     record(ev, 1, st);
   }
   record(ev, 2, st);
-  pr.total = pr.batch * pr.ns * pr.nheads;
-  const size_t shm = (size_t)C * lam_words(pr.ll, (int)sizeof(T)) * 4;
-  hipLaunchKernelGGL((output_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), shm, st, pr);
+  // pairs of heads of one group (shared B, C and scores) where requested;
+  // the host only accepts that for bf16 with 64 columns
+  constexpr bool PAIRS = sizeof(T) == 2 && P == 64;
+  if (PAIRS && pr.hp == 2)
+    launch_output<T, C, P, N, PAIRS ? 2 : 1>(pr, st);
+  else
+    launch_output<T, C, P, N, 1>(pr, st);
   record(ev, 3, st);
   return (int)hipGetLastError();
 }

@@ -33,12 +33,12 @@ def to_device(d, cfg, dev="cuda"):
     return t
 
 
-def run_gpu(cfg, t, chunk=None, seg_log2=None, out=None, stream=None):
+def run_gpu(cfg, t, chunk=None, seg_log2=None, out=None, stream=None, heads_per_block=None):
     chunk = chunk or cfg.chunk
     if out is None:
         out = torch.empty_like(t["X"])
     L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], chunk, out,
-                 seg_log2=seg_log2, stream=stream)
+                 seg_log2=seg_log2, stream=stream, heads_per_block=heads_per_block)
     return out
 
 

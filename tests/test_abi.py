@@ -90,16 +90,33 @@ def test_workspace_errors():
 
 def test_options_errors():
     o = L.loglin_opts()
-    o.seg_log2, o.reserved = -2, 0
+    o.seg_log2, o.heads_per_block = -2, 0
     assert validate(good_dims(), opts=o) == -12
-    o.seg_log2, o.reserved = 0, 1
+    o.seg_log2, o.heads_per_block = 0, 3
     assert validate(good_dims(), opts=o) == -12
-    o.seg_log2, o.reserved = 4, 0  # deeper than the on-chip stack
+    o.seg_log2, o.heads_per_block = 4, 0  # deeper than the on-chip stack
     assert validate(good_dims(), opts=o) == -12
     o.seg_log2 = 2  # deeper than log2 of the chunk count (2 chunks)
     assert validate(good_dims(seqlen=128, nlevels=8), opts=o) == -12
     o.seg_log2 = 1
     assert validate(good_dims(seqlen=128, nlevels=8), opts=o) == 0
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(), True), (dict(ngroups=48), False), (dict(ngroups=16), False),
+    (dict(ngroups=12), True), (dict(headdim=32), False),
+    (dict(io_dtype=L.LOGLIN_F32), False),
+])
+def test_head_pairs_option(kw, ok):
+    """Two heads per work-group need bf16, 64 columns and an even number of
+    heads per group; one head is always accepted."""
+    o = L.loglin_opts()
+    o.seg_log2 = -1
+    for hp in (0, 1):
+        o.heads_per_block = hp
+        assert validate(good_dims(**kw), opts=o) == 0
+    o.heads_per_block = 2
+    assert validate(good_dims(**kw), opts=o) == (0 if ok else -12)
 
 
 def test_null_dims():

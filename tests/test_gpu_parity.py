@@ -17,11 +17,12 @@ from .gpu_helpers import (max_rel_err, run_gpu, say, small_cfg, to_device, tol_o
 pytestmark = pytest.mark.gpu
 
 
-def check(cfg, seed=0, variant=None, chunk=None, seg_log2=None):
-    say(f"[parity] {cfg.name} seed={seed} variant={variant} chunk={chunk} seg={seg_log2}")
+def check(cfg, seed=0, variant=None, chunk=None, seg_log2=None, heads_per_block=None):
+    say(f"[parity] {cfg.name} seed={seed} variant={variant} chunk={chunk} seg={seg_log2} "
+        f"hp={heads_per_block}")
     d = inputs.make_inputs(cfg, seed, variant=variant)
     t = to_device(d, cfg)
-    out = run_gpu(cfg, t, chunk=chunk, seg_log2=seg_log2)
+    out = run_gpu(cfg, t, chunk=chunk, seg_log2=seg_log2, heads_per_block=heads_per_block)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"])
@@ -152,3 +153,45 @@ def test_extra_levels_ignored():
     b = run_gpu(cfg, t2)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("H,G", [(2, 2), (3, 1), (4, 1), (6, 3)])
+def test_head_grouping(H, G):
+    """Heads per group 1, 3, 4 and 2 with one head per work-group."""
+    check(small_cfg(T=1344, H=H, G=G), variant="slow_decay")
+
+
+@pytest.mark.parametrize("T,seg", [(1344, None), (64 * 33, None), (64 * 64, None), (2048, 1),
+                                   (2048, 0), (64, None), (320, None)])
+def test_head_pairs(T, seg):
+    """Two heads of a group per work-group (shared B, C and scores, lowest
+    level slot above the segment in LDS): 2 and 4 heads per group, chunk
+    counts whose segments reach 1..3 levels above them, segment depths 0..3
+    and one chunk."""
+    check(small_cfg(T=T, H=4, G=1), variant="slow_decay", seg_log2=seg, heads_per_block=2)
+    check(small_cfg(T=T, H=4, G=2), seg_log2=seg, heads_per_block=2)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_head_pairs_chunks(chunk):
+    check(small_cfg(T=1024, H=2, G=1), chunk=chunk, variant="slow_decay", heads_per_block=2)
+
+
+@pytest.mark.parametrize("level", [0, 5, 6, 7, 9, 11])
+def test_head_pairs_onehot_levels(level):
+    check(small_cfg(T=2048, H=2, G=1), variant=f"lam_onehot_{level}", heads_per_block=2)
+
+
+def test_head_pairs_odd_levels():
+    """An odd level count: bf16 rows of the second head start mid-word."""
+    cfg = small_cfg(T=512, H=2, G=1)
+    d = inputs.make_inputs(cfg, 0)
+    t = to_device(d, cfg)
+    lam2 = torch.cat([t["lam"], torch.full_like(t["lam"][..., :3], 7.0)], dim=-1).contiguous()
+    t2 = dict(t, lam=lam2)
+    a = run_gpu(cfg, t2, heads_per_block=1).clone()
+    b2 = run_gpu(cfg, t2, heads_per_block=2)
+    torch.cuda.synchronize()
+    ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"])
+    assert max_rel_err(b2.float().cpu().numpy(), ref) <= 2e-2
+    assert max_rel_err(a.float().cpu().numpy(), ref) <= 2e-2
