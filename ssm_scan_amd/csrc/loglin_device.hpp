@@ -445,10 +445,14 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
     }
     for (int i = C + tid; i < KC; i += Tl::NT) wst[i] = 0.f;
   }
-  const int q = tile % pr.ns;
-  const int bh = tile / pr.ns;
-  const int h = bh % H, b = bh / H;
-  const int grp = h / (H / G);
+  // heads of one group next to each other: they read the same B rows
+  const int hpg = H / G;
+  const int hi = tile % hpg;
+  const int q = (tile / hpg) % pr.ns;
+  const int grp = (tile / (hpg * pr.ns)) % G;
+  const int b = tile / (hpg * pr.ns * G);
+  const int h = grp * hpg + hi;
+  const int bh = b * H + h;
   const T* X = static_cast<const T*>(pr.X);
   const T* Bm = static_cast<const T*>(pr.Bm);
   const int seg = 1 << pr.m;
@@ -510,49 +514,60 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
 // fp32 registers: after segment q the top entry is the sum over the largest
 // aligned block of segments ending at q, decayed to q's end.  That block is
 // the lower half a later segment reads at level trailing_ones(q) + 1.
+//
+// Before segment q the live entries are the set bits of q (entry i: a block
+// of 2^i segments), so the log-decay from the start of q's 2^(k-1)-aligned
+// block to q's start is the sum of the live entries' decays below bit k-1;
+// the first thread of each (batch, head) writes these gap decays.
 template <class T>
 __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
   using M = Mfma<T>;
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const bool valid = e < pn;
+  const bool gap_writer = blockIdx.x == 0 && threadIdx.x == 0;
   const float* src = pr.seg_state + (int64_t)bh * pr.ns * pn;
   const float* dec = pr.seg_decay + (int64_t)bh * pr.ns;
   T* dst = static_cast<T*>(pr.slots) + (int64_t)bh * pr.ns * pn;
-
-  // Gap decays: for segment q and segment level k (1..ks), the log-decay
-  // over the segments from the start of q's 2^(k-1)-aligned block to q-1.
-  if (blockIdx.x == 0 && threadIdx.x < pr.ks) {
-    const int k = threadIdx.x + 1;
-    const int mask = (1 << (k - 1)) - 1;
-    float run = 0.f;
-    float* gd = pr.gap_decay + (int64_t)bh * pr.ns * (pr.ks + 1);
-    for (int q = 0; q < pr.ns; ++q) {
-      if ((q & mask) == 0) run = 0.f;
-      gd[q * (pr.ks + 1) + k] = run;
-      run += dec[q];
-    }
-  }
+  float* gd = pr.gap_decay + (int64_t)bh * pr.ns * (pr.ks + 1);
 
   float stk[MAX_DEPTH], stka[MAX_DEPTH];
 #pragma unroll
   for (int i = 0; i < MAX_DEPTH; ++i) stk[i] = stka[i] = 0.f;
-  constexpr int U = 8;  // segments whose loads are in flight together
-  const int nq = pr.ns - 1;  // the last segment is never read
-  for (int q0 = 0; q0 < nq; q0 += U) {
-    float vb[U], db[U];
+  constexpr int U = 8;  // segments per batch; the next batch's loads fly meanwhile
+  const int ns = pr.ns;
+  float vb[U], db[U];
+  auto load = [&](int q0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = q0 + u;
-      vb[u] = (valid && q < nq) ? src[(int64_t)q * pn + e] : 0.f;
-      db[u] = q < nq ? dec[q] : 0.f;
+      vb[u] = (valid && q < ns - 1) ? src[(int64_t)q * pn + e] : 0.f;  // last one is never read
+      db[u] = q < ns ? dec[q] : 0.f;
     }
+  };
+  load(0);
+  for (int q0 = 0; q0 < ns; q0 += U) {
+    float v_cur[U], d_cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v_cur[u] = vb[u];
+      d_cur[u] = db[u];
+    }
+    if (q0 + U < ns) load(q0 + U);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = q0 + u;
-      if (q >= nq) break;
-      float v = vb[u];
-      float acur = db[u];
+      if (q >= ns) break;
+      if (gap_writer) {
+        float run = 0.f;
+        gd[q * (pr.ks + 1)] = 0.f;
+        for (int k = 1; k <= pr.ks; ++k) {
+          gd[q * (pr.ks + 1) + k] = run;
+          if ((q >> (k - 1)) & 1) run += stka[k - 1];
+        }
+      }
+      float v = v_cur[u];
+      float acur = d_cur[u];
       const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q
 #pragma unroll
       for (int i = 0; i < MAX_DEPTH; ++i) {
@@ -568,7 +583,7 @@ __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
           stka[i] = acur;
         }
       }
-      if (valid) dst[(int64_t)q * pn + e] = from_f<T>(v);
+      if (valid && q < ns - 1) dst[(int64_t)q * pn + e] = from_f<T>(v);
     }
   }
 }
