@@ -568,20 +568,18 @@ __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
       }
       float v = v_cur[u];
       float acur = d_cur[u];
-      const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q
-#pragma unroll
-      for (int i = 0; i < MAX_DEPTH; ++i) {
-        if (i < z) {
-          v = M::ex(acur) * stk[i] + v;
-          acur += stka[i];
-        }
-      }
+      const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q (uniform)
+      // Unrolled with uniform early exits: only z + 1 steps execute, and the
+      // stack stays in registers (its index is a constant in every step).
 #pragma unroll
       for (int i = 0; i < MAX_DEPTH; ++i) {
         if (i == z) {
           stk[i] = v;
           stka[i] = acur;
+          break;
         }
+        v = M::ex(acur) * stk[i] + v;
+        acur += stka[i];
       }
       if (valid && q < ns - 1) dst[(int64_t)q * pn + e] = from_f<T>(v);
     }
