@@ -415,49 +415,63 @@ __device__ inline void chunk_state_mma(const T* bs, const T* xs, const float* w,
 
 // ------------------------------------------------------------- pass 1
 
-// One work-group per (batch, head, segment).  Wave w owns state columns
-// [16w, 16w+16) and all N rows, as NB 16x16 fp32 tiles.  B and X rows go
-// straight to LDS, double-buffered: the next chunk's rows are requested as
-// soon as the current chunk's have landed.
-template <class T, int C, int P, int N>
-__global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params pr) {
+// One work-group per (batch, segment, HS heads of one group).  Wave w
+// serves head w / (P/16) and owns its state columns [16 (w mod P/16), +16)
+// and all N rows, as NB 16x16 fp32 tiles.  The heads of a group read the
+// same B rows, so with HS = 2 one copy of them in LDS serves both.  B and X
+// rows go straight to LDS, double-buffered: the next chunk's rows are
+// requested as soon as the current chunk's have landed.
+template <class T, int C, int P, int N, int HS>
+__global__ __launch_bounds__((HS * Tiles<T, C, P, N>::NT), (HS * Tiles<T, C, P, N>::NW / 2))
+void state_kernel(Params pr) {
   using Tl = Tiles<T, C, P, N>;
   using M = Mfma<T>;
   constexpr int KC = Tl::KC;  // token rows of a tile; rows C..KC-1 stay zero
+  constexpr int NT = HS * Tl::NT;
   // Two named buffers (not one 2-D array) so that the compiler can tell the
   // asynchronous fill of one from reads of the other and does not wait.
   __shared__ __attribute__((aligned(1024))) T bsh0[KC * N];
   __shared__ __attribute__((aligned(1024))) T bsh1[KC * N];
-  __shared__ __attribute__((aligned(1024))) T xsh0[KC * P];
-  __shared__ __attribute__((aligned(1024))) T xsh1[KC * P];
-  __shared__ __attribute__((aligned(16))) float cum[C], ecum[C], wst[KC];
+  __shared__ __attribute__((aligned(1024))) T xsh0[HS * KC * P];
+  __shared__ __attribute__((aligned(1024))) T xsh1[HS * KC * P];
+  __shared__ __attribute__((aligned(16))) float cum[HS * C], ecum[HS * C], wst[HS * KC];
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = wave / Tl::NW, wv = wave % Tl::NW;
   const int g = lane >> 4, r = lane & 15;
   const int H = pr.nheads, G = pr.ngroups;
   if (KC > C) {
-    for (int i = tid; i < (KC - C) * (N + P); i += Tl::NT) {
-      const int rr = C + i / (N + P), c = i % (N + P);
-      if (c < N) bsh0[rr * N + c] = bsh1[rr * N + c] = from_f<T>(0.f);
-      else xsh0[rr * P + c - N] = xsh1[rr * P + c - N] = from_f<T>(0.f);
+    for (int i = tid; i < (KC - C) * (N + HS * P); i += NT) {
+      const int rr = C + i / (N + HS * P), c = i % (N + HS * P);
+      if (c < N) {
+        bsh0[rr * N + c] = bsh1[rr * N + c] = from_f<T>(0.f);
+      } else {
+        const int x = c - N, o = (x / P) * KC * P + rr * P + x % P;
+        xsh0[o] = xsh1[o] = from_f<T>(0.f);
+      }
     }
-    for (int i = C + tid; i < KC; i += Tl::NT) wst[i] = 0.f;
+    for (int i = tid; i < HS * (KC - C); i += NT) wst[(i / (KC - C)) * KC + C + i % (KC - C)] = 0.f;
   }
   // heads of one group next to each other: they read the same B rows
-  const int hpg = H / G;
-  const int hi = tile % hpg;
-  const int q = (tile / hpg) % pr.ns;
-  const int grp = (tile / (hpg * pr.ns)) % G;
-  const int b = tile / (hpg * pr.ns * G);
-  const int h = grp * hpg + hi;
+  const int hpg = H / G, npair = hpg / HS;
+  const int pi = tile % npair;
+  const int q = (tile / npair) % pr.ns;
+  const int grp = (tile / (npair * pr.ns)) % G;
+  const int b = tile / (npair * pr.ns * G);
+  const int h0 = grp * hpg + pi * HS;
+  const int h = h0 + hh;
   const int bh = b * H + h;
   const T* X = static_cast<const T*>(pr.X);
   const T* Bm = static_cast<const T*>(pr.Bm);
   const int seg = 1 << pr.m;
   const int j0 = q * seg;
   const int nch = min(seg, pr.nc - j0);
+  float* cum_h = cum + hh * C;
+  float* ecum_h = ecum + hh * C;
+  float* wst_h = wst + hh * KC;
 
   f32x4 S[Tl::NB];
 #pragma unroll
@@ -466,31 +480,41 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
 
   auto issue = [&](int j, T* bs, T* xs) __attribute__((always_inline)) {
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, Tl::NW>(Bm + (row0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
-    rows_to_lds<T, C, P, Tl::NW>(X + (row0 * H + h) * P, (int64_t)H * P, xs, wave, lane);
+    rows_to_lds<T, C, N, HS * Tl::NW>(Bm + (row0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
+#pragma unroll
+    for (int k = 0; k < HS; ++k)
+      rows_to_lds<T, C, P, HS * Tl::NW>(X + (row0 * H + h0 + k) * P, (int64_t)H * P, xs + k * KC * P,
+                                        wave, lane);
   };
-  float la = tid < C ? pr.log_a[((int64_t)b * pr.seqlen + (int64_t)j0 * C + tid) * H + h] : 0.f;
+  // log-decays of each head, loaded and scanned by its first wave
+  auto load_la = [&](int j) __attribute__((always_inline)) {
+    const int64_t rn = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    return (wv == 0 && lane < C) ? pr.log_a[(rn + lane) * H + h] : 0.f;
+  };
+  float la = load_la(j0);
   issue(j0, bsh0, xsh0);
   // one chunk per call; CUR selects the buffer pair at compile time
   auto step = [&](auto cur_c, int jl) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_c)::value;
     T* bs = CUR ? bsh1 : bsh0;
-    T* xs = CUR ? xsh1 : xsh0;
-    chunk_decays<T, C>(la, cum, ecum, wst, tid);
+    T* xs = (CUR ? xsh1 : xsh0) + hh * KC * P;
+    if (wv == 0) chunk_decays<T, C>(la, cum_h, ecum_h, wst_h, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     lds_barrier();
     if (jl + 1 < nch) {  // the other buffer was released by the previous barrier
       issue(j0 + jl + 1, CUR ? bsh0 : bsh1, CUR ? xsh0 : xsh1);
-      const int64_t rn = (int64_t)b * pr.seqlen + (int64_t)(j0 + jl + 1) * C;
-      la = tid < C ? pr.log_a[(rn + tid) * H + h] : 0.f;
+      la = load_la(j0 + jl + 1);
     }
-    const float atot = cum[C - 1];
+    const float atot = cum_h[C - 1];
     if (jl > 0) {
       const float dec = M::ex(atot);
 #pragma unroll
       for (int nb = 0; nb < Tl::NB; ++nb) S[nb] *= dec;
     }
-    chunk_state_mma<T, C, P, N>(bs, xs, wst, S, wave, g, r);
+    // lane addresses rebuilt per chunk rather than held across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    chunk_state_mma<T, C, P, N>(bs, xs, wst_h, S, wv, ln >> 4, ln & 15);
     seg_sum += atot;
     lds_barrier();
   };
@@ -499,12 +523,12 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void state_kernel(Params p
     if (jl + 1 < nch) step(std::integral_constant<int, 1>{}, jl + 1);
   }
 
-  float* dst = pr.seg_state + ((int64_t)bh * pr.ns + q) * (P * N) + (16 * wave + r) * N;
+  float* dst = pr.seg_state + ((int64_t)bh * pr.ns + q) * (P * N) + (16 * wv + r) * N;
 #pragma unroll
   for (int nb = 0; nb < Tl::NB; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[M::state_pos(16 * nb + 4 * g + i)] = S[nb][i];
-  if (tid == 0) pr.seg_decay[(int64_t)bh * pr.ns + q] = seg_sum;
+  if (wv == 0 && lane == 0) pr.seg_decay[(int64_t)bh * pr.ns + q] = seg_sum;
 }
 
 // ------------------------------------------------------------- pass 2

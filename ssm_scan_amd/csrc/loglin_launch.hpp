@@ -28,8 +28,16 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   Params pr = base;
   record(ev, 0, st);
   if (pr.ns > 1) {
-    pr.total = pr.batch * pr.nheads * pr.ns;
-    hipLaunchKernelGGL((state_kernel<T, C, P, N>), dim3(pad8(pr.total)), dim3(Tl::NT), 0, st, pr);
+    // bf16 heads of one group share their B rows in one work-group
+    constexpr bool SPAIRS = sizeof(T) == 2;
+    if (SPAIRS && (pr.nheads / pr.ngroups) % 2 == 0) {
+      pr.total = pr.batch * pr.ns * (pr.nheads / 2);
+      hipLaunchKernelGGL((state_kernel<T, C, P, N, SPAIRS ? 2 : 1>), dim3(pad8(pr.total)),
+                         dim3(2 * Tl::NT), 0, st, pr);
+    } else {
+      pr.total = pr.batch * pr.nheads * pr.ns;
+      hipLaunchKernelGGL((state_kernel<T, C, P, N, 1>), dim3(pad8(pr.total)), dim3(Tl::NT), 0, st, pr);
+    }
     record(ev, 1, st);
     dim3 g2((P * N + 255) / 256, pr.batch * pr.nheads);
     hipLaunchKernelGGL((scan_kernel<T>), g2, dim3(256), 0, st, pr, P * N);
