@@ -278,6 +278,26 @@ struct Rows {
   }
 };
 
+// Level slots (pass 2 output, pass 3 input) are stored in the order the
+// output pass loads them as MFMA A operands: for each 16-row block w of the
+// P rows and contraction step kk, the 64 lanes' KPL-element fragments lie
+// back to back (lane 16 g + r at position 4 r + g), so every load
+// instruction of a wave reads whole cache lines.  Element (p, n) of a state
+// in state order (n = state_pos of the state row) goes to slot_index(p, n).
+template <class T, int N>
+__host__ __device__ constexpr int slot_index(int p, int n) {
+  using M = Mfma<T>;
+  constexpr int NKN = N / M::KB;
+  const int w = p >> 4, r = p & 15, kk = n / M::KB, g = (n % M::KB) / M::KPL, j = n % M::KPL;
+  return ((w * NKN + kk) * 64 + r * 4 + g) * M::KPL + j;
+}
+// First element of lane (g, r)'s fragment at step kk of row block w.
+template <class T, int N>
+__host__ __device__ constexpr int slot_frag(int w, int kk, int g, int r) {
+  using M = Mfma<T>;
+  return ((w * (N / M::KB) + kk) * 64 + r * 4 + g) * M::KPL;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* global_ptr_t;
 
@@ -330,6 +350,21 @@ __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, in
       const T* src = g + (int64_t)row * grs + lb * L::VEC;
       dma_16x64(src, lds_addr(lds) + inst * 1024u);
     }
+  }
+}
+
+// Copy BYTES contiguous bytes (a multiple of 16) into LDS unchanged.
+template <int BYTES, int NW>
+__device__ inline void flat_to_lds(const void* g, void* lds, int wave, int lane) {
+  constexpr int PIECES = BYTES / 16;
+  constexpr int INSTS = (PIECES + 63) / 64;
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int k = 0; k < (INSTS + NW - 1) / NW; ++k) {
+    const int inst = ws + k * NW;
+    const int piece = inst * 64 + lane;
+    if (inst < INSTS && piece < PIECES)
+      dma_16x64(static_cast<const char*>(g) + piece * 16, lds_addr(lds) + inst * 1024u);
   }
 }
 
@@ -543,7 +578,7 @@ void state_kernel(Params pr) {
 // of 2^i segments), so the log-decay from the start of q's 2^(k-1)-aligned
 // block to q's start is the sum of the live entries' decays below bit k-1;
 // the first thread of each (batch, head) writes these gap decays.
-template <class T>
+template <class T, int N>
 __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
   using M = Mfma<T>;
   const int bh = blockIdx.y;
@@ -605,7 +640,7 @@ __global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
         v = M::ex(acur) * stk[i] + v;
         acur += stka[i];
       }
-      if (valid && q < ns - 1) dst[(int64_t)q * pn + e] = from_f<T>(v);
+      if (valid && q < ns - 1) dst[(int64_t)q * pn + slot_index<T, N>(e / N, e % N)] = from_f<T>(v);
     }
   }
 }
@@ -701,7 +736,10 @@ void output_kernel(Params pr) {
   __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? HP * KC * P : 1];
   __shared__ __attribute__((aligned(1024))) T csh[C * N];          // C rows
   __shared__ __attribute__((aligned(1024))) T zres[NR ? HP * NR * P * N : 1];  // resident slots
-  __shared__ __attribute__((aligned(16))) T wt[HP * C * Tl::XS];   // W[t][s]
+  // W[t][s] of each head; after the intra product, the head's output tile
+  // [t][P] (Rows layout) on its way to memory
+  constexpr int WTS = C * Tl::XS > C * P ? C * Tl::XS : C * P;
+  __shared__ __attribute__((aligned(16))) T wt[HP * WTS];
   __shared__ __attribute__((aligned(16))) float cum[HP * C], ecum[HP * C], wst[HP * KC];
   __shared__ float gap_s[HP * GS];     // gap log-decays of this segment
   extern __shared__ unsigned lam_w[];  // [HP][C][lam_words]: level weights
@@ -711,6 +749,7 @@ void output_kernel(Params pr) {
   const int tid0 = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // uniform: keep it scalar
   const int hh = wave / Cfg::NWH;  // head of this wave within the work-group
+  static_assert(WTS >= C * Tl::XS, "W buffer");
   const int wv = wave % Cfg::NWH;  // its 16-column block
   if (KC > C) {  // contraction padding of the token tiles and of W stays zero
     for (int i = tid0; i < (KC - C) * (N + HP * P); i += Cfg::NT) {
@@ -725,8 +764,8 @@ void output_kernel(Params pr) {
       }
     }
     for (int i = tid0; i < HP * C * (KC - C); i += Cfg::NT) {
-      const int row = i / (KC - C);  // head-major rows of W
-      wt[row * Tl::XS + C + i % (KC - C)] = from_f<T>(0.f);
+      const int row = i / (KC - C), k = row / C;  // head-major rows of W
+      wt[k * WTS + (row % C) * Tl::XS + C + i % (KC - C)] = from_f<T>(0.f);
     }
     for (int i = tid0; i < HP * (KC - C); i += Cfg::NT) wst[(i / (KC - C)) * KC + C + i % (KC - C)] = 0.f;
   }
@@ -800,9 +839,9 @@ void output_kernel(Params pr) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const int lane = tid & 63, r = lane & 15, g = lane >> 4;
     if (stream_mask) {
-      const T* zr = slot_of(h, __builtin_ctz(stream_mask) + 1) + (16 * wv + r) * N + g * Tl::KPL;
+      const T* zr = slot_of(h, __builtin_ctz(stream_mask) + 1) + slot_frag<T, N>(wv, 0, g, r);
 #pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk) zfirst[kk] = load_frag<T>(zr + kk * Tl::KB);
+      for (int kk = 0; kk < Tl::NKN; ++kk) zfirst[kk] = load_frag<T>(zr + kk * 64 * Tl::KPL);
     }
     la = (wv == 0 && lane < C) ? pr.log_a[(r0 + lane) * H + h] : 0.f;
   };
@@ -846,7 +885,7 @@ void output_kernel(Params pr) {
         mk &= mk - 1;
 #pragma unroll
         for (int k = 0; k < HP; ++k)
-          rows_to_lds<T, P, N, NTW>(slot_of(h0 + k, ks), N, zres + (k * NR + i) * P * N, wave, tid0 & 63);
+          flat_to_lds<P * N * (int)sizeof(T), NTW>(slot_of(h0 + k, ks), zres + (k * NR + i) * P * N, wave, tid0 & 63);
       }
     }
   }
@@ -906,14 +945,14 @@ void output_kernel(Params pr) {
                               : 0.f;
           }
         }
-        store4(wt + k * C * Tl::XS + Tl::at(t, 16 * sb + 4 * g), wv4);
+        store4(wt + k * WTS + Tl::at(t, 16 * sb + 4 * g), wv4);
       }
     }
     lds_barrier();
 
     // ---- output tiles: intra block, then every active inter-chunk level
     {
-      const T* wth = wt + hh * C * Tl::XS;
+      T* wth = wt + hh * WTS;
       const int par_r = lpar & (((int)row0 + r) * H + h);  // parity of token 16 tb + r
       f32x4 Y[Tl::TB];
       frag cf[Tl::TB][Tl::NKN];  // C^T fragments in state order
@@ -958,7 +997,7 @@ void output_kernel(Params pr) {
           frag zf[Tl::NKN];
           const T* zt = zres + (hh * NR + i) * P * N;
 #pragma unroll
-          for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = frag_along<T, RB>(zt, 16 * wv + r, kk * Tl::KB, g);
+          for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = load_frag<T>(zt + slot_frag<T, N>(wv, kk, g, r));
           add_level(zf, c_log + m + ks, gap_h[ks] + accseg);
         }
       }
@@ -970,9 +1009,9 @@ void output_kernel(Params pr) {
         mask &= mask - 1;
         frag znext[Tl::NKN];
         if (mask) {
-          const T* zr = slot_of(h, __builtin_ctz(mask) + 1) + (16 * wv + r) * N + g * Tl::KPL;
+          const T* zr = slot_of(h, __builtin_ctz(mask) + 1) + slot_frag<T, N>(wv, 0, g, r);
 #pragma unroll
-          for (int kk = 0; kk < Tl::NKN; ++kk) znext[kk] = load_frag<T>(zr + kk * Tl::KB);
+          for (int kk = 0; kk < Tl::NKN; ++kk) znext[kk] = load_frag<T>(zr + kk * 64 * Tl::KPL);
         }
         add_level(zcur, c_log + m + ks, gap_h[ks] + accseg);
 #pragma unroll
@@ -982,15 +1021,27 @@ void output_kernel(Params pr) {
       for (int e = 0; e < MM; ++e) {  // levels inside the segment
         if (e < m && ((jl >> e) & 1)) add_level(zl[e], c_log + e + 1, dloc[e + 1]);
       }
+      // Stage the tile in LDS (W is consumed; the barrier below also tells
+      // that every wave has read its C^T fragments) so that each token's
+      // output row leaves as whole cache lines.
 #pragma unroll
-      for (int tb = 0; tb < Tl::TB; ++tb) {
-        const int t = 16 * tb + r;
-        store4(out + ((row0 + t) * H + h) * P + 16 * wv + 4 * g, Y[tb]);
+      for (int tb = 0; tb < Tl::TB; ++tb) store4(wth + RX::at(16 * tb + r, 16 * wv + 4 * g), Y[tb]);
+    }
+    lds_barrier();
+    {
+      constexpr int VEC = 16 / (int)sizeof(T), NBP = P / VEC, PIECES = C * NBP;
+      const T* ys = wt + hh * WTS;
+#pragma unroll
+      for (int pc0 = 0; pc0 < PIECES; pc0 += Cfg::NWH * 64) {
+        const int pc = pc0 + wv * 64 + lane;
+        if (PIECES % (Cfg::NWH * 64) == 0 || pc < PIECES) {
+          const int t = pc / NBP, bb = pc % NBP;
+          store16(out + ((row0 + t) * H + h) * P + bb * VEC, load16(ys + RX::at(t, bb * VEC)));
+        }
       }
     }
 
     if (need_state) {
-      lds_barrier();  // every wave has read its C^T fragments
       issue_c(j + 1, lane);
       issue_lam(j + 1, lane);
       issue_regs(j + 1, tid);  // land during the state MFMAs

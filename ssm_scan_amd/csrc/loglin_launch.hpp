@@ -40,7 +40,7 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
     }
     record(ev, 1, st);
     dim3 g2((P * N + 255) / 256, pr.batch * pr.nheads);
-    hipLaunchKernelGGL((scan_kernel<T>), g2, dim3(256), 0, st, pr, P * N);
+    hipLaunchKernelGGL((scan_kernel<T, N>), g2, dim3(256), 0, st, pr, P * N);
   } else {
     record(ev, 1, st);
   }
