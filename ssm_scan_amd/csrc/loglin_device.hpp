@@ -681,8 +681,8 @@ __device__ inline void score_tile(int u, int& tb, int& sb) {
 // Inter-chunk level k of chunk j reads the lower half of j's 2^k-chunk
 // block.  For k > m that block is a run of whole segments: its sum is slot
 // ((q >> ks) << ks) + 2^(ks-1) - 1 of pass 2 (ks = k - m), shared by every
-// chunk of the segment.  The first NR of those slots stay in LDS for the
-// whole segment; the others are fetched per chunk.  For k <= m the block
+// chunk of the segment.  The first RZ of those slots stay in registers for
+// the whole segment; the others are fetched per chunk.  For k <= m the block
 // lies inside the segment: the wave keeps a Fenwick stack of those block
 // sums, entry e holding the block of 2^e chunks that ends just before the
 // current chunk, as MFMA A-operand fragments.  The state MFMA leaves a lane
@@ -700,14 +700,8 @@ struct OutCfg {
   static constexpr int NT = NTW * 64;
   static constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;
   static constexpr int KC = Tl::KC;
-  static constexpr int LAM_MAX = HP * C * (sizeof(T) == 2 ? 17 : 33) * 4;  // <= 32 levels
-  static constexpr int STATIC_LDS =
-      (int)sizeof(T) * (NBUF * KC * N + C * N + HP * NBUF * KC * P + HP * C * Tl::XS) +
-      4 * (HP * (2 * C + KC) + HP * (MAX_DEPTH + 1));
-  static constexpr int SLOT_BYTES = HP * P * N * (int)sizeof(T);
-  // resident slots only where a work-group holds the whole CU anyway
-  static constexpr int NR_FIT = (160 * 1024 - STATIC_LDS - LAM_MAX - 2048) / SLOT_BYTES;
-  static constexpr int NR = HP == 1 ? 0 : (NR_FIT > MAX_DEPTH ? MAX_DEPTH : NR_FIT);
+  // slots above the segment held in registers for the whole segment
+  static constexpr int RZ = sizeof(T) == 2 ? 3 : 1;
   static constexpr int MIN_BLOCKS = HP == 1 ? 2 : 1;
 };
 
@@ -722,7 +716,7 @@ void output_kernel(Params pr) {
   using RX = Rows<T, P>;
   constexpr int MM = MAX_SEG_LOG2;
   constexpr int NBUF = Cfg::NBUF;
-  constexpr int NR = Cfg::NR;
+  constexpr int RZ = Cfg::RZ;
   constexpr int NTW = Cfg::NTW;
   constexpr int KC = Tl::KC;  // token rows of the B / X tiles; rows C..KC-1 stay zero
   constexpr int GS = MAX_DEPTH + 1;
@@ -735,7 +729,6 @@ void output_kernel(Params pr) {
   __shared__ __attribute__((aligned(1024))) T xsh0[HP * KC * P];
   __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? HP * KC * P : 1];
   __shared__ __attribute__((aligned(1024))) T csh[C * N];          // C rows
-  __shared__ __attribute__((aligned(1024))) T zres[NR ? HP * NR * P * N : 1];  // resident slots
   // W[t][s] of each head; after the intra product, the head's output tile
   // [t][P] (Rows layout) on its way to memory
   constexpr int WTS = C * Tl::XS > C * P ? C * Tl::XS : C * P;
@@ -820,10 +813,24 @@ void output_kernel(Params pr) {
   // levels past the resident ones are fetched per chunk
   unsigned stream_mask = ext_mask;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) stream_mask &= stream_mask - 1;
+  for (int i = 0; i < RZ; ++i) stream_mask &= stream_mask - 1;
+  // the segment's lowest RZ level slots, in registers for all its chunks
+  frag zres[RZ][Tl::NKN];
+  {
+    const int lane = tid0 & 63, r = lane & 15, g = lane >> 4;
+    unsigned mk = ext_mask;
+#pragma unroll
+    for (int i = 0; i < RZ; ++i) {
+      if (mk) {
+        const T* zr = slot_of(h, __builtin_ctz(mk) + 1) + slot_frag<T, N>(wv, 0, g, r);
+        mk &= mk - 1;
+#pragma unroll
+        for (int kk = 0; kk < Tl::NKN; ++kk) zres[i][kk] = load_frag<T>(zr + kk * 64 * Tl::KPL);
+      }
+    }
+  }
 
   float la = 0.f;
-  frag zfirst[Tl::NKN];  // first streamed level slot
   auto issue_bx = [&](int j, T* bs, T* xs, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     rows_to_lds<T, C, N, NTW>(Bm + (r0 * G + grp) * N, (int64_t)G * N, bs, wave, lane);
@@ -838,11 +845,6 @@ void output_kernel(Params pr) {
   auto issue_regs = [&](int j, int tid) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const int lane = tid & 63, r = lane & 15, g = lane >> 4;
-    if (stream_mask) {
-      const T* zr = slot_of(h, __builtin_ctz(stream_mask) + 1) + slot_frag<T, N>(wv, 0, g, r);
-#pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk) zfirst[kk] = load_frag<T>(zr + kk * 64 * Tl::KPL);
-    }
     la = (wv == 0 && lane < C) ? pr.log_a[(r0 + lane) * H + h] : 0.f;
   };
   // level weights of chunk j into lam_w (the last word of the tensor bounds
@@ -876,19 +878,6 @@ void output_kernel(Params pr) {
     }
   };
   const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
-  if constexpr (NR > 0) {  // resident slots, published by the first barrier
-    unsigned mk = ext_mask;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      if (mk) {
-        const int ks = __builtin_ctz(mk) + 1;
-        mk &= mk - 1;
-#pragma unroll
-        for (int k = 0; k < HP; ++k)
-          flat_to_lds<P * N * (int)sizeof(T), NTW>(slot_of(h0 + k, ks), zres + (k * NR + i) * P * N, wave, tid0 & 63);
-      }
-    }
-  }
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
   issue_c(j0, tid0 & 63);
   issue_lam(j0, tid0 & 63);
@@ -955,7 +944,6 @@ void output_kernel(Params pr) {
       T* wth = wt + hh * WTS;
       const int par_r = lpar & (((int)row0 + r) * H + h);  // parity of token 16 tb + r
       f32x4 Y[Tl::TB];
-      frag cf[Tl::TB][Tl::NKN];  // C^T fragments in state order
 #pragma unroll
       for (int tb = 0; tb < Tl::TB; ++tb) {
         Y[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -967,59 +955,77 @@ void output_kernel(Params pr) {
             Y[tb] = M::mma(af, bf, Y[tb]);
           }
         }
+      }
+      // level weight of token 16 tb + r times e^(Lambda_t + D)
+      auto level_scale = [&](int tb, int level, float eD) __attribute__((always_inline)) {
+        const int t = 16 * tb + r;
+        // 16 tb keeps the parity of the row start: H * 16 tb is even
+        return lam_at(hh, t, level, par_r) * ecum_h[t] * eD;
+      };
+
+      // Levels whose slots are in registers (the segment's resident ones and
+      // the local stack), one token block at a time: its C^T fragments are
+      // read once and serve all of them.
+      float eres[RZ];
+      int lres[RZ];
+      {
+        unsigned mk = ext_mask;
 #pragma unroll
-        for (int kk = 0; kk < Tl::NKN; ++kk) cf[tb][kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
+        for (int i = 0; i < RZ; ++i) {
+          const int ks = mk ? __builtin_ctz(mk) + 1 : 1;
+          mk &= mk - 1;
+          lres[i] = c_log + m + ks;
+          eres[i] = M::ex(gap_h[ks] + accseg);
+        }
+      }
+      const int nres = min(__builtin_popcount(ext_mask), RZ);
+      float eloc[MM];
+#pragma unroll
+      for (int e = 0; e < MM; ++e) eloc[e] = M::ex(dloc[e + 1]);
+#pragma unroll
+      for (int tb = 0; tb < Tl::TB; ++tb) {
+        frag cf[Tl::NKN];  // C^T fragments of the block, in state order
+#pragma unroll
+        for (int kk = 0; kk < Tl::NKN; ++kk) cf[kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
+#pragma unroll
+        for (int i = 0; i < RZ; ++i) {
+          if (i < nres) {
+            f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zres[i][kk], cf[kk], tmp);
+            Y[tb] += level_scale(tb, lres[i], eres[i]) * tmp;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < MM; ++e) {  // levels inside the segment
+          if (e < m && ((jl >> e) & 1)) {
+            f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zl[e][kk], cf[kk], tmp);
+            Y[tb] += level_scale(tb, c_log + e + 1, eloc[e]) * tmp;
+          }
+        }
       }
 
-      auto add_level = [&](const frag* zf, int level, float D) __attribute__((always_inline)) {
-        const float eD = M::ex(D);
+      // The remaining levels above the segment (rare: a segment index with
+      // more than RZ set bits), from memory; C^T comes from LDS again.
+      unsigned mask = stream_mask;
+      while (mask) {
+        const int ks = __builtin_ctz(mask) + 1;
+        mask &= mask - 1;
+        frag zcur[Tl::NKN];
+        const T* zr = slot_of(h, ks) + slot_frag<T, N>(wv, 0, g, r);
+#pragma unroll
+        for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = load_frag<T>(zr + kk * 64 * Tl::KPL);
+        const float eD = M::ex(gap_h[ks] + accseg);
 #pragma unroll
         for (int tb = 0; tb < Tl::TB; ++tb) {
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zf[kk], cf[tb][kk], tmp);
-          const int t = 16 * tb + r;
-          // 16 tb keeps the parity of the row start: H * 16 tb is even
-          const float sc = lam_at(hh, t, level, par_r) * ecum_h[t] * eD;
-          Y[tb] += sc * tmp;
+          for (int kk = 0; kk < Tl::NKN; ++kk)
+            tmp = M::mma(zcur[kk], rows_state_frag<T, N>(csh, 16 * tb + r, kk, g), tmp);
+          Y[tb] += level_scale(tb, c_log + m + ks, eD) * tmp;
         }
-      };
-
-      // levels above the segment: resident slots from LDS, then the others
-      // from memory (the first one is in registers already, the rest are
-      // loaded one level ahead)
-      unsigned mask = ext_mask;
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (mask) {
-          const int ks = __builtin_ctz(mask) + 1;
-          mask &= mask - 1;
-          frag zf[Tl::NKN];
-          const T* zt = zres + (hh * NR + i) * P * N;
-#pragma unroll
-          for (int kk = 0; kk < Tl::NKN; ++kk) zf[kk] = load_frag<T>(zt + slot_frag<T, N>(wv, kk, g, r));
-          add_level(zf, c_log + m + ks, gap_h[ks] + accseg);
-        }
-      }
-      frag zcur[Tl::NKN];
-#pragma unroll
-      for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = zfirst[kk];
-      while (mask) {
-        const int ks = __builtin_ctz(mask) + 1;
-        mask &= mask - 1;
-        frag znext[Tl::NKN];
-        if (mask) {
-          const T* zr = slot_of(h, __builtin_ctz(mask) + 1) + slot_frag<T, N>(wv, 0, g, r);
-#pragma unroll
-          for (int kk = 0; kk < Tl::NKN; ++kk) znext[kk] = load_frag<T>(zr + kk * 64 * Tl::KPL);
-        }
-        add_level(zcur, c_log + m + ks, gap_h[ks] + accseg);
-#pragma unroll
-        for (int kk = 0; kk < Tl::NKN; ++kk) zcur[kk] = znext[kk];
-      }
-#pragma unroll
-      for (int e = 0; e < MM; ++e) {  // levels inside the segment
-        if (e < m && ((jl >> e) & 1)) add_level(zl[e], c_log + e + 1, dloc[e + 1]);
       }
       // Stage the tile in LDS (W is consumed; the barrier below also tells
       // that every wave has read its C^T fragments) so that each token's
