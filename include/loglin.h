@@ -104,11 +104,10 @@ typedef struct {
    * chip.  -1 lets the library choose (min(3, ceil(log2(seqlen/chunk)))).
    * Valid: 0 <= seg_log2 <= min(3, ceil(log2(seqlen/chunk))). */
   int32_t seg_log2;
-  /* Heads served by one work-group of the output pass.  0 or 1: one head
-   * (the default).  2: two heads of the same group share the group's B and
-   * C rows and the scores C B^T, and the lowest level slot above a segment
-   * stays in LDS; needs bf16, headdim 64 and an even number of heads per
-   * group (nheads / ngroups), else LOGLIN_ERR_OPTS. */
+  /* Heads served by one work-group of the output pass.  2: two heads of the
+   * same group share the group's B and C rows and the scores C B^T; needs
+   * bf16, headdim 64 and an even number of heads per group (nheads /
+   * ngroups), else LOGLIN_ERR_OPTS.  0 or 1: one head (the default). */
   int32_t heads_per_block;
   /* NULL, or LOGLIN_NUM_STAGES + 1 events (hipEvent_t) recorded on
    * `stream` at the stage boundaries, for per-pass timing. */

@@ -57,14 +57,15 @@ int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) 
   // block a chunk reads lies before it.
   const int kc = ceil_log2(nc);
   int m = kc < loglin::MAX_SEG_LOG2 ? kc : loglin::MAX_SEG_LOG2;
+  // heads of one group per output work-group: one unless asked for two
+  // (two measured slower on the 32K workload)
+  const bool pairs_ok = d->io_dtype == LOGLIN_BF16 && d->headdim == 64 &&
+                        (d->nheads / d->ngroups) % 2 == 0;
   int hp = 1;
   if (o) {
     if (o->heads_per_block < 0 || o->heads_per_block > 2) return LOGLIN_ERR_OPTS;
-    if (o->heads_per_block == 2) {
-      if (d->io_dtype != LOGLIN_BF16 || d->headdim != 64 || (d->nheads / d->ngroups) % 2)
-        return LOGLIN_ERR_OPTS;
-      hp = 2;
-    }
+    if (o->heads_per_block == 2 && !pairs_ok) return LOGLIN_ERR_OPTS;
+    if (o->heads_per_block > 0) hp = o->heads_per_block;
     if (o->seg_log2 < -1 || o->seg_log2 > loglin::MAX_SEG_LOG2) return LOGLIN_ERR_OPTS;
     if (o->seg_log2 > kc) return LOGLIN_ERR_OPTS;
     if (o->seg_log2 >= 0) m = o->seg_log2;

@@ -195,3 +195,9 @@ def test_head_pairs_odd_levels():
     ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"])
     assert max_rel_err(b2.float().cpu().numpy(), ref) <= 2e-2
     assert max_rel_err(a.float().cpu().numpy(), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("T,seg", [(1344, None), (2048, 0), (64 * 64, None)])
+def test_one_head_per_block(T, seg):
+    """One head per output work-group forced where pairs are the default."""
+    check(small_cfg(T=T, H=4, G=2), variant="slow_decay", seg_log2=seg, heads_per_block=1)
