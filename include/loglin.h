@@ -152,6 +152,39 @@ const char* loglin_strerror(int code);
 int loglin_plan_seg_log2(const loglin_dims* dims, int chunk,
                          const loglin_opts* opts);
 
+/* ---- One-token decode (Fenwick recurrence) -------------------------------
+ *
+ * Operation (log-linear attention write-up, section "log-linear attention"
+ * and "special structure: tree partition"): decoding keeps one N x P state
+ * per Fenwick bucket of the prefix, O(log T) of them.  Step t (t = 0, 1, ...)
+ * merges the buckets of levels 0..z into level z+1 (z = trailing zeros of
+ * t, t > 0), decays every older bucket by a_t, starts level 0 with
+ * B_t X_t^T and returns, for every batch entry and head,
+ *
+ *     out_t = sum_l lambda[t, l] S_l^T C_t,
+ *
+ * which equals row t of loglin_fwd's output for the same inputs.
+ *
+ * dims: as for loglin_fwd, with seqlen the number of positions the state
+ * can hold (steps t = 0 .. seqlen - 1) and nlevels >= ceil(log2 seqlen) + 1.
+ * Layouts (row-major, one token):
+ *   X      [batch, nheads, headdim]    io dtype
+ *   B, C   [batch, ngroups, dstate]    io dtype
+ *   log_a  [batch, nheads]             float32
+ *   lambda [batch, nheads, nlevels]    io dtype
+ *   out    [batch, nheads, headdim]    io dtype
+ * state: loglin_decode_state_bytes bytes of device memory owned by the
+ * caller, 256-byte aligned, reused across the steps of one sequence
+ * (batch).  Step 0 initialises it (no clearing needed); steps must run in
+ * order t = 0, 1, 2, ... on one stream.  Other pointers: device pointers,
+ * `out` 16-byte aligned, the inputs aligned to their element size.  Errors
+ * as for loglin_fwd; t outside [0, seqlen) is LOGLIN_ERR_DIM. */
+size_t loglin_decode_state_bytes(const loglin_dims* dims);
+
+int loglin_decode_step(void* state, int64_t t, const void* X, const void* B,
+                       const void* C, const float* log_a, const void* lambda,
+                       void* out, const loglin_dims* dims, void* stream);
+
 /* Event helpers for callers that time stages without linking HIP
  * themselves.  *event receives a hipEvent_t with timing enabled. */
 int loglin_event_create(void** event);

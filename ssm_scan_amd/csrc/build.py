@@ -1,7 +1,7 @@
 """Build libloglin.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-Compiles the host C-ABI unit and six kernel instantiation units (io type x
-chunk) in parallel, then links ssm_scan_amd/_lib/libloglin.so.
+Compiles the host C-ABI unit, the decode unit and six forward instantiation
+units (io type x chunk) in parallel, then links ssm_scan_amd/_lib/libloglin.so.
 """
 from __future__ import annotations
 
@@ -30,7 +30,8 @@ FLAGS = [
 
 
 def _units():
-    units = [("loglin_host", os.path.join(HERE, "loglin_host.cpp"), [])]
+    units = [("loglin_host", os.path.join(HERE, "loglin_host.cpp"), []),
+             ("loglin_decode", os.path.join(HERE, "loglin_decode.hip"), [])]
     for io in ("bf16", "f32"):
         for chunk in (16, 32, 64):
             units.append((f"loglin_inst_{io}_{chunk}",

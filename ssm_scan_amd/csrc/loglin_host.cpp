@@ -7,6 +7,7 @@
 
 #include <cstdint>
 
+#include "loglin_decode.hpp"
 #include "loglin_launch.hpp"
 
 namespace {
@@ -133,9 +134,77 @@ loglin::LaunchFn pick(int dtype, int chunk, int P, int N) {
   return nullptr;
 }
 
+// Decode state: level states fp32 [B, H, LL, N, P], then the two banks of
+// per-level decay factors [B, H, 2, LL]; each region 256-byte aligned.
+struct DecodePlan {
+  int ll;
+  size_t off_g, bytes;
+};
+
+int check_decode(const loglin_dims* d, DecodePlan* pl) {
+  if (!d) return LOGLIN_ERR_NULL;
+  if (d->reserved != 0) return LOGLIN_ERR_DIM;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->ngroups <= 0 ||
+      d->headdim <= 0 || d->dstate <= 0 || d->nlevels <= 0)
+    return LOGLIN_ERR_DIM;
+  if (d->io_dtype != LOGLIN_F32 && d->io_dtype != LOGLIN_BF16) return LOGLIN_ERR_DTYPE;
+  if (d->nheads % d->ngroups) return LOGLIN_ERR_GROUPS;
+  if (d->seqlen > (int64_t(1) << 40) || d->nheads > 4096 || d->nlevels > 64 ||
+      d->batch * d->nheads > (int64_t(1) << 24))
+    return LOGLIN_ERR_DIM;
+  const int ll = ceil_log2(d->seqlen) + 1;
+  if (d->nlevels < ll) return LOGLIN_ERR_LEVELS;
+  if (!supported_shape(d->io_dtype, d->headdim, d->dstate)) return LOGLIN_ERR_SHAPE;
+  if (ll > 256) return LOGLIN_ERR_DIM;  // one thread per level writes the decay factors
+  pl->ll = ll;
+  const size_t bh = (size_t)(d->batch * d->nheads);
+  pl->off_g = round_up(bh * ll * (size_t)(d->headdim * d->dstate) * sizeof(float));
+  pl->bytes = round_up(pl->off_g + bh * 2 * ll * sizeof(float));
+  return LOGLIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t loglin_decode_state_bytes(const loglin_dims* dims) {
+  DecodePlan pl;
+  return check_decode(dims, &pl) ? 0 : pl.bytes;
+}
+
+int loglin_decode_step(void* state, int64_t t, const void* X, const void* B, const void* C,
+                       const float* log_a, const void* lambda, void* out,
+                       const loglin_dims* dims, void* stream) {
+  DecodePlan pl;
+  int rc = check_decode(dims, &pl);
+  if (rc) return rc;
+  if (t < 0 || t >= dims->seqlen) return LOGLIN_ERR_DIM;
+  if (!state || !X || !B || !C || !log_a || !lambda || !out) return LOGLIN_ERR_NULL;
+  // one token's rows are small: inputs need only element alignment
+  const uintptr_t es = dims->io_dtype == LOGLIN_BF16 ? 2 : 4;
+  auto off = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; };
+  if (off(X, es) || off(B, es) || off(C, es) || off(lambda, es) || off(log_a, 4) ||
+      misaligned(out) || off(state, kAlign))
+    return LOGLIN_ERR_ALIGN;
+  loglin::DecodeFn fn = loglin::lookup_decode(dims->io_dtype, (int)dims->headdim, (int)dims->dstate);
+  if (!fn) return LOGLIN_ERR_SHAPE;
+  loglin::DecodeParams dp{};
+  dp.X = X;
+  dp.Bm = B;
+  dp.Cm = C;
+  dp.log_a = log_a;
+  dp.lam = lambda;
+  dp.out = out;
+  dp.S = static_cast<float*>(state);
+  dp.gd = reinterpret_cast<float*>(static_cast<char*>(state) + pl.off_g);
+  dp.batch = (int)dims->batch;
+  dp.nheads = (int)dims->nheads;
+  dp.ngroups = (int)dims->ngroups;
+  dp.nlevels = (int)dims->nlevels;
+  dp.ll = pl.ll;
+  dp.t = t;
+  return fn(dp, stream) ? LOGLIN_ERR_HIP : LOGLIN_OK;
+}
 
 size_t loglin_workspace_bytes_ex(const loglin_dims* dims, int chunk, const loglin_opts* opts) {
   Plan pl;

@@ -53,7 +53,7 @@ EXPORTS = (
     "loglin_workspace_bytes", "loglin_workspace_bytes_ex", "loglin_fwd",
     "loglin_fwd_ex", "loglin_validate", "loglin_strerror",
     "loglin_plan_seg_log2", "loglin_event_create", "loglin_event_destroy",
-    "loglin_event_elapsed_ms",
+    "loglin_event_elapsed_ms", "loglin_decode_state_bytes", "loglin_decode_step",
 )
 
 
@@ -89,6 +89,10 @@ def lib():
     L.loglin_event_destroy.restype = i32
     L.loglin_event_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
     L.loglin_event_elapsed_ms.restype = i32
+    L.loglin_decode_state_bytes.argtypes = [pd]
+    L.loglin_decode_state_bytes.restype = sz
+    L.loglin_decode_step.argtypes = [vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, pd, vp]
+    L.loglin_decode_step.restype = i32
     _lib = L
     return L
 
@@ -216,5 +220,54 @@ def loglin_fwd(X, B, C, log_a, lam, chunk, out, *, workspace=None, stream=None,
     rc = lib().loglin_fwd_ex(_ptr(X), _ptr(B), _ptr(C), _ptr(log_a), _ptr(lam), int(chunk),
                              _ptr(out), ctypes.byref(dims), _ptr(workspace), ws_bytes, sptr,
                              popts)
+    _check(rc)
+    return out
+
+
+def decode_dims(X, B, lam, seqlen) -> loglin_dims:
+    """Dims of a decode state for tokens X [Bt,H,P], B [Bt,G,N], lam
+    [Bt,H,L] and `seqlen` positions."""
+    Bt, H, P = X.shape
+    G, N = B.shape[1], B.shape[2]
+    if X.dtype == torch.bfloat16:
+        dt = LOGLIN_BF16
+    elif X.dtype == torch.float32:
+        dt = LOGLIN_F32
+    else:
+        raise TypeError(f"unsupported dtype {X.dtype}")
+    return make_dims(Bt, seqlen, H, G, P, N, lam.shape[2], dt)
+
+
+def loglin_decode_state_bytes(dims: loglin_dims) -> int:
+    return int(lib().loglin_decode_state_bytes(ctypes.byref(dims)))
+
+
+def loglin_decode_step(state, t, X, B, C, log_a, lam, out, *, seqlen, stream=None):
+    """Enqueue decode step t: advance `state` (a uint8 device tensor of
+    loglin_decode_state_bytes bytes, reused across the steps t = 0, 1, ...)
+    by token t and write its output to `out`.  Tensors: X/out [Bt,H,P], B/C
+    [Bt,G,N], log_a [Bt,H] float32, lam [Bt,H,L]; `seqlen` is the number of
+    positions the state was sized for.  Returns `out`."""
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("loglin_decode_step needs GPU tensors")
+    dims = decode_dims(X, B, lam, seqlen)
+    io = X.dtype
+    Bt, H, P = X.shape
+    G, N = B.shape[1], B.shape[2]
+    _check_tensor("X", X, (Bt, H, P), io, dev)
+    _check_tensor("B", B, (Bt, G, N), io, dev)
+    _check_tensor("C", C, (Bt, G, N), io, dev)
+    _check_tensor("log_a", log_a, (Bt, H), torch.float32, dev)
+    _check_tensor("lam", lam, (Bt, H, lam.shape[2]), io, dev)
+    _check_tensor("out", out, (Bt, H, P), io, dev)
+    need = loglin_decode_state_bytes(dims)
+    if state.numel() * state.element_size() < need:
+        raise ValueError(f"state holds {state.numel() * state.element_size()} bytes, needs {need}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib().loglin_decode_step(_ptr(state), int(t), _ptr(X), _ptr(B), _ptr(C), _ptr(log_a),
+                                  _ptr(lam), _ptr(out), ctypes.byref(dims),
+                                  ctypes.c_void_p(stream.cuda_stream))
     _check(rc)
     return out

@@ -156,3 +156,49 @@ def test_strerror_all_codes():
     for code in L.ERRORS:
         assert isinstance(L.loglin_strerror(code), str)
     assert L.loglin_strerror(-99) == "unknown error code"
+
+
+def decode_dims(**kw):
+    d = dict(batch=1, seqlen=32768, nheads=48, ngroups=24, headdim=64, dstate=128,
+             nlevels=16, io_dtype=L.LOGLIN_BF16)
+    d.update(kw)
+    return L.make_dims(**d)
+
+
+def test_decode_state_bytes_formula():
+    """Level states fp32 [B,H,LL,N,P] then two banks of decay factors
+    [B,H,2,LL], each 256-byte aligned; LL = ceil(log2 seqlen) + 1."""
+    d = decode_dims()
+    need = L.loglin_decode_state_bytes(d)
+    core = 48 * 16 * 128 * 64 * 4
+    assert core + 48 * 2 * 16 * 4 <= need <= core + 48 * 2 * 16 * 4 + 512
+    assert L.loglin_decode_state_bytes(decode_dims(seqlen=1, nlevels=1)) > 0
+    assert L.loglin_decode_state_bytes(decode_dims(nlevels=15)) == 0
+    assert L.lib().loglin_decode_state_bytes(None) == 0
+
+
+def decode_step(dims, t=0, state=1 << 20, ptrs=None):
+    p = dict(X=FAKE, B=FAKE, C=FAKE, log_a=FAKE, lam=FAKE, out=FAKE)
+    p.update(ptrs or {})
+    return L.lib().loglin_decode_step(state, t, p["X"], p["B"], p["C"], p["log_a"], p["lam"],
+                                      p["out"], ctypes.byref(dims), None)
+
+
+@pytest.mark.parametrize("kw,t,code", [
+    (dict(), -1, -2), (dict(), 32768, -2), (dict(batch=0), 0, -2),
+    (dict(nlevels=15), 0, -6), (dict(ngroups=5), 0, -5), (dict(io_dtype=9), 0, -7),
+    (dict(headdim=48), 0, -10),
+])
+def test_decode_step_errors(kw, t, code):
+    """Invalid decode steps fail on the host, before any HIP call."""
+    assert decode_step(decode_dims(**kw), t=t) == code
+
+
+@pytest.mark.parametrize("name", ["X", "B", "C", "log_a", "lam", "out"])
+def test_decode_null_and_misaligned(name):
+    assert decode_step(decode_dims(), ptrs={name: None}) == -1
+    assert decode_step(decode_dims(), ptrs={name: FAKE + 1}) == -9
+    if name == "out":
+        assert decode_step(decode_dims(), ptrs={name: FAKE + 4}) == -9
+    assert decode_step(decode_dims(), state=None) == -1
+    assert decode_step(decode_dims(), state=FAKE + 64) == -9
