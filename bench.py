@@ -12,6 +12,10 @@ of the dominant kernel (its algorithmic bytes and flops per launch over its
 average duration, measured with HIP events the library records on the
 launch stream), and the fp64 CPU oracle timed on a bounded sample of the
 same workload on this host's cores.
+
+--mode decode instead times one-token decode steps at the end of the same
+32K-token context (the state is first built by decode steps from t = 0)
+and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -179,6 +183,7 @@ def main():
     ap.add_argument("--seg-log2", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of wall time for the CPU oracle sample (0: skip)")
+    ap.add_argument("--mode", choices=("forward", "decode"), default="forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of this many MiB "
                          "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -191,6 +196,8 @@ def main():
     cfg = inputs.CONFIGS[args.workload]
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     d = inputs.make_inputs(cfg, seed=0)
+    if args.mode == "decode":
+        return main_decode(args, cfg, d)
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -316,6 +323,91 @@ def main():
         "gpu_event_ms_per_step": round(gpu_s / K * 1e3, 4),
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample")},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def decode_bytes_per_step(cfg, t: int) -> int:
+    """Algorithmic bytes of decode step t: every occupied bucket state read
+    once (fp32 N x P per head), the new and the merged bucket written, the
+    token's inputs read and its output written."""
+    Bt, H, G, P, N, L = cfg.batch, cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.nlevels
+    e = 2 if cfg.dtype == "bf16" else 4
+    # buckets occupied after step t - 1: level 0 and level k + 1 for every
+    # set bit k of t - 1; a step reads all of them
+    occupied = 0 if t == 0 else 1 + bin(t - 1).count("1")
+    state = N * P * 4
+    per_head = occupied * state + 2 * state + (2 * P + L) * e + 4
+    return Bt * H * per_head + Bt * G * 2 * N * e
+
+
+def main_decode(args, cfg, d):
+    import torch
+
+    from ssm_scan_amd import loglin as L
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = {}
+    for k in ("X", "B", "C", "lam"):
+        if cfg.dtype == "bf16":
+            t[k] = torch.from_numpy(np.ascontiguousarray(d["bits"][k]).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        else:
+            t[k] = torch.from_numpy(d[k]).to(dev)
+    t["log_a"] = torch.from_numpy(d["log_a"]).to(dev)
+    del d
+    T, K = cfg.seqlen, args.steps
+    toks = [{k: t[k][:, s].contiguous() for k in ("X", "B", "C", "log_a", "lam")}
+            for s in range(T - K - args.warmup, T)]
+    out = torch.empty_like(toks[0]["X"])
+    dims = L.decode_dims(toks[0]["X"], toks[0]["B"], toks[0]["lam"], T)
+    state = torch.empty(L.loglin_decode_state_bytes(dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s, tok):
+        L.loglin_decode_step(state, s, tok["X"], tok["B"], tok["C"], tok["log_a"], tok["lam"], out,
+                             seqlen=T, stream=stream)
+
+    print(f"[bench] building the decode state over {T - K} tokens", file=sys.stderr, flush=True)
+    t0 = T - K - args.warmup
+    for s in range(t0):
+        tok = {k: t[k][:, s].contiguous() for k in ("X", "B", "C", "log_a", "lam")}
+        step(s, tok)
+    for i in range(args.warmup):
+        step(t0 + i, toks[i])
+    torch.cuda.synchronize()
+    print("[bench] timed decode steps", file=sys.stderr, flush=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    w0 = time.perf_counter()
+    for i in range(K):
+        evs[2 * i].record(stream)
+        step(T - K + i, toks[args.warmup + i])
+        evs[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kern_us = [evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3 for i in range(K)]
+    byts = [decode_bytes_per_step(cfg, T - K + i) for i in range(K)]
+    gbs = float(np.mean([b / (u * 1e-6) / 1e9 for b, u in zip(byts, kern_us)]))
+    res = {
+        "metric": "log-linear Mamba-2 decode tokens/s at a 32K context, H=48",
+        "value": round(cfg.batch * K / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"log-linear Mamba-2 one-token decode, {cfg.name} context",
+                   "batch": cfg.batch, "positions": [T - K, T - 1], "nheads": cfg.nheads,
+                   "ngroups": cfg.ngroups, "headdim": cfg.headdim, "dstate": cfg.dstate,
+                   "nlevels": cfg.nlevels},
+        "kernel_us_mean": round(float(np.mean(kern_us)), 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "alg_bytes_per_step_mean": int(np.mean(byts))},
     }
     print(json.dumps(res), flush=True)
 

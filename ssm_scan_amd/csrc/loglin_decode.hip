@@ -23,102 +23,88 @@
 
 namespace loglin {
 
-// grid: batch * heads * (P / 16) work-groups of 256 threads.  Thread
-// (r, u) = (tid / 4, tid % 4) owns columns 16 pb + 4u .. +3 of the rows
-// n = r + 64 k.
+// grid: batch * heads * (P / 4) work-groups of 128 threads: thread n owns
+// row n of the 4 columns 4 pq .. 4 pq + 3 (rows n >= N idle), so a level
+// costs one 16-byte read per thread and many small work-groups spread the
+// step over the CUs.  A level state is stored column-quad major,
+// [P/4][N][4], so a work-group's reads of a level are one contiguous run.
 template <class T, int P, int N>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams dp) {
-  constexpr int PB = P / 16;
-  constexpr int RK = (N + 63) / 64;  // rows per thread
-  const int tid = threadIdx.x, u = tid & 3, rr = tid >> 2;
-  const int pb = blockIdx.x % PB;
-  const int bh = blockIdx.x / PB;
+__global__ __launch_bounds__(128) void decode_kernel(DecodeParams dp) {
+  constexpr int PQ = P / 4;
+  static_assert(N <= 128, "one row per thread");
+  const int n = threadIdx.x;
+  const bool row = n < N;
+  const int pq = blockIdx.x % PQ;
+  const int bh = blockIdx.x / PQ;
   const int H = dp.nheads, G = dp.ngroups, LL = dp.ll, L = dp.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t t = dp.t;
   const int z = t > 0 ? __builtin_ctzll((unsigned long long)t) : -1;  // levels 0..z merge into z+1
   const float a = expf(dp.log_a[bh]);
   const T* lam = static_cast<const T*>(dp.lam) + (int64_t)bh * L;
-  const T* Cv = static_cast<const T*>(dp.Cm) + ((int64_t)b * G + grp) * N;
-  const T* Bv = static_cast<const T*>(dp.Bm) + ((int64_t)b * G + grp) * N;
   const T* Xv = static_cast<const T*>(dp.X) + (int64_t)bh * P;
   const float* gold = dp.gd + ((int64_t)bh * 2 + (t & 1)) * LL;
   float* S = dp.S + (int64_t)bh * LL * N * P;
-  const int c0 = 16 * pb + 4 * u;  // first of this thread's 4 columns
+  const int c0 = 4 * pq;  // first of the work-group's 4 columns
 
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = to_f(Xv[c0 + i]);
-  float cn[RK], bn[RK];
-#pragma unroll
-  for (int k = 0; k < RK; ++k) {
-    const int n = rr + 64 * k;
-    cn[k] = n < N ? to_f(Cv[n]) : 0.f;
-    bn[k] = n < N ? to_f(Bv[n]) : 0.f;
-  }
+  const int64_t gb = ((int64_t)b * G + grp) * N;
+  const float cn = row ? to_f(static_cast<const T*>(dp.Cm)[gb + n]) : 0.f;
+  const float bn = row ? to_f(static_cast<const T*>(dp.Bm)[gb + n]) : 0.f;
   const float lam_merge = z >= 0 ? to_f(lam[z + 1]) : 0.f;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 merged[RK];
+  // new level 0, the token itself (S_0 = B_t X_t^T), then every occupied
+  // older level; the levels 0..z also merge into level z+1
+  f32x4 acc = (to_f(lam[0]) * bn * cn) * f32x4{x[0], x[1], x[2], x[3]};
+  f32x4 merged = {0.f, 0.f, 0.f, 0.f};
+  if (t > 0 && row) {
+    constexpr int U = 8;  // levels whose loads are in flight together
+    for (int l0 = 0; l0 < LL; l0 += U) {  // uniform; empty levels load nothing
+      f32x4 sv[U];
+      float gv[U];
 #pragma unroll
-  for (int k = 0; k < RK; ++k) merged[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (t > 0) {
-    for (int l = 0; l < LL; ++l) {  // uniform loop; empty levels are skipped
-      const float gl = gold[l];
-      if (gl == 0.f || l == z + 1) continue;
-      const bool merge = l <= z;
-      const float w = (merge ? lam_merge : to_f(lam[l])) * a * gl;
-      const float* Sl = S + (int64_t)l * N * P;
+      for (int i = 0; i < U; ++i) {
+        const int l = l0 + i;
+        gv[i] = (l < LL && l != z + 1) ? gold[l] : 0.f;
+        sv[i] = gv[i] != 0.f ? *reinterpret_cast<const f32x4*>(S + (((int64_t)l * PQ + pq) * N + n) * 4)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-      for (int k = 0; k < RK; ++k) {
-        const int n = rr + 64 * k;
-        if (n < N) {
-          const f32x4 s = *reinterpret_cast<const f32x4*>(Sl + n * P + c0);
-          acc += (w * cn[k]) * s;
-          if (merge) merged[k] += gl * s;
+      for (int i = 0; i < U; ++i) {
+        const int l = l0 + i;
+        if (gv[i] != 0.f) {
+          const bool merge = l <= z;
+          const float w = (merge ? lam_merge : to_f(lam[l])) * a * gv[i];
+          acc += (w * cn) * sv[i];
+          if (merge) merged += gv[i] * sv[i];
         }
       }
     }
   }
-  // new level 0: the token itself, S_0 = B_t X_t^T
-  {
-    float bc = 0.f;
-#pragma unroll
-    for (int k = 0; k < RK; ++k) bc += bn[k] * cn[k];
-    const float w0 = to_f(lam[0]) * bc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += w0 * x[i];
+  if (row) {  // the merged level and level 0, stored without decay factor
+    if (z >= 0) *reinterpret_cast<f32x4*>(S + (((int64_t)(z + 1) * PQ + pq) * N + n) * 4) = merged;
+    *reinterpret_cast<f32x4*>(S + ((int64_t)pq * N + n) * 4) =
+        f32x4{bn * x[0], bn * x[1], bn * x[2], bn * x[3]};
   }
 
-  // the merged level and level 0, stored without decay factor
+  // sum over the rows: each wave by shuffles, then the two waves in LDS
 #pragma unroll
-  for (int k = 0; k < RK; ++k) {
-    const int n = rr + 64 * k;
-    if (n < N) {
-      if (z >= 0) *reinterpret_cast<f32x4*>(S + ((int64_t)(z + 1) * N + n) * P + c0) = merged[k];
-      *reinterpret_cast<f32x4*>(S + (int64_t)n * P + c0) = f32x4{bn[k] * x[0], bn[k] * x[1], bn[k] * x[2], bn[k] * x[3]};
-    }
-  }
-
-  // reduce acc over the 64 row groups: lanes with equal u within a wave,
-  // then the four waves through LDS
-#pragma unroll
-  for (int d = 4; d < 64; d <<= 1) {
+  for (int d = 1; d < 64; d <<= 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], d, 64);
   }
-  __shared__ f32x4 part[4][4];
-  const int wave = tid >> 6, lane = tid & 63;
-  if (lane < 4) part[wave][lane] = acc;
+  __shared__ f32x4 part[2];
+  if ((n & 63) == 0) part[n >> 6] = acc;
   __syncthreads();
-  if (tid < 4) {
-    f32x4 y = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
-    T* o = static_cast<T*>(dp.out) + (int64_t)bh * P + 16 * pb + 4 * tid;
-    store4(o, y);
+  if (n == 0) {
+    T* o = static_cast<T*>(dp.out) + (int64_t)bh * P + c0;
+    store4(o, part[0] + part[1]);
   }
   // decay factors for the next step (one work-group per head writes them)
-  if (pb == 0 && tid < LL) {
-    const int l = tid;
+  if (pq == 0 && n < LL) {
+    const int l = n;
     float gn;
     if (l == 0) gn = 1.f;
     else if (t == 0 || l <= z) gn = 0.f;
@@ -130,8 +116,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams dp) {
 
 template <class T, int P, int N>
 int launch_decode(const DecodeParams& dp, void* stream) {
-  const int grid = dp.batch * dp.nheads * (P / 16);
-  hipLaunchKernelGGL((decode_kernel<T, P, N>), dim3(grid), dim3(256), 0,
+  const int grid = dp.batch * dp.nheads * (P / 4);
+  hipLaunchKernelGGL((decode_kernel<T, P, N>), dim3(grid), dim3(128), 0,
                      static_cast<hipStream_t>(stream), dp);
   return (int)hipGetLastError();
 }

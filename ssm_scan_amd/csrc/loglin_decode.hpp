@@ -13,7 +13,7 @@ struct DecodeParams {
   const float* log_a; // [B, H]
   const void* lam;    // [B, H, L]
   void* out;          // [B, H, P]
-  float* S;           // [B, H, LL, N, P] level states (fp32, stored without their decay)
+  float* S;           // [B, H, LL, P/4, N, 4] level states (fp32, stored without their decay)
   float* gd;          // [B, H, 2, LL] per-level decay factors; bank t & 1 is read at step t
   int batch, nheads, ngroups, nlevels, ll;
   int64_t t;

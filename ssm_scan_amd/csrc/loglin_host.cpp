@@ -134,7 +134,7 @@ loglin::LaunchFn pick(int dtype, int chunk, int P, int N) {
   return nullptr;
 }
 
-// Decode state: level states fp32 [B, H, LL, N, P], then the two banks of
+// Decode state: level states fp32 [B, H, LL, P/4, N, 4], then the two banks of
 // per-level decay factors [B, H, 2, LL]; each region 256-byte aligned.
 struct DecodePlan {
   int ll;
@@ -155,7 +155,7 @@ int check_decode(const loglin_dims* d, DecodePlan* pl) {
   const int ll = ceil_log2(d->seqlen) + 1;
   if (d->nlevels < ll) return LOGLIN_ERR_LEVELS;
   if (!supported_shape(d->io_dtype, d->headdim, d->dstate)) return LOGLIN_ERR_SHAPE;
-  if (ll > 256) return LOGLIN_ERR_DIM;  // one thread per level writes the decay factors
+  if (ll > 128) return LOGLIN_ERR_DIM;  // one thread per level writes the decay factors
   pl->ll = ll;
   const size_t bh = (size_t)(d->batch * d->nheads);
   pl->off_g = round_up(bh * ll * (size_t)(d->headdim * d->dstate) * sizeof(float));
