@@ -15,7 +15,9 @@ same workload on this host's cores.
 
 --mode decode instead times one-token decode steps at the end of the same
 32K-token context (the state is first built by decode steps from t = 0)
-and prints its own JSON line.
+and prints its own JSON line.  --mode naive times the unfused variant: one
+whole pass per level (only that level's terms computed), summed in fp32,
+against the fused pass on the same inputs.
 """
 from __future__ import annotations
 
@@ -183,7 +185,7 @@ def main():
     ap.add_argument("--seg-log2", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of wall time for the CPU oracle sample (0: skip)")
-    ap.add_argument("--mode", choices=("forward", "decode"), default="forward")
+    ap.add_argument("--mode", choices=("forward", "decode", "naive"), default="forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of this many MiB "
                          "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -228,6 +230,9 @@ def main():
         L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], cfg.chunk, out,
                      workspace=ws, stream=stream, seg_log2=args.seg_log2,
                      stage_events=events)
+
+    if args.mode == "naive":
+        return main_naive(args, cfg, t, out, ws, stream, step)
 
     if args.calibrate_copy > 0:
         nb = args.calibrate_copy << 20
@@ -323,6 +328,63 @@ def main():
         "gpu_event_ms_per_step": round(gpu_s / K * 1e3, 4),
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample")},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def main_naive(args, cfg, t, out, ws, stream, fused_step):
+    import torch
+
+    from ssm_scan_amd import loglin as L
+
+    LL = inputs.num_levels(cfg.seqlen)
+    acc = torch.zeros(out.shape, dtype=torch.float32, device=out.device)
+    part = torch.empty_like(out)
+
+    def naive_step():
+        acc.zero_()
+        for lv in range(LL):  # one whole pass per level, only that level's terms
+            L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], cfg.chunk, part,
+                         workspace=ws, stream=stream, level_mask=1 << lv)
+            acc.add_(part.float())
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    for _ in range(2):
+        naive_step()
+        fused_step()
+    torch.cuda.synchronize()
+    ref = out.float()
+    err = float(((acc - ref).abs().amax(dim=(1, 3)) / ref.abs().amax(dim=(1, 3))).max())
+    K = max(1, args.steps // 5)
+    naive_ms = timed(naive_step, K)
+    fused_ms = timed(fused_step, K)
+    res = {
+        "metric": "log-linear Mamba-2 fwd tokens/s at T=32K, H=48: one pass per level (unfused)",
+        "value": round(cfg.batch * cfg.seqlen / (naive_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "ms_per_step": round(naive_ms, 4),
+        "fused_ms_per_step": round(fused_ms, 4),
+        "fused_over_naive_speedup": round(naive_ms / fused_ms, 2),
+        "passes_per_step": LL,
+        "max_rel_diff_sum_vs_fused": err,
+        "higher_is_better": True,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"log-linear Mamba-2 forward, {cfg.name}, one pass per level",
+                   "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
+                   "ngroups": cfg.ngroups, "headdim": cfg.headdim, "dstate": cfg.dstate,
+                   "chunk": cfg.chunk, "nlevels": cfg.nlevels},
     }
     print(json.dumps(res), flush=True)
 

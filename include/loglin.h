@@ -112,6 +112,10 @@ typedef struct {
   /* NULL, or LOGLIN_NUM_STAGES + 1 events (hipEvent_t) recorded on
    * `stream` at the stage boundaries, for per-pass timing. */
   void* const* stage_events;
+  /* Levels the output includes: bit l set keeps level l (0 = all levels).
+   * The excluded levels' terms are skipped, not computed and zeroed, so a
+   * pass per level ("naive", unfused) can be timed against the fused one. */
+  uint64_t level_mask;
 } loglin_opts;
 
 /* Bytes of device workspace loglin_fwd needs for these sizes (may be 0).

@@ -69,6 +69,7 @@ struct Params {
   int ks;     // log2(ns)
   int ll;     // levels used: log2(seqlen) + 1
   int hp;     // heads per work-group of the output pass (1 or 2)
+  unsigned long long lmask;  // levels the output includes (bit l: level l)
   int total;  // logical work-groups of the kernel being launched
 };
 
@@ -705,7 +706,9 @@ struct OutCfg {
   static constexpr int MIN_BLOCKS = HP == 1 ? 2 : 1;
 };
 
-template <class T, int C, int P, int N, int HP>
+// MASKED: only the levels in pr.lmask enter the output (a separate
+// instantiation, so the full pass pays nothing for the option).
+template <class T, int C, int P, int N, int HP, bool MASKED>
 __global__ __launch_bounds__((OutCfg<T, C, P, N, HP>::NT), (OutCfg<T, C, P, N, HP>::MIN_BLOCKS))
 void output_kernel(Params pr) {
   using Cfg = OutCfg<T, C, P, N, HP>;
@@ -868,15 +871,20 @@ void output_kernel(Params pr) {
   // weight of level lvl for token t of head h0 + k in the current chunk;
   // par: the row starts in the upper half of its first word (bf16, odd
   // level count)
+  const unsigned long long lmask = MASKED ? pr.lmask : ~0ull;
   auto lam_at = [&](int k, int t, int lvl, int par) __attribute__((always_inline)) -> float {
     const int row = k * C + t;
+    float v;
     if constexpr (sizeof(T) == 4) {
-      return __uint_as_float(lam_w[row * LW + lvl]);
+      v = __uint_as_float(lam_w[row * LW + lvl]);
     } else {
       const unsigned short* hw = reinterpret_cast<const unsigned short*>(lam_w);
-      return __uint_as_float((unsigned)hw[2 * row * LW + par + lvl] << 16);
+      v = __uint_as_float((unsigned)hw[2 * row * LW + par + lvl] << 16);
     }
+    if constexpr (MASKED) return (lmask >> lvl) & 1 ? v : 0.f;  // left-out levels weigh 0
+    return v;
   };
+  const bool intra_on = !MASKED || (lmask & ((2ull << c_log) - 1)) != 0;  // levels 0..log2 C
   const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
   issue_c(j0, tid0 & 63);
@@ -909,7 +917,7 @@ void output_kernel(Params pr) {
 
     // ---- intra-chunk weights W[t][s] of every head, from the shared
     // transposed scores B C^T
-    for (int u = wave; u < Tl::TB * Tl::TB; u += NTW) {
+    for (int u = intra_on ? wave : Tl::TB * Tl::TB; u < Tl::TB * Tl::TB; u += NTW) {
       int tb, sb;
       score_tile<Tl::TB>(u, tb, sb);
       const int t = 16 * tb + r;
@@ -949,7 +957,7 @@ void output_kernel(Params pr) {
         Y[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < Tl::NKT; ++kt) {
-          if (kt * Tl::KB < 16 * (tb + 1)) {
+          if (intra_on && kt * Tl::KB < 16 * (tb + 1)) {
             auto af = frag_down<T, RX>(xs, kt * Tl::KB, 16 * wv, g, r);
             auto bf = load_frag<T>(wth + Tl::at(16 * tb + r, kt * Tl::KB + g * Tl::KPL));
             Y[tb] = M::mma(af, bf, Y[tb]);
@@ -989,7 +997,7 @@ void output_kernel(Params pr) {
         for (int kk = 0; kk < Tl::NKN; ++kk) cf[kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
 #pragma unroll
         for (int i = 0; i < RZ; ++i) {
-          if (i < nres) {
+          if (i < nres && (!MASKED || ((lmask >> lres[i]) & 1))) {
             f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zres[i][kk], cf[kk], tmp);
@@ -998,7 +1006,7 @@ void output_kernel(Params pr) {
         }
 #pragma unroll
         for (int e = 0; e < MM; ++e) {  // levels inside the segment
-          if (e < m && ((jl >> e) & 1)) {
+          if (e < m && ((jl >> e) & 1) && (!MASKED || ((lmask >> (c_log + e + 1)) & 1))) {
             f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zl[e][kk], cf[kk], tmp);
@@ -1013,6 +1021,7 @@ void output_kernel(Params pr) {
       while (mask) {
         const int ks = __builtin_ctz(mask) + 1;
         mask &= mask - 1;
+        if (MASKED && !((lmask >> (c_log + m + ks)) & 1)) continue;
         frag zcur[Tl::NKN];
         const T* zr = slot_of(h, ks) + slot_frag<T, N>(wv, 0, g, r);
 #pragma unroll

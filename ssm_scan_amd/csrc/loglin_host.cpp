@@ -266,6 +266,7 @@ int loglin_fwd_ex(const void* X, const void* B, const void* C, const float* log_
   pr.ks = pl.ks;
   pr.ll = pl.ll;
   pr.hp = pl.hp;
+  pr.lmask = (opts && opts->level_mask) ? opts->level_mask : ~0ull;
   void* const* ev = opts ? opts->stage_events : nullptr;
   int herr = fn(pr, static_cast<hipStream_t>(stream), ev);
   return herr ? LOGLIN_ERR_HIP : LOGLIN_OK;

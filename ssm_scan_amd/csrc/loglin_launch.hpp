@@ -18,7 +18,10 @@ void launch_output(Params pr, hipStream_t st) {
   using Cfg = OutCfg<T, C, P, N, HP>;
   pr.total = pr.batch * pr.ns * (pr.nheads / HP);
   const size_t shm = (size_t)HP * C * lam_words(pr.ll, (int)sizeof(T)) * 4;
-  hipLaunchKernelGGL((output_kernel<T, C, P, N, HP>), dim3(pad8(pr.total)), dim3(Cfg::NT), shm, st, pr);
+  if (pr.lmask == ~0ull)
+    hipLaunchKernelGGL((output_kernel<T, C, P, N, HP, false>), dim3(pad8(pr.total)), dim3(Cfg::NT), shm, st, pr);
+  else
+    hipLaunchKernelGGL((output_kernel<T, C, P, N, HP, true>), dim3(pad8(pr.total)), dim3(Cfg::NT), shm, st, pr);
 }
 
 // Returns 0 or hipError_t of the first failing launch (caller maps it).

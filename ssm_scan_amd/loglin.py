@@ -38,7 +38,8 @@ class loglin_dims(ctypes.Structure):
 
 class loglin_opts(ctypes.Structure):
     _fields_ = [("seg_log2", ctypes.c_int32), ("heads_per_block", ctypes.c_int32),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("level_mask", ctypes.c_uint64)]
 
 
 class LoglinError(RuntimeError):
@@ -111,10 +112,11 @@ def make_dims(batch, seqlen, nheads, ngroups, headdim, dstate, nlevels, io_dtype
                        io_dtype, 0)
 
 
-def _opts(seg_log2, events, heads_per_block=None):
-    if seg_log2 is None and events is None and heads_per_block is None:
+def _opts(seg_log2, events, heads_per_block=None, level_mask=None):
+    if seg_log2 is None and events is None and heads_per_block is None and level_mask is None:
         return None
     o = loglin_opts()
+    o.level_mask = 0 if level_mask is None else int(level_mask)
     o.seg_log2 = -1 if seg_log2 is None else int(seg_log2)
     o.heads_per_block = 0 if heads_per_block is None else int(heads_per_block)
     if events is not None:
@@ -188,7 +190,7 @@ def _check_tensor(name, t, shape, dtype, device):
 
 
 def loglin_fwd(X, B, C, log_a, lam, chunk, out, *, workspace=None, stream=None,
-               seg_log2=None, stage_events=None, heads_per_block=None):
+               seg_log2=None, stage_events=None, heads_per_block=None, level_mask=None):
     """Enqueue O = (C B^T . M^H) X into `out` on `stream` (default: torch's
     current stream).  Tensors: X/out [Bt,T,H,P], B/C [Bt,T,G,N], log_a
     [Bt,T,H] float32, lam [Bt,T,H,L]; X, B, C, lam, out share one dtype
@@ -208,7 +210,7 @@ def loglin_fwd(X, B, C, log_a, lam, chunk, out, *, workspace=None, stream=None,
     _check_tensor("log_a", log_a, (Bt, T, H), torch.float32, dev)
     _check_tensor("lam", lam, (Bt, T, H, lam.shape[3]), io, dev)
     _check_tensor("out", out, (Bt, T, H, P), io, dev)
-    opts = _opts(seg_log2, stage_events, heads_per_block)
+    opts = _opts(seg_log2, stage_events, heads_per_block, level_mask)
     popts = ctypes.byref(opts) if opts is not None else None
     need = int(lib().loglin_workspace_bytes_ex(ctypes.byref(dims), int(chunk), popts))
     if workspace is None and need > 0:

@@ -11,6 +11,7 @@ import torch
 
 from oracle import loglin_ref
 from ssm_scan_amd import inputs
+from ssm_scan_amd import loglin as L
 
 from .gpu_helpers import (max_rel_err, run_gpu, say, small_cfg, to_device, tol_of)
 
@@ -201,3 +202,49 @@ def test_head_pairs_odd_levels():
 def test_one_head_per_block(T, seg):
     """One head per output work-group forced where pairs are the default."""
     check(small_cfg(T=T, H=4, G=2), variant="slow_decay", seg_log2=seg, heads_per_block=1)
+
+
+def run_masked(cfg, t, mask, **kw):
+    out = torch.empty_like(t["X"])
+    L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], cfg.chunk, out, level_mask=mask,
+                 **kw)
+    return out
+
+
+@pytest.mark.parametrize("name", ["one", "intra", "inter", "mixed"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_level_mask(name, dtype):
+    """Only the masked levels enter the output: against the oracle with the
+    other levels' weights set to zero."""
+    cfg = small_cfg(dtype=dtype, T=2048, H=2, G=1, P=64, N=128 if dtype == "bf16" else 64,
+                    C=64 if dtype == "bf16" else 32)
+    LL = inputs.num_levels(cfg.seqlen)
+    c = cfg.chunk.bit_length() - 1
+    masks = {"one": 1 << (c + 2), "intra": (2 << c) - 1, "inter": ((1 << LL) - 1) & ~((2 << c) - 1),
+             "mixed": 0b101001 | (1 << (LL - 1))}
+    mask = masks[name]
+    say(f"[mask] {cfg.name} mask={mask:#x}")
+    d = inputs.make_inputs(cfg, 0, variant="slow_decay")
+    t = to_device(d, cfg)
+    got = run_masked(cfg, t, mask)
+    torch.cuda.synchronize()
+    keep = np.array([(mask >> l) & 1 for l in range(d["lam"].shape[-1])], dtype=np.float32)
+    ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"] * keep)
+    err = max_rel_err(got.float().cpu().numpy(), ref)
+    say(f"         max_rel_err={err:.3e}")
+    assert err <= tol_of(cfg), err
+
+
+def test_per_level_passes_sum_to_fused():
+    """One pass per level (the unfused variant), summed in fp32, equals the
+    fused output."""
+    cfg = small_cfg(T=4096, H=4, G=2)
+    d = inputs.make_inputs(cfg, 0, variant="slow_decay")
+    t = to_device(d, cfg)
+    LL = inputs.num_levels(cfg.seqlen)
+    total = sum(run_masked(cfg, t, 1 << l).float() for l in range(LL))
+    fused = run_gpu(cfg, t).float()
+    torch.cuda.synchronize()
+    ref = loglin_ref.loglin_forward(d["X"], d["B"], d["C"], d["log_a"], d["lam"])
+    assert max_rel_err(total.cpu().numpy(), ref) <= tol_of(cfg)
+    assert max_rel_err(total.cpu().numpy(), fused.cpu().numpy()) <= tol_of(cfg)
