@@ -569,81 +569,142 @@ void state_kernel(Params pr) {
 
 // ------------------------------------------------------------- pass 2
 
-// grid (ceil(P*N/256), batch*nheads).  Each thread owns one state element
-// and sweeps the segments in order, keeping a Fenwick stack of block sums in
-// fp32 registers: after segment q the top entry is the sum over the largest
-// aligned block of segments ending at q, decayed to q's end.  That block is
-// the lower half a later segment reads at level trailing_ones(q) + 1.
+// grid (ceil(P*N/512), batch*nheads), 128 threads.  Each thread owns four
+// consecutive state elements (16 bytes per segment) and sweeps the segments
+// in order, keeping a Fenwick stack of block sums in fp32 registers: after
+// segment q the top entry is the sum over the largest aligned block of
+// segments ending at q, decayed to q's end.  That block is the lower half a
+// later segment reads at level trailing_ones(q) + 1.  The four elements
+// share a state row, so they land in four consecutive slot positions.  D
+// bounds the stack depth: the host passes ns < 2^D.
 //
 // Before segment q the live entries are the set bits of q (entry i: a block
 // of 2^i segments), so the log-decay from the start of q's 2^(k-1)-aligned
 // block to q's start is the sum of the live entries' decays below bit k-1;
-// the first thread of each (batch, head) writes these gap decays.
-template <class T, int N>
-__global__ __launch_bounds__(256) void scan_kernel(Params pr, int pn) {
-  using M = Mfma<T>;
-  const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const bool valid = e < pn;
-  const bool gap_writer = blockIdx.x == 0 && threadIdx.x == 0;
-  const float* src = pr.seg_state + (int64_t)bh * pr.ns * pn;
-  const float* dec = pr.seg_decay + (int64_t)bh * pr.ns;
-  T* dst = static_cast<T*>(pr.slots) + (int64_t)bh * pr.ns * pn;
-  float* gd = pr.gap_decay + (int64_t)bh * pr.ns * (pr.ks + 1);
+// the stack's decays are the same in every thread, so threads 0..ks of the
+// first work-group of each (batch, head) write one level's gap each.
+//
+// Loads run SCAN_U segments ahead through a per-wave LDS ring, filled by
+// global_load_lds (lane i's 16 bytes land at ring slot + 16 i, and lane i
+// reads back only those).  In registers the prefetch would be copied around
+// the loop by the register allocator (the stack pushes loaded values), and
+// each copy waits for its load.  The segment log-decays are staged in LDS
+// too, SCAN_DEC at a time: as scalar loads their waits would complete out
+// of order and also wait for the prefetch.
+constexpr int SCAN_NT = 128;
+constexpr int SCAN_U = 16;
+constexpr int SCAN_DEC = 1024;
 
-  float stk[MAX_DEPTH], stka[MAX_DEPTH];
-#pragma unroll
-  for (int i = 0; i < MAX_DEPTH; ++i) stk[i] = stka[i] = 0.f;
-  constexpr int U = 8;  // segments per batch; the next batch's loads fly meanwhile
+// s_waitcnt on the vector memory counter alone.  Written as inline assembly
+// with a memory clobber so that no LDS read of the copied data is moved
+// above it (the builtin form does not order memory accesses).
+template <int NV>
+__device__ inline void wait_vm() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NV) : "memory");
+}
+
+template <class T, int N, int D>
+__global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
+  using M = Mfma<T>;
+  constexpr int U = SCAN_U;
+  static_assert(SCAN_DEC % U == 0, "decay tiles hold whole batches");
+  __shared__ float dec_s[SCAN_DEC];
+  __shared__ f32x4 ring[SCAN_NT / 64][U][64];
+  const int bh = blockIdx.y;
   const int ns = pr.ns;
-  float vb[U], db[U];
-  auto load = [&](int q0) __attribute__((always_inline)) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const float* dec = pr.seg_decay + (int64_t)bh * ns;
+  // pn is a multiple of 256, so a wave's 256 elements are all valid or all idle
+  const int e = (blockIdx.x * SCAN_NT + threadIdx.x) * 4;
+  const bool valid = e < pn;
+  const bool gap_lane = blockIdx.x == 0 && (int)threadIdx.x <= pr.ks;
+  const float* src = pr.seg_state + (int64_t)bh * ns * pn;
+  T* dst = static_cast<T*>(pr.slots) + (int64_t)bh * ns * pn;
+  float* gd = pr.gap_decay + (int64_t)bh * ns * (pr.ks + 1);
+  const int di = valid ? slot_index<T, N>(e / N, e % N) : 0;
+
+  f32x4 stk[D];
+  float stka[D];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + u;
-      vb[u] = (valid && q < ns - 1) ? src[(int64_t)q * pn + e] : 0.f;  // last one is never read
-      db[u] = q < ns ? dec[q] : 0.f;
-    }
+  for (int i = 0; i < D; ++i) {
+    stk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stka[i] = 0.f;
+  }
+  // Every prefetch is issued, so that each wave's count of memory operations
+  // per segment is fixed: the segment index is clamped to the last one
+  // stored, ns - 2 (the pass runs for ns > 1), and idle lanes read element 0.
+  // What such a copy holds is only ever pushed by the final segment, whose
+  // result no one reads.
+  const int ec = valid ? e : 0;
+  auto prefetch = [&](int q, int slot) __attribute__((always_inline)) {
+    dma_16x64(src + (int64_t)min(q, ns - 2) * pn + ec, lds_addr(&ring[wv][slot][0]));
   };
-  load(0);
-  for (int q0 = 0; q0 < ns; q0 += U) {
-    float v_cur[U], d_cur[U];
+  auto refill = [&](int q0) __attribute__((always_inline)) {  // uniform
+    __syncthreads();
+    for (int i = threadIdx.x; i < SCAN_DEC && q0 + i < ns; i += SCAN_NT) dec_s[i] = dec[q0 + i];
+    __syncthreads();
+  };
+  // one segment: fold the stack entries below its level in, push, store
+  auto step = [&](f32x4 v, int q) __attribute__((always_inline)) {
+    float acur = dec_s[q % SCAN_DEC];
+    const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q (uniform)
+    if (gap_lane) {  // lane k writes level k's gap; one store, no loop
+      float run = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v_cur[u] = vb[u];
-      d_cur[u] = db[u];
+      for (int i = 0; i + 1 < D; ++i)
+        if (i + 1 < (int)threadIdx.x && ((q >> i) & 1)) run += stka[i];
+      gd[q * (pr.ks + 1) + threadIdx.x] = run;
     }
-    if (q0 + U < ns) load(q0 + U);
+    // Unrolled into uniform branches, one per entry, so that every stack
+    // index is a constant and the stack stays in registers (a loop with an
+    // early exit lets the compiler sink the push into one store at a
+    // runtime index, which moves the stack to scratch memory).
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + u;
-      if (q >= ns) break;
-      if (gap_writer) {
-        float run = 0.f;
-        gd[q * (pr.ks + 1)] = 0.f;
-        for (int k = 1; k <= pr.ks; ++k) {
-          gd[q * (pr.ks + 1) + k] = run;
-          if ((q >> (k - 1)) & 1) run += stka[k - 1];
-        }
-      }
-      float v = v_cur[u];
-      float acur = d_cur[u];
-      const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q (uniform)
-      // Unrolled with uniform early exits: only z + 1 steps execute, and the
-      // stack stays in registers (its index is a constant in every step).
+    for (int i = 0; i < D; ++i) {
+      if (i < z) {
+        const float w = M::ex(acur);
 #pragma unroll
-      for (int i = 0; i < MAX_DEPTH; ++i) {
-        if (i == z) {
-          stk[i] = v;
-          stka[i] = acur;
-          break;
-        }
-        v = M::ex(acur) * stk[i] + v;
+        for (int c = 0; c < 4; ++c) v[c] = w * stk[i][c] + v[c];
         acur += stka[i];
       }
-      if (valid && q < ns - 1) dst[(int64_t)q * pn + slot_index<T, N>(e / N, e % N)] = from_f<T>(v);
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (i == z) {
+        stk[i] = v;
+        stka[i] = acur;
+      }
+    }
+    if (valid && q < ns - 1) store4(dst + (int64_t)q * pn + di, v);
+  };
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) prefetch(u, u);
+  const int nfull = ns / U * U;
+  for (int q0 = 0; q0 < nfull; q0 += U) {
+    if (q0 % SCAN_DEC == 0) refill(q0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // Memory operations this wave issued after segment q0+u's copy: the
+      // U-1 later copies, and in a valid wave the slot stores of the U-1
+      // segments since (none in the first batch).  The first work-group's
+      // gap stores only add to the count, which makes the wait longer.
+      if (valid && q0 > 0)
+        wait_vm<2 * U - 2>();
+      else
+        wait_vm<U - 1>();
+      const f32x4 v = ring[wv][u][lane];
+      step(v, q0 + u);
+      prefetch(q0 + U + u, u);  // v has been used, so its slot is free
     }
   }
+  // The last ns mod U segments: their copies were issued by the final batch
+  // (or the prologue) into slots 0, 1, ...
+  wait_vm<0>();
+  if (nfull < ns && nfull % SCAN_DEC == 0) refill(nfull);
+  for (int q = nfull; q < ns; ++q) step(ring[wv][q - nfull][lane], q);
 }
 
 // ------------------------------------------------------------- pass 3
