@@ -12,7 +12,8 @@ per-head scalar parameterisation, log a_t = -dt_t * exp(A_log[h]).
 
 Every tensor is drawn in float32 from numpy PCG64 streams, in flat blocks
 of BLOCK elements; block i of tensor k uses its own stream seeded with
-SeedSequence([seed, k, i]) (k: 0 X, 1 B, 2 C, 3 dt noise, 4 lambda, 5 A_log).
+SeedSequence([seed, k, i]) (k: 0 X, 1 B, 2 C, 3 dt noise, 4 lambda, 5 A_log,
+6 the output gradient dO of the backward pass).
 The values therefore do not depend on how many threads fill the blocks.
 bf16 inputs are rounded to nearest-even from those float32 draws.
 """
@@ -31,6 +32,7 @@ __all__ = [
     "make_inputs",
     "bf16_round",
     "num_levels",
+    "make_grad_output",
 ]
 
 
@@ -211,3 +213,20 @@ def make_inputs(cfg: Config, seed: int = 0, *, variant: str | None = None):
     else:
         raise ValueError(cfg.dtype)
     return out
+
+
+def make_grad_output(cfg: Config, seed: int = 0):
+    """Seeded upstream gradient dO [Bt,T,H,P] ~ N(0, 1) for the backward
+    pass, in the configuration's storage type (its own stream, so the
+    forward inputs of the same seed are unchanged).
+
+    Returns ``(values, bits)``: float32 values exactly as the kernels see
+    them, and the uint16 bf16 bit patterns (None for fp32 configs).
+    """
+    dO = _normal(seed, 6, cfg.shapes()["out"])
+    if cfg.dtype == "bf16":
+        bits, vals = bf16_round(dO)
+        return vals, bits
+    if cfg.dtype == "fp32":
+        return np.ascontiguousarray(dO, dtype=np.float32), None
+    raise ValueError(cfg.dtype)
