@@ -189,6 +189,49 @@ int loglin_decode_step(void* state, int64_t t, const void* X, const void* B,
                        const void* C, const float* log_a, const void* lambda,
                        void* out, const loglin_dims* dims, void* stream);
 
+/* ---- Backward pass -------------------------------------------------------
+ *
+ * Operation: the gradients of loglin_fwd's O = (C B^T ⊙ M^H) X (log-linear
+ * attention write-up, sections "special structure: tree partition" and
+ * "efficient training algorithm"; the write-up names the backward pass but
+ * prints no formula, so these are the calculus of that definition) for an
+ * upstream gradient dO, with S = C B^T, D = dO X^T and M = M^H:
+ *
+ *     dX_s = sum_t (M ⊙ S)[t, s] dO_t        dB_s = sum_t (M ⊙ D)[t, s] C_t
+ *     dC_t = sum_s (M ⊙ D)[t, s] B_s         dlambda[t, l] = dO_t . Y_t^(l)
+ *     dlog_a_r = sum over t >= r, s < r of (M ⊙ S ⊙ D)[t, s]
+ *
+ * where Y^(l) is the output with lambda one-hot on level l; dB and dC sum
+ * over the heads of each group.
+ *
+ * Inputs as for loglin_fwd (same dims, chunk and layouts), plus
+ *   dO      [batch, seqlen, nheads, headdim]   io dtype
+ * Outputs (written, not accumulated):
+ *   dX      [batch, seqlen, nheads, headdim]   io dtype
+ *   dB, dC  [batch, seqlen, ngroups, dstate]   io dtype
+ *   dlog_a  [batch, seqlen, nheads]            float32
+ *   dlambda [batch, seqlen, nheads, nlevels]   io dtype (0 on levels
+ *                                              >= ceil(log2 seqlen) + 1)
+ * All pointers are device pointers owned by the caller, 16-byte aligned;
+ * outputs must not alias inputs or each other.  Accumulation is fp32 and
+ * every output is written once, by one thread (no atomics): repeated calls
+ * are bit-identical.
+ *
+ * Supported: bf16 with chunk 32 or 64, headdim 32 or 64, dstate 32..128;
+ * float32 with chunk 16..64 and the forward's (headdim, dstate) pairs
+ * except headdim 64 with dstate 128 at chunk 64 (LDS); otherwise
+ * LOGLIN_ERR_SHAPE.  seqlen <= 2^31.  Errors as for loglin_fwd, all
+ * checked on the host before any HIP call.  The workspace (at least
+ * loglin_bwd_workspace_bytes bytes, 256-byte aligned, contents ignored on
+ * entry) must not be used by other work until the call's kernels finish. */
+size_t loglin_bwd_workspace_bytes(const loglin_dims* dims, int chunk);
+
+int loglin_bwd(const void* X, const void* B, const void* C,
+               const float* log_a, const void* lambda, const void* dO,
+               int chunk, void* dX, void* dB, void* dC, float* dlog_a,
+               void* dlambda, const loglin_dims* dims, void* workspace,
+               size_t workspace_bytes, void* stream);
+
 /* Event helpers for callers that time stages without linking HIP
  * themselves.  *event receives a hipEvent_t with timing enabled. */
 int loglin_event_create(void** event);

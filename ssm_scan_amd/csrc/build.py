@@ -1,7 +1,8 @@
 """Build libloglin.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-Compiles the host C-ABI unit, the decode unit and six forward instantiation
-units (io type x chunk) in parallel, then links ssm_scan_amd/_lib/libloglin.so.
+Compiles the host C-ABI unit, the decode unit, six forward instantiation
+units (io type x chunk) and five backward ones in parallel, then links
+ssm_scan_amd/_lib/libloglin.so.
 """
 from __future__ import annotations
 
@@ -36,6 +37,11 @@ def _units():
         for chunk in (16, 32, 64):
             units.append((f"loglin_inst_{io}_{chunk}",
                           os.path.join(HERE, "loglin_inst.hip"),
+                          [f"-DLOGLIN_IO={io}", f"-DLOGLIN_CHUNK={chunk}"]))
+    for io, chunks in (("bf16", (32, 64)), ("f32", (16, 32, 64))):
+        for chunk in chunks:
+            units.append((f"loglin_bwd_{io}_{chunk}",
+                          os.path.join(HERE, "loglin_bwd_inst.hip"),
                           [f"-DLOGLIN_IO={io}", f"-DLOGLIN_CHUNK={chunk}"]))
     return units
 

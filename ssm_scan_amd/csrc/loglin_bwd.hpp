@@ -1,0 +1,728 @@
+// Device code of the log-linear Mamba-2 backward pass for gfx950 (MI355X).
+//
+// Method: log-linear attention write-up (yoousoft.com/industry/3746),
+// sections "special structure: tree partition" (O = (C B^T ⊙ M^H) X with
+// M^H[t, s] = prod_{r=s+1..t} a_r * lambda[t, level(t, s)]) and "efficient
+// training algorithm" (intra-chunk blocks plus one low-rank term per chunk
+// level).  The write-up gives no backward formulas; these are the calculus
+// of that definition.  With S = C B^T, D = dO X^T and G = M ⊙ S ⊙ D:
+//
+//   dX_s = sum_t (M ⊙ S)[t, s] dO_t     dB_s = sum_t (M ⊙ D)[t, s] C_t
+//   dC_t = sum_s (M ⊙ D)[t, s] B_s      dlambda[t, l] = dO_t . Y^(l)_t
+//   dlog_a_r = sum_{t >= r} (dO_t . O_t - X_t . dX_t)
+//
+// (G's row sums are dO_t . O_t and its column sums X_s . dX_s, and log a_r
+// enters the entries with s < r <= t.)  dB and dC sum over the heads of a
+// group.
+//
+// Chunk level k (token level c + k, C = 2^c) pairs the lower and upper
+// halves of each aligned block of 2^k chunks.  Queries in the upper half
+// read the lower half's state (forward direction: key B, value X, lambda of
+// the query); keys in the lower half receive from the upper half (reverse
+// direction: key C, value dO, and lambda[t, c + k] of the upper half's
+// tokens, which is why those states are per level).  Launches:
+//   1. bwd_atot_kernel          per-chunk total log-decay;
+//   2. bwd_level_state_kernel   per (level, pair, piece of <= 8 chunks): the
+//                               decayed sum over the piece's chunks of the
+//                               lower half (forward) or upper half (reverse);
+//   3. bwd_level_reduce_kernel  pieces -> one state per (level, pair), io type;
+//   4. bwd_dq_kernel            per chunk: dC (this head) and dlambda, from the
+//                               intra block and the lower-half states;
+//   5. bwd_dkv_kernel           per chunk: dX and dB (this head), from the
+//                               intra block and the upper-half states;
+//   6. bwd_group_sum_kernel     dB, dC = sums over each group's heads;
+//   7. bwd_dloga_kernel         suffix sums of dO.O - X.dX.
+#pragma once
+
+#include "loglin_device.hpp"
+
+namespace loglin {
+
+struct BwdParams {
+  const void* X;
+  const void* Bm;
+  const void* Cm;
+  const float* log_a;
+  const void* lam;
+  const void* dO;
+  void* dX;
+  void* dB;
+  void* dC;
+  float* dloga;
+  void* dlam;
+  float* atot;    // [batch*nheads, nc]
+  float* part_f;  // [batch*nheads, npart, N, P] fp32, lower-half pieces
+  float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
+  void* zst;      // [batch*nheads, nstate, N, P] io type, lower-half sums
+  void* rst;      // [batch*nheads, nstate, N, P] io type, upper-half sums
+  float* dch;     // [batch, seqlen, nheads, N] this head's share of dC
+  float* dbh;     // [batch, seqlen, nheads, N] this head's share of dB
+  float* term1;   // [batch*nheads, seqlen] dO_t . O_t
+  float* term2;   // [batch*nheads, seqlen] X_t . dX_t
+  int batch, seqlen, nheads, ngroups, nlevels;
+  int nc, kc, ll;
+  int npart, nstate;  // per (batch, head)
+};
+
+// Pieces of at most BWD_PIECE chunks bound the serial work of one
+// work-group in the level-state pass.
+constexpr int BWD_PIECE = 8;
+// Levels held per token row in LDS (sequences up to 2^31 tokens).
+constexpr int BWD_LMAX = 32;
+
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// Pairs at chunk level k whose upper half holds at least one chunk.
+__host__ __device__ inline int bwd_pairs(int nc, int k) {
+  const int half = 1 << (k - 1);
+  return nc > half ? (nc - half + 2 * half - 1) / (2 * half) : 0;
+}
+// Pieces per half at chunk level k.
+__host__ __device__ inline int bwd_pieces(int k) {
+  return ((1 << (k - 1)) + BWD_PIECE - 1) / BWD_PIECE;
+}
+// Flat piece index (levels in order, then pairs, then pieces) -> parts.
+__device__ inline void bwd_piece_of(int item, int nc, int kc, int& k, int& pair, int& pc) {
+  for (k = 1; k <= kc; ++k) {
+    const int np = bwd_pieces(k), cnt = bwd_pairs(nc, k) * np;
+    if (item < cnt) {
+      pair = item / np;
+      pc = item % np;
+      return;
+    }
+    item -= cnt;
+  }
+  k = pair = pc = 0;  // not reached for item < npart
+}
+// Flat state index (levels in order, then pairs) -> parts, and back.
+__device__ inline void bwd_state_of(int item, int nc, int kc, int& k, int& pair) {
+  for (k = 1; k <= kc; ++k) {
+    const int cnt = bwd_pairs(nc, k);
+    if (item < cnt) {
+      pair = item;
+      return;
+    }
+    item -= cnt;
+  }
+  k = pair = 0;
+}
+__device__ inline int bwd_state_index(int nc, int k, int pair) {
+  int s = 0;
+  for (int k2 = 1; k2 < k; ++k2) s += bwd_pairs(nc, k2);
+  return s + pair;
+}
+__device__ inline int bwd_piece_base(int nc, int k) {
+  int s = 0;
+  for (int k2 = 1; k2 < k; ++k2) s += bwd_pairs(nc, k2) * bwd_pieces(k2);
+  return s;
+}
+
+// R token rows of W elements (global row stride grs) into LDS, Rows layout.
+template <class T, int R, int W, int NT>
+__device__ inline void rows_load(const T* g, int64_t grs, T* lds, int tid) {
+  using L = Rows<T, W>;
+  constexpr int PIECES = R * L::NBLK;
+#pragma unroll
+  for (int i0 = 0; i0 < PIECES; i0 += NT) {
+    const int i = i0 + tid;
+    if (i < PIECES) {
+      const int row = i / L::NBLK, pb = i % L::NBLK;
+      store16(lds + L::at(row, pb * L::VEC), load16(g + (int64_t)row * grs + pb * L::VEC));
+    }
+  }
+}
+
+// sum of a[lo..hi), the same bits in every lane of the wave
+__device__ inline float range_sum(const float* a, int lo, int hi, int lane) {
+  float s = 0.f;
+  for (int m = lo + lane; m < hi; m += 64) s += a[m];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  return s;
+}
+
+// sum over the 16 lanes r of a lane group (MFMA result columns)
+__device__ inline float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+// ------------------------------------------------------------ launch 1
+
+template <class T, int C>
+__global__ __launch_bounds__(64) void bwd_atot_kernel(BwdParams pr) {
+  __shared__ float cum[64], ecum[64], wst[64];
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int b = bh / pr.nheads, h = bh % pr.nheads;
+  const float la =
+      tid < C ? pr.log_a[((int64_t)b * pr.seqlen + (int64_t)j * C + tid) * pr.nheads + h] : 0.f;
+  chunk_decays<T, C>(la, cum, ecum, wst, tid);  // the same sums the chunk passes form
+  __syncthreads();
+  if (tid == 0) pr.atot[(int64_t)bh * pr.nc + j] = cum[C - 1];
+}
+
+// ------------------------------------------------------------ launch 2
+
+// grid (npart, batch*nheads).  Wave w owns state columns [16 w, 16 w + 16)
+// and all N rows (NB tiles of 16x16 fp32), as in the forward's state pass.
+// Forward direction (REV false): chunks of the piece in order, key B, value
+// X, weight exp(decay s -> chunk end); acc <- exp(Atot_j) acc + chunk state,
+// so the result is decayed to the end of the piece.  Reverse: chunks in
+// reverse order, key C, value dO, weight lambda[t, c + k] exp(decay from the
+// chunk start to t); acc <- exp(Atot_j) acc + chunk state, decayed to the
+// start of the piece.
+template <class T, int C, int P, int N, bool REV>
+__global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kernel(BwdParams pr) {
+  using Tl = Tiles<T, C, P, N>;
+  using M = Mfma<T>;
+  constexpr int NT = Tl::NT;
+  static_assert(Tl::KC == C, "token tiles are not padded here");
+  __shared__ __attribute__((aligned(16))) T ksh[C * N];
+  __shared__ __attribute__((aligned(16))) T vsh[C * P];
+  __shared__ __attribute__((aligned(16))) float cum[64], ecum[64], wst[64], wsh[64];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.y, H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
+  const int b = bh / H, h = bh % H, grp = h / (H / G);
+  const int64_t T_ = pr.seqlen;
+  int k, pair, pc;
+  bwd_piece_of(blockIdx.x, pr.nc, pr.kc, k, pair, pc);
+  const int half = 1 << (k - 1);
+  const int base = pair * 2 * half + (REV ? half : 0);  // first chunk of the half
+  const int lo = base + pc * BWD_PIECE;
+  const int hi = min(min(lo + BWD_PIECE, base + half), pr.nc);
+  constexpr int c_log = ilog2c(C);
+
+  f32x4 S[Tl::NB];
+#pragma unroll
+  for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int step = 0; step < hi - lo; ++step) {
+    const int j = REV ? hi - 1 - step : lo + step;
+    const int64_t t0 = (int64_t)j * C;
+    const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+    chunk_decays<T, C>(la, cum, ecum, wst, tid);
+    if (REV) {
+      rows_load<T, C, N, NT>(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N,
+                             (int64_t)G * N, ksh, tid);
+      rows_load<T, C, P, NT>(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P,
+                             (int64_t)H * P, vsh, tid);
+    } else {
+      rows_load<T, C, N, NT>(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N,
+                             (int64_t)G * N, ksh, tid);
+      rows_load<T, C, P, NT>(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P,
+                             (int64_t)H * P, vsh, tid);
+    }
+    __syncthreads();
+    if (tid < C) {
+      if (REV) {
+        const T* lr = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0 + tid) * H + h) * L;
+        wsh[tid] = to_f(lr[c_log + k]) * ecum[tid];
+      } else {
+        wsh[tid] = wst[tid];
+      }
+    }
+    __syncthreads();
+    const float dec = M::ex(cum[C - 1]);
+#pragma unroll
+    for (int nb = 0; nb < Tl::NB; ++nb) S[nb] *= dec;
+    chunk_state_mma<T, C, P, N>(ksh, vsh, wsh, S, wave, g, r);
+    __syncthreads();  // the next chunk restages the tiles
+  }
+  float* dst = (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
+#pragma unroll
+  for (int nb = 0; nb < Tl::NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wave + r] = S[nb][i];
+}
+
+// ------------------------------------------------------------ launch 3
+
+// grid (nstate, batch*nheads), 256 threads.  Combines the pieces of one
+// half: forward, each piece decayed from its end to the end of the half
+// (pieces from last to first); reverse, from the start of the half to the
+// piece's start (pieces in order).  Writes the state in the io type,
+// row-major [N][P].
+template <class T, int P, int N, bool REV>
+__global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
+  constexpr int Q4 = N * P / 4;              // float4 groups of a state
+  constexpr int EPT = (Q4 + 255) / 256;      // per thread
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  int k, pair;
+  bwd_state_of(blockIdx.x, pr.nc, pr.kc, k, pair);
+  const int half = 1 << (k - 1);
+  const int base = pair * 2 * half + (REV ? half : 0);
+  const int np = bwd_pieces(k);
+  const int pbase = bwd_piece_base(pr.nc, k) + pair * np;
+  const float* at = pr.atot + (int64_t)bh * pr.nc;
+  const float* part = (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + pbase) * (N * P);
+  f32x4 acc[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float run = 0.f;  // log-decay between the piece and the reference point
+  for (int s = 0; s < np; ++s) {
+    const int pcs = REV ? s : np - 1 - s;
+    const int clo = base + pcs * BWD_PIECE;
+    const int chi = min(min(clo + BWD_PIECE, base + half), pr.nc);
+    const float w = Mfma<T>::ex(run);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q)
+      if (q * 256 + tid < Q4)
+        acc[q] += w * *reinterpret_cast<const f32x4*>(part + (int64_t)pcs * (N * P) + (q * 256 + tid) * 4);
+    float pt = 0.f;  // the piece's total log-decay (uniform)
+    for (int m = clo; m < chi; ++m) pt += at[m];
+    run += pt;
+  }
+  T* dst = static_cast<T*>(REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + blockIdx.x) * (N * P);
+#pragma unroll
+  for (int q = 0; q < EPT; ++q)
+    if (q * 256 + tid < Q4) store4(dst + (q * 256 + tid) * 4, acc[q]);
+}
+
+// ------------------------------------------------------------ launches 4, 5
+
+// LDS bytes of the two chunk passes (the host only instantiates shapes that
+// fit the 160 KB of a CU).
+template <class T, int C, int P, int N>
+constexpr int bwd_dq_lds() {
+  return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + N * P) +
+         4 * (C * (C + 1) + C * 8 + C * BWD_LMAX + 4 * 64);
+}
+template <class T, int C, int P, int N>
+constexpr int bwd_dkv_lds() {
+  return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + N * P) + 4 * (C * 8 + 3 * 64);
+}
+
+// S = C B^T and D = dO X^T for the query rows [16 wave, +16) of the chunk
+// (score tiles above the diagonal block are skipped), then the mask
+// M[t, s] = exp(cum_t - cum_s) lambda[t, level(t, s)] for s <= t:
+// wm = M ⊙ S (if WANT_WS), wd = M ⊙ D in the io type, and optionally
+// E ⊙ S ⊙ D or G = M ⊙ S ⊙ D in fp32.
+template <class T, int C, int P, int N, bool WANT_WS, bool WANT_ESD, bool WANT_G>
+__device__ inline void bwd_intra_scores(const T* csh, const T* bsh, const T* xsh, const T* osh,
+                                        const float* cum, const float (*lam_s)[8], T* wm, T* wd,
+                                        float (*esd)[C + 1], int wave, int g, int r) {
+  using M = Mfma<T>;
+  using LN = Rows<T, N>;
+  using LP = Rows<T, P>;
+  using LC = Rows<T, C>;
+  constexpr int KB = M::KB, TB = C / 16;
+  const int tw = 16 * wave;
+#pragma unroll
+  for (int sb = 0; sb < TB; ++sb) {
+    f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
+    if (sb <= wave) {
+#pragma unroll
+      for (int kk = 0; kk < N / KB; ++kk)
+        s4 = M::mma(frag_along<T, LN>(csh, tw + r, kk * KB, g),
+                    frag_along<T, LN>(bsh, 16 * sb + r, kk * KB, g), s4);
+#pragma unroll
+      for (int kk = 0; kk < P / KB; ++kk)
+        d4 = M::mma(frag_along<T, LP>(osh, tw + r, kk * KB, g),
+                    frag_along<T, LP>(xsh, 16 * sb + r, kk * KB, g), d4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tw + 4 * g + i, s = 16 * sb + r;
+      float e = 0.f, m = 0.f;
+      if (s <= t) {
+        e = M::ex(cum[t] - cum[s]);
+        m = e * lam_s[t][bit_length((unsigned)(t ^ s))];
+      }
+      if constexpr (WANT_WS) wm[LC::at(t, s)] = from_f<T>(m * s4[i]);
+      wd[LC::at(t, s)] = from_f<T>(m * d4[i]);
+      if constexpr (WANT_ESD) esd[t][s] = e * s4[i] * d4[i];
+      if constexpr (WANT_G) esd[t][s] = m * s4[i] * d4[i];
+    }
+  }
+}
+
+// grid (nc, batch*nheads), C/16 waves; wave w owns query rows [16 w, +16).
+// dC_t = sum_s (M ⊙ D)[t, s] B_s within the chunk plus, for each chunk level
+// k whose bit is set in j, lambda[t, c+k] exp(decay) (Z_k dO_t) with Z_k the
+// lower half's state; dlambda[t, l] = sum over the level-l bucket of E S D
+// inside the chunk, and exp(decay) C_t . (Z_k dO_t) at level c + k.
+template <class T, int C, int P, int N>
+__global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
+  using M = Mfma<T>;
+  using LN = Rows<T, N>;
+  using LP = Rows<T, P>;
+  using LC = Rows<T, C>;
+  constexpr int NT = C / 16 * 64, KB = M::KB, NB = N / 16;
+  constexpr int c_log = ilog2c(C);
+  __shared__ __attribute__((aligned(16))) T csh[C * N];
+  __shared__ __attribute__((aligned(16))) T bsh[C * N];
+  __shared__ __attribute__((aligned(16))) T xsh[C * P];
+  __shared__ __attribute__((aligned(16))) T osh[C * P];
+  __shared__ __attribute__((aligned(16))) T wsh[C * C];
+  __shared__ __attribute__((aligned(16))) T zsh[N * P];
+  __shared__ float esd[C][C + 1];
+  __shared__ float lam_s[C][8];
+  __shared__ float dlam_s[C][BWD_LMAX];
+  __shared__ float cum[64], ecum[64], wst[64], term_s[64];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
+  const int b = bh / H, h = bh % H, grp = h / (H / G);
+  const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
+  const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
+  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N,
+                         (int64_t)G * N, csh, tid);
+  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N,
+                         (int64_t)G * N, bsh, tid);
+  rows_load<T, C, P, NT>(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P,
+                         (int64_t)H * P, xsh, tid);
+  rows_load<T, C, P, NT>(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P,
+                         (int64_t)H * P, osh, tid);
+  for (int i = tid; i < C * (c_log + 1); i += NT) {
+    const int t = i / (c_log + 1), l = i % (c_log + 1);
+    lam_s[t][l] = to_f(lg[(int64_t)t * H * L + l]);
+  }
+  for (int i = tid; i < C * pr.ll; i += NT) dlam_s[i / pr.ll][i % pr.ll] = 0.f;
+  const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+  chunk_decays<T, C>(la, cum, ecum, wst, tid);
+  __syncthreads();
+
+  bwd_intra_scores<T, C, P, N, false, true, false>(csh, bsh, xsh, osh, cum, lam_s, nullptr,
+                                                   wsh, esd, wave, g, r);
+  __syncthreads();
+
+  // intra-chunk levels: the level-l bucket of t (l >= 1) is the 2^(l-1) keys
+  // below t's aligned 2^l block boundary, present when bit l-1 of t is set
+  if (tid < C) {
+    const int t = tid;
+    float v0 = esd[t][t];
+    dlam_s[t][0] = v0;
+    float tsum = lam_s[t][0] * v0;
+    for (int l = 1; l <= c_log; ++l) {
+      float v = 0.f;
+      if ((t >> (l - 1)) & 1) {
+        const int lo = t & ~((1 << l) - 1);
+        for (int s = lo; s < lo + (1 << (l - 1)); ++s) v += esd[t][s];
+      }
+      dlam_s[t][l] = v;
+      tsum += lam_s[t][l] * v;
+    }
+    term_s[t] = tsum;
+  }
+
+  const int tw = 16 * wave;
+  f32x4 dc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < C / KB; ++kt) {  // keys s; entries with s > t are zero
+    const auto a = frag_along<T, LC>(wsh, tw + r, kt * KB, g);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      dc[nb] = M::mma(a, frag_down<T, LN>(bsh, kt * KB, 16 * nb, g, r), dc[nb]);
+  }
+  __syncthreads();  // term_s and dlam_s of the intra levels are written
+
+  const float* at = pr.atot + (int64_t)bh * pr.nc;
+  for (int k = 1; k <= pr.kc; ++k) {
+    if (!((j >> (k - 1)) & 1)) continue;  // uniform
+    const int h0 = (j >> (k - 1)) << (k - 1);  // first chunk of j's upper half
+    const float gap = range_sum(at, h0, j, lane);
+    const T* zg = static_cast<const T*>(pr.zst) +
+                  ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, j >> k)) * (N * P);
+    rows_load<T, N, P, NT>(zg, P, zsh, tid);
+    __syncthreads();
+    f32x4 u[NB];  // u[t][n] = sum_p dO[t][p] Z[n][p]
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) u[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kp = 0; kp < P / KB; ++kp) {
+      const auto a = frag_along<T, LP>(osh, tw + r, kp * KB, g);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        u[nb] = M::mma(a, frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g), u[nb]);
+    }
+    const int lv = c_log + k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tw + 4 * g + i;
+      const float wt = M::ex(cum[t] + gap);
+      float part = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) part += u[nb][i] * to_f(csh[LN::at(t, 16 * nb + r)]);
+      const float dl = wt * sum16(part);
+      const float lk = to_f(lg[(int64_t)t * H * L + lv]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dc[nb][i] += (lk * wt) * u[nb][i];
+      if (r == 0) {
+        dlam_s[t][lv] = dl;
+        term_s[t] += lk * dl;
+      }
+    }
+    __syncthreads();  // zsh is restaged by the next level
+  }
+
+  float* dcg = pr.dch + (((int64_t)b * T_ + t0) * H + h) * N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * nb + r] = dc[nb][i];
+  __syncthreads();
+  T* dlg = static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L;
+  for (int i = tid; i < C * L; i += NT) {
+    const int t = i / L, l = i % L;
+    dlg[(int64_t)t * H * L + l] = from_f<T>(l < pr.ll ? dlam_s[t][l] : 0.f);
+  }
+  if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid];
+}
+
+// grid (nc, batch*nheads), C/16 waves.  The mask epilogue runs per query row
+// block as in bwd_dq_kernel; then wave w owns key rows [16 w, +16):
+// dX_s = sum_t (M ⊙ S)[t, s] dO_t and dB_s = sum_t (M ⊙ D)[t, s] C_t within the
+// chunk, plus, for each chunk level k whose bit is clear in i and whose upper
+// half exists, exp(decay s -> end of the lower half) (R_k^T B_s, R_k X_s)
+// with R_k the upper half's state (lambda already on its tokens).
+template <class T, int C, int P, int N>
+__global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
+  using M = Mfma<T>;
+  using LN = Rows<T, N>;
+  using LP = Rows<T, P>;
+  using LC = Rows<T, C>;
+  constexpr int NT = C / 16 * 64, KB = M::KB, NB = N / 16, PB = P / 16;
+  constexpr int c_log = ilog2c(C);
+  __shared__ __attribute__((aligned(16))) T csh[C * N];
+  __shared__ __attribute__((aligned(16))) T bsh[C * N];
+  __shared__ __attribute__((aligned(16))) T xsh[C * P];
+  __shared__ __attribute__((aligned(16))) T osh[C * P];
+  __shared__ __attribute__((aligned(16))) T wsh[C * C];
+  __shared__ __attribute__((aligned(16))) T vsh[C * C];
+  __shared__ __attribute__((aligned(16))) T rsh[N * P];
+  __shared__ float gsh[C][C + 1];
+  __shared__ float lam_s[C][8];
+  __shared__ float cum[64], ecum[64], wst[64], colsum[64];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i_ch = blockIdx.x, bh = blockIdx.y;
+  const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
+  const int b = bh / H, h = bh % H, grp = h / (H / G);
+  const int64_t T_ = pr.seqlen, t0 = (int64_t)i_ch * C;
+  const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
+  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N,
+                         (int64_t)G * N, csh, tid);
+  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N,
+                         (int64_t)G * N, bsh, tid);
+  rows_load<T, C, P, NT>(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P,
+                         (int64_t)H * P, xsh, tid);
+  rows_load<T, C, P, NT>(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P,
+                         (int64_t)H * P, osh, tid);
+  for (int i = tid; i < C * (c_log + 1); i += NT) {
+    const int t = i / (c_log + 1), l = i % (c_log + 1);
+    lam_s[t][l] = to_f(lg[(int64_t)t * H * L + l]);
+  }
+  const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+  chunk_decays<T, C>(la, cum, ecum, wst, tid);
+  __syncthreads();
+
+  bwd_intra_scores<T, C, P, N, true, false, true>(csh, bsh, xsh, osh, cum, lam_s, wsh, vsh,
+                                                  gsh, wave, g, r);
+  __syncthreads();
+  // X_s . dX_s within the chunk is the column sum of G: taken in fp32 from
+  // the same entries whose row sums form dO_t . O_t, so that the two terms of
+  // dlog_a agree where they overlap (the rounding of M ⊙ S to the io type for
+  // the dX product would otherwise enter one term and not the other).
+  if (tid < C) {
+    float cs = 0.f;
+    for (int t = tid; t < C; ++t) cs += gsh[t][tid];
+    colsum[tid] = cs;
+  }
+  __syncthreads();  // colsum is read by every wave at the end
+
+  const int sw = 16 * wave;
+  f32x4 dx[PB], dxe[PB], db[NB];  // dX: intra-chunk part, chunk-level part
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) dx[pb] = dxe[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) db[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < C / KB; ++kt) {  // queries t; entries with t < s are zero
+    const auto aw = frag_down<T, LC>(wsh, kt * KB, sw, g, r);
+    const auto av = frag_down<T, LC>(vsh, kt * KB, sw, g, r);
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+      dx[pb] = M::mma(aw, frag_down<T, LP>(osh, kt * KB, 16 * pb, g, r), dx[pb]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      db[nb] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * nb, g, r), db[nb]);
+  }
+
+  const float* at = pr.atot + (int64_t)bh * pr.nc;
+  for (int k = 1; k <= pr.kc; ++k) {
+    if ((i_ch >> (k - 1)) & 1) continue;  // uniform: i is in an upper half
+    const int h0 = ((i_ch >> (k - 1)) + 1) << (k - 1);  // first chunk of the upper half
+    if (h0 >= pr.nc) continue;
+    const float gap = range_sum(at, i_ch + 1, h0, lane);
+    const T* rg = static_cast<const T*>(pr.rst) +
+                  ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, i_ch >> k)) * (N * P);
+    rows_load<T, N, P, NT>(rg, P, rsh, tid);
+    __syncthreads();
+    f32x4 tx[PB], tb[NB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) tx[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) tb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kn = 0; kn < N / KB; ++kn) {  // tx[s][p] = sum_n B[s][n] R[n][p]
+      const auto a = frag_along<T, LN>(bsh, sw + r, kn * KB, g);
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb)
+        tx[pb] = M::mma(a, frag_down<T, LP>(rsh, kn * KB, 16 * pb, g, r), tx[pb]);
+    }
+#pragma unroll
+    for (int kp = 0; kp < P / KB; ++kp) {  // tb[s][n] = sum_p X[s][p] R[n][p]
+      const auto a = frag_along<T, LP>(xsh, sw + r, kp * KB, g);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        tb[nb] = M::mma(a, frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g), tb[nb]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = sw + 4 * g + i;
+      const float w = M::ex(cum[C - 1] - cum[s] + gap);
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) dxe[pb][i] += w * tx[pb][i];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) db[nb][i] += w * tb[nb][i];
+    }
+    __syncthreads();  // rsh is restaged by the next level
+  }
+
+  T* dxg = static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P;
+  float* dbg = pr.dbh + (((int64_t)b * T_ + t0) * H + h) * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = sw + 4 * g + i;
+    float part = 0.f;  // X_s . (chunk-level part of dX_s)
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      part += dxe[pb][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
+      dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[pb][i] + dxe[pb][i]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dbg[(int64_t)s * H * N + 16 * nb + r] = db[nb][i];
+    part = sum16(part);
+    if (r == 0) pr.term2[(int64_t)bh * T_ + t0 + s] = colsum[s] + part;
+  }
+}
+
+// ------------------------------------------------------------ launch 6
+
+// dB and dC: the heads of each group summed in head order; 4 elements per thread.
+template <class T, int N>
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams pr) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int H = pr.nheads, G = pr.ngroups, hpg = H / G;
+  const int64_t total = (int64_t)pr.batch * pr.seqlen * G * (N / 4);
+  if (q >= total) return;
+  const int n = (int)(q % (N / 4)) * 4;
+  const int64_t rest = q / (N / 4);
+  const int grp = (int)(rest % G);
+  const int64_t bt = rest / G;
+  f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < hpg; ++k) {
+    const int64_t idx = (bt * H + grp * hpg + k) * N + n;
+    sb += *reinterpret_cast<const f32x4*>(pr.dbh + idx);
+    sc += *reinterpret_cast<const f32x4*>(pr.dch + idx);
+  }
+  store4(static_cast<T*>(pr.dB) + (bt * G + grp) * N + n, sb);
+  store4(static_cast<T*>(pr.dC) + (bt * G + grp) * N + n, sc);
+}
+
+// ------------------------------------------------------------ launch 7
+
+// grid (batch*nheads), 1024 threads: dlog_a[t] = sum_{t' >= t} (term1 - term2),
+// each thread a contiguous run of tokens, runs combined by a suffix scan.
+constexpr int BWD_SCAN_NT = 1024;
+template <class T>  // (a template so that every unit's copy is a weak symbol)
+__global__ __launch_bounds__(BWD_SCAN_NT) void bwd_dloga_kernel(BwdParams pr) {
+  __shared__ float sh[BWD_SCAN_NT];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int H = pr.nheads, b = bh / H, h = bh % H;
+  const int64_t T_ = pr.seqlen;
+  const int64_t per = (T_ + BWD_SCAN_NT - 1) / BWD_SCAN_NT;
+  const int64_t lo = min((int64_t)tid * per, T_), hi = min(lo + per, T_);
+  const float* t1 = pr.term1 + (int64_t)bh * T_;
+  const float* t2 = pr.term2 + (int64_t)bh * T_;
+  float tot = 0.f;
+  for (int64_t t = hi - 1; t >= lo; --t) tot += t1[t] - t2[t];
+  sh[tid] = tot;
+  __syncthreads();
+  for (int d = 1; d < BWD_SCAN_NT; d <<= 1) {  // inclusive suffix sums over threads
+    const float v = tid + d < BWD_SCAN_NT ? sh[tid + d] : 0.f;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  float run = tid + 1 < BWD_SCAN_NT ? sh[tid + 1] : 0.f;
+  for (int64_t t = hi - 1; t >= lo; --t) {
+    run += t1[t] - t2[t];
+    pr.dloga[((int64_t)b * T_ + t) * H + h] = run;
+  }
+}
+
+// ------------------------------------------------------------ launch sequence
+
+using BwdFn = int (*)(const BwdParams&, hipStream_t);
+
+template <class T, int C, int P, int N>
+int launch_backward(const BwdParams& pr, hipStream_t st) {
+  using Tl = Tiles<T, C, P, N>;
+  const int bh = pr.batch * pr.nheads;
+  hipLaunchKernelGGL((bwd_atot_kernel<T, C>), dim3(pr.nc, bh), dim3(64), 0, st, pr);
+  if (pr.npart > 0) {
+    hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, false>), dim3(pr.npart, bh),
+                       dim3(Tl::NT), 0, st, pr);
+    hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh),
+                       dim3(Tl::NT), 0, st, pr);
+    hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, false>), dim3(pr.nstate, bh), dim3(256),
+                       0, st, pr);
+    hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>), dim3(pr.nstate, bh), dim3(256),
+                       0, st, pr);
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(pr.nc, bh), dim3(C / 16 * 64), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(pr.nc, bh), dim3(C / 16 * 64), 0, st, pr);
+  const int64_t groups4 = (int64_t)pr.batch * pr.seqlen * pr.ngroups * (N / 4);
+  hipLaunchKernelGGL((bwd_group_sum_kernel<T, N>), dim3((unsigned)((groups4 + 255) / 256)),
+                     dim3(256), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dloga_kernel<T>), dim3(bh), dim3(BWD_SCAN_NT), 0, st, pr);
+  return (int)hipGetLastError();
+}
+
+// Shapes with a backward instantiation: bf16 needs P >= 32 and chunk >= 32
+// (one MFMA step of 32 along the token and head dimensions); both chunk
+// passes must fit in a CU's 160 KB of LDS.
+template <class T, int C, int P, int N>
+constexpr bool bwd_supported() {
+  constexpr int KB = Mfma<T>::KB;
+  return P >= KB && C >= KB && N >= KB &&
+         bwd_dq_lds<T, C, P, N>() <= 160 * 1024 && bwd_dkv_lds<T, C, P, N>() <= 160 * 1024;
+}
+
+template <class T, int C>
+BwdFn lookup_bwd(int P, int N) {
+#define LOGLIN_BCASE(PP, NN)                                            \
+  if constexpr (bwd_supported<T, C, PP, NN>())                          \
+    if (P == PP && N == NN) return &launch_backward<T, C, PP, NN>;
+  LOGLIN_BCASE(16, 16) LOGLIN_BCASE(16, 32) LOGLIN_BCASE(16, 64) LOGLIN_BCASE(16, 128)
+  LOGLIN_BCASE(32, 16) LOGLIN_BCASE(32, 32) LOGLIN_BCASE(32, 64) LOGLIN_BCASE(32, 128)
+  LOGLIN_BCASE(64, 16) LOGLIN_BCASE(64, 32) LOGLIN_BCASE(64, 64) LOGLIN_BCASE(64, 128)
+#undef LOGLIN_BCASE
+  return nullptr;
+}
+
+// Defined in one translation unit per (io type, chunk).
+BwdFn lookup_bwd_bf16_32(int P, int N);
+BwdFn lookup_bwd_bf16_64(int P, int N);
+BwdFn lookup_bwd_f32_16(int P, int N);
+BwdFn lookup_bwd_f32_32(int P, int N);
+BwdFn lookup_bwd_f32_64(int P, int N);
+
+}  // namespace loglin

@@ -7,6 +7,7 @@
 
 #include <cstdint>
 
+#include "loglin_bwd.hpp"
 #include "loglin_decode.hpp"
 #include "loglin_launch.hpp"
 
@@ -132,6 +133,70 @@ loglin::LaunchFn pick(int dtype, int chunk, int P, int N) {
     if (chunk == 64) return lookup_f32_64(P, N);
   }
   return nullptr;
+}
+
+loglin::BwdFn pick_bwd(int dtype, int chunk, int P, int N) {
+  using namespace loglin;
+  if (dtype == LOGLIN_BF16) {  // chunk 16 is below one bf16 MFMA step
+    if (chunk == 32) return lookup_bwd_bf16_32(P, N);
+    if (chunk == 64) return lookup_bwd_bf16_64(P, N);
+  } else {
+    if (chunk == 16) return lookup_bwd_f32_16(P, N);
+    if (chunk == 32) return lookup_bwd_f32_32(P, N);
+    if (chunk == 64) return lookup_bwd_f32_64(P, N);
+  }
+  return nullptr;
+}
+
+// Backward workspace: chunk log-decays, the two directions' piece partials
+// (fp32) and level states (io type), the per-head dC and dB shares and the
+// two per-token terms of dlog_a; each region 256-byte aligned.
+struct BwdPlan {
+  int nc, kc, ll, npart, nstate;
+  size_t off_atot, off_pf, off_pr, off_z, off_r, off_dch, off_dbh, off_t1, off_t2, bytes;
+};
+
+int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
+  Plan fp;
+  int rc = check_dims(d, chunk, nullptr, &fp);
+  if (rc) return rc;
+  if (fp.ll > loglin::BWD_LMAX) return LOGLIN_ERR_DIM;
+  if (!pick_bwd(d->io_dtype, chunk, (int)d->headdim, (int)d->dstate)) return LOGLIN_ERR_SHAPE;
+  pl->nc = fp.nc;
+  pl->kc = fp.kc;
+  pl->ll = fp.ll;
+  int64_t npart = 0, nstate = 0;
+  for (int k = 1; k <= fp.kc; ++k) {
+    npart += (int64_t)loglin::bwd_pairs(fp.nc, k) * loglin::bwd_pieces(k);
+    nstate += loglin::bwd_pairs(fp.nc, k);
+  }
+  pl->npart = (int)npart;
+  pl->nstate = (int)nstate;
+  const size_t bh = (size_t)(d->batch * d->nheads);
+  const size_t pn = (size_t)(d->headdim * d->dstate);
+  const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;
+  const size_t tok = (size_t)(d->batch * d->seqlen);
+  size_t off = 0;
+  pl->off_atot = off;
+  off = round_up(off + bh * fp.nc * sizeof(float));
+  pl->off_pf = off;
+  off = round_up(off + bh * npart * pn * sizeof(float));
+  pl->off_pr = off;
+  off = round_up(off + bh * npart * pn * sizeof(float));
+  pl->off_z = off;
+  off = round_up(off + bh * nstate * pn * esz);
+  pl->off_r = off;
+  off = round_up(off + bh * nstate * pn * esz);
+  pl->off_dch = off;
+  off = round_up(off + tok * d->nheads * d->dstate * sizeof(float));
+  pl->off_dbh = off;
+  off = round_up(off + tok * d->nheads * d->dstate * sizeof(float));
+  pl->off_t1 = off;
+  off = round_up(off + bh * d->seqlen * sizeof(float));
+  pl->off_t2 = off;
+  off = round_up(off + bh * d->seqlen * sizeof(float));
+  pl->bytes = off;
+  return LOGLIN_OK;
 }
 
 // Decode state: level states fp32 [B, H, LL, P/4, N, 4], then the two banks of
@@ -277,6 +342,66 @@ int loglin_fwd(const void* X, const void* B, const void* C, const float* log_a,
                void* workspace, size_t workspace_bytes, void* stream) {
   return loglin_fwd_ex(X, B, C, log_a, lambda, chunk, out, dims, workspace, workspace_bytes,
                        stream, nullptr);
+}
+
+size_t loglin_bwd_workspace_bytes(const loglin_dims* dims, int chunk) {
+  BwdPlan pl;
+  return check_bwd_dims(dims, chunk, &pl) ? 0 : pl.bytes;
+}
+
+int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
+               const void* lambda, const void* dO, int chunk, void* dX, void* dB, void* dC,
+               float* dlog_a, void* dlambda, const loglin_dims* dims, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  BwdPlan pl;
+  int rc = check_bwd_dims(dims, chunk, &pl);
+  if (rc) return rc;
+  if (!X || !B || !C || !log_a || !lambda || !dO || !dX || !dB || !dC || !dlog_a || !dlambda ||
+      !workspace)
+    return !workspace && X && B && C && log_a && lambda && dO && dX && dB && dC && dlog_a &&
+                   dlambda
+               ? LOGLIN_ERR_WORKSPACE
+               : LOGLIN_ERR_NULL;
+  if (misaligned(X) || misaligned(B) || misaligned(C) || misaligned(log_a) ||
+      misaligned(lambda) || misaligned(dO) || misaligned(dX) || misaligned(dB) ||
+      misaligned(dC) || misaligned(dlog_a) || misaligned(dlambda))
+    return LOGLIN_ERR_ALIGN;
+  if (workspace_bytes < pl.bytes) return LOGLIN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return LOGLIN_ERR_ALIGN;
+  loglin::BwdFn fn = pick_bwd(dims->io_dtype, chunk, (int)dims->headdim, (int)dims->dstate);
+  char* ws = static_cast<char*>(workspace);
+  loglin::BwdParams pr{};
+  pr.X = X;
+  pr.Bm = B;
+  pr.Cm = C;
+  pr.log_a = log_a;
+  pr.lam = lambda;
+  pr.dO = dO;
+  pr.dX = dX;
+  pr.dB = dB;
+  pr.dC = dC;
+  pr.dloga = dlog_a;
+  pr.dlam = dlambda;
+  pr.atot = reinterpret_cast<float*>(ws + pl.off_atot);
+  pr.part_f = reinterpret_cast<float*>(ws + pl.off_pf);
+  pr.part_r = reinterpret_cast<float*>(ws + pl.off_pr);
+  pr.zst = ws + pl.off_z;
+  pr.rst = ws + pl.off_r;
+  pr.dch = reinterpret_cast<float*>(ws + pl.off_dch);
+  pr.dbh = reinterpret_cast<float*>(ws + pl.off_dbh);
+  pr.term1 = reinterpret_cast<float*>(ws + pl.off_t1);
+  pr.term2 = reinterpret_cast<float*>(ws + pl.off_t2);
+  pr.batch = (int)dims->batch;
+  pr.seqlen = (int)dims->seqlen;
+  pr.nheads = (int)dims->nheads;
+  pr.ngroups = (int)dims->ngroups;
+  pr.nlevels = (int)dims->nlevels;
+  pr.nc = pl.nc;
+  pr.kc = pl.kc;
+  pr.ll = pl.ll;
+  pr.npart = pl.npart;
+  pr.nstate = pl.nstate;
+  return fn(pr, static_cast<hipStream_t>(stream)) ? LOGLIN_ERR_HIP : LOGLIN_OK;
 }
 
 const char* loglin_strerror(int code) {

@@ -1,7 +1,7 @@
 """ctypes binding of libloglin.so (the C ABI in include/loglin.h).
 
-Argument marshalling only: every step of the forward pass runs in the HIP
-kernels of the library.  PyTorch supplies device memory and the stream.
+Argument marshalling only: every step of the forward pass, the backward pass
+and the decode step runs in the HIP kernels of the library.  PyTorch supplies device memory and the stream.
 There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
@@ -55,6 +55,7 @@ EXPORTS = (
     "loglin_fwd_ex", "loglin_validate", "loglin_strerror",
     "loglin_plan_seg_log2", "loglin_event_create", "loglin_event_destroy",
     "loglin_event_elapsed_ms", "loglin_decode_state_bytes", "loglin_decode_step",
+    "loglin_bwd_workspace_bytes", "loglin_bwd",
 )
 
 
@@ -94,6 +95,10 @@ def lib():
     L.loglin_decode_state_bytes.restype = sz
     L.loglin_decode_step.argtypes = [vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, pd, vp]
     L.loglin_decode_step.restype = i32
+    L.loglin_bwd_workspace_bytes.argtypes = [pd, i32]
+    L.loglin_bwd_workspace_bytes.restype = sz
+    L.loglin_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, pd, vp, sz, vp]
+    L.loglin_bwd.restype = i32
     _lib = L
     return L
 
@@ -273,3 +278,47 @@ def loglin_decode_step(state, t, X, B, C, log_a, lam, out, *, seqlen, stream=Non
                                   ctypes.c_void_p(stream.cuda_stream))
     _check(rc)
     return out
+
+
+def loglin_bwd_workspace_bytes(dims: loglin_dims, chunk: int) -> int:
+    return int(lib().loglin_bwd_workspace_bytes(ctypes.byref(dims), int(chunk)))
+
+
+def loglin_bwd(X, B, C, log_a, lam, dO, chunk, dX, dB, dC, dlog_a, dlam, *, workspace=None,
+               stream=None):
+    """Enqueue the gradients of O = (C B^T . M^H) X for the upstream gradient
+    dO [Bt,T,H,P]: dX [Bt,T,H,P], dB and dC [Bt,T,G,N] (summed over each
+    group's heads), dlog_a [Bt,T,H] float32 and dlam [Bt,T,H,L] (zero on levels
+    the sequence does not reach).  Inputs as for loglin_fwd; dO, dX, dB, dC and
+    dlam in the io dtype.  `workspace` is a uint8 device tensor of at least
+    loglin_bwd_workspace_bytes bytes (allocated here when None).  Returns
+    (dX, dB, dC, dlog_a, dlam)."""
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("loglin_bwd needs GPU tensors")
+    dims = dims_of(X, B, lam)
+    io = X.dtype
+    Bt, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    L = lam.shape[3]
+    for name, t, shape, dt in (("X", X, (Bt, T, H, P), io), ("B", B, (Bt, T, G, N), io),
+                               ("C", C, (Bt, T, G, N), io),
+                               ("log_a", log_a, (Bt, T, H), torch.float32),
+                               ("lam", lam, (Bt, T, H, L), io), ("dO", dO, (Bt, T, H, P), io),
+                               ("dX", dX, (Bt, T, H, P), io), ("dB", dB, (Bt, T, G, N), io),
+                               ("dC", dC, (Bt, T, G, N), io),
+                               ("dlog_a", dlog_a, (Bt, T, H), torch.float32),
+                               ("dlam", dlam, (Bt, T, H, L), io)):
+        _check_tensor(name, t, shape, dt, dev)
+    need = loglin_bwd_workspace_bytes(dims, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib().loglin_bwd(_ptr(X), _ptr(B), _ptr(C), _ptr(log_a), _ptr(lam), _ptr(dO), int(chunk),
+                          _ptr(dX), _ptr(dB), _ptr(dC), _ptr(dlog_a), _ptr(dlam),
+                          ctypes.byref(dims), _ptr(workspace), ws_bytes,
+                          ctypes.c_void_p(stream.cuda_stream))
+    _check(rc)
+    return dX, dB, dC, dlog_a, dlam
