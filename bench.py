@@ -17,7 +17,9 @@ same workload on this host's cores.
 32K-token context (the state is first built by decode steps from t = 0)
 and prints its own JSON line.  --mode naive times the unfused variant: one
 whole pass per level (only that level's terms computed), summed in fp32,
-against the fused pass on the same inputs.
+against the fused pass on the same inputs.  --mode backward times the
+backward pass (dX, dB, dC, dlog_a, dlambda for a seeded upstream gradient)
+on the same workload, and the forward + backward pair.
 """
 from __future__ import annotations
 
@@ -89,6 +91,39 @@ def algorithmic(cfg) -> dict:
             "bytes_per_token_group": 2 * N * e,
         },
     }
+
+
+def algorithmic_bwd(cfg) -> dict:
+    """Algorithmic bytes and MFMA flops of one backward pass.
+
+    Bytes: X, B, C, log_a, lambda and dO read once; dX, dB, dC, dlog_a and
+    dlambda written once.  Flops (causal counting inside a chunk): the score
+    matrices C B^T and dO X^T, and the three products with them (dC, dX,
+    dB); one chunk state per (head, chunk) in the forward direction (B, X);
+    in the reverse direction one chunk state per (head, chunk, level at which
+    the chunk lies in an upper half), since those carry that level's lambda;
+    and per (head, chunk, level) pairing: one C x P x N product for dC and
+    dlambda (upper-half chunk), two for dX and dB (lower-half chunk)."""
+    Bt, T, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
+    P, N, L, C = cfg.headdim, cfg.dstate, cfg.nlevels, cfg.chunk
+    e = 2 if cfg.dtype == "bf16" else 4
+    nc = T // C
+    tri = C * (C + 1) // 2
+    x = Bt * T * H * P * e
+    bc = Bt * T * G * N * e
+    lam = Bt * T * H * L * e
+    la = Bt * T * H * 4
+    reads = 2 * x + 2 * bc + lam + la
+    writes = x + 2 * bc + lam + la
+    kc = (nc - 1).bit_length()
+    upper = sum(1 for j in range(nc) for k in range(1, kc + 1) if (j >> (k - 1)) & 1)
+    lower = sum(1 for i in range(nc) for k in range(1, kc + 1)
+                if not (i >> (k - 1)) & 1 and (((i >> (k - 1)) + 1) << (k - 1)) < nc)
+    fl_intra = Bt * H * nc * 2 * tri * (3 * N + 2 * P)
+    fl_states = Bt * H * 2 * N * P * C * (nc + upper)
+    fl_levels = Bt * H * 2 * C * N * P * (upper + 2 * lower)
+    return {"bytes_total": reads + writes, "reads": reads, "writes": writes,
+            "flops_total": fl_intra + fl_states + fl_levels}
 
 
 # ------------------------------------------------------------ CPU oracle
@@ -185,7 +220,8 @@ def main():
     ap.add_argument("--seg-log2", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of wall time for the CPU oracle sample (0: skip)")
-    ap.add_argument("--mode", choices=("forward", "decode", "naive"), default="forward")
+    ap.add_argument("--mode", choices=("forward", "decode", "naive", "backward"),
+                    default="forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of this many MiB "
                          "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -233,6 +269,8 @@ def main():
 
     if args.mode == "naive":
         return main_naive(args, cfg, t, out, ws, stream, step)
+    if args.mode == "backward":
+        return main_backward(args, cfg, t, out, ws, stream, step)
 
     if args.calibrate_copy > 0:
         nb = args.calibrate_copy << 20
@@ -385,6 +423,82 @@ def main_naive(args, cfg, t, out, ws, stream, fused_step):
                    "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
                    "ngroups": cfg.ngroups, "headdim": cfg.headdim, "dstate": cfg.dstate,
                    "chunk": cfg.chunk, "nlevels": cfg.nlevels},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def main_backward(args, cfg, t, out, ws, stream, fwd_step):
+    import torch
+
+    from ssm_scan_amd import loglin as L
+
+    dev = t["X"].device
+    vals, bits = inputs.make_grad_output(cfg, seed=0)
+    if bits is not None:
+        dO = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        dO = torch.from_numpy(vals).to(dev)
+    del vals, bits
+    g = dict(dX=torch.empty_like(t["X"]), dB=torch.empty_like(t["B"]),
+             dC=torch.empty_like(t["C"]), dlog_a=torch.empty_like(t["log_a"]),
+             dlam=torch.empty_like(t["lam"]))
+    dims = L.dims_of(t["X"], t["B"], t["lam"])
+    bws = torch.empty(L.loglin_bwd_workspace_bytes(dims, cfg.chunk), dtype=torch.uint8, device=dev)
+
+    def bwd_step():
+        L.loglin_bwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], dO, cfg.chunk, g["dX"],
+                     g["dB"], g["dC"], g["dlog_a"], g["dlam"], workspace=bws, stream=stream)
+
+    def timed(fn, K):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return max(time.perf_counter() - w0, e0.elapsed_time(e1) / 1e3) / K
+
+    print("[bench] backward warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        bwd_step()
+    torch.cuda.synchronize()
+    K = args.steps
+    print("[bench] timed backward steps", file=sys.stderr, flush=True)
+    bwd_s = timed(bwd_step, K)
+    fwd_s = timed(fwd_step, K)
+    pair_s = timed(lambda: (fwd_step(), bwd_step()), K)
+    alg = algorithmic_bwd(cfg)
+    gbs = alg["bytes_total"] / bwd_s / 1e9
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    tfl = alg["flops_total"] / bwd_s / 1e12
+    tokens = cfg.batch * cfg.seqlen
+    res = {
+        "metric": "log-linear Mamba-2 bwd tokens/s at T=32K, H=48",
+        "value": round(tokens / bwd_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(bwd_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"log-linear Mamba-2 backward, {cfg.name}", "batch": cfg.batch,
+                   "seqlen": cfg.seqlen, "nheads": cfg.nheads, "ngroups": cfg.ngroups,
+                   "headdim": cfg.headdim, "dstate": cfg.dstate, "chunk": cfg.chunk,
+                   "nlevels": cfg.nlevels},
+        "path_hbm": {"bound": "hbm", "alg_bytes_per_step": alg["bytes_total"],
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "path_mfma": {"alg_flops_per_step": alg["flops_total"], "achieved": round(tfl, 2),
+                      "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(tfl / mfma_peak, 4)},
+        "forward_ms": round(fwd_s * 1e3, 4),
+        "fwd_plus_bwd_ms": round(pair_s * 1e3, 4),
+        "fwd_plus_bwd_tokens_per_s": round(tokens / pair_s, 1),
     }
     print(json.dumps(res), flush=True)
 

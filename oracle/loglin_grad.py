@@ -30,9 +30,10 @@ algorithm and its benchmarks) but prints no formula for it, so the
 gradients here are the plain calculus of the forward definition.
 
 Pins (tests/test_oracle_grad.py): central finite differences of the pinned
-forward oracle for every input; dlog_a at r = 0 is exactly zero; with
-lambda one-hot on level l, dlambda's other levels vanish and its level l
-equals the bucket-masked brute force; gradients are linear in dO.
+forward oracle for every input; dlambda[t, l] equals dO_t . O_t of the
+forward with lambda one-hot on level l; dlog_a at r = 0 is exactly zero;
+gradients are linear in dO; planted mistakes are caught.  The O(T) sampled
+helpers at the end are checked entry by entry against loglin_grad.
 """
 from __future__ import annotations
 
@@ -121,3 +122,70 @@ def loglin_grad(X, B, C, log_a, lam, dO, *, row_block: int = 256):
             out["dlam"][b, :, h] = r["dlam"]
             out["dlog_a"][b, :, h] = r["dlog_a"]
     return out
+
+
+# --------------------------------------------------- sampled entries, O(T) each
+#
+# For sequences too long to form every row, single gradient entries follow
+# from one row or one column of the T x T matrices.  Same definitions as
+# above; tests pin these against loglin_grad on small sizes.
+
+def _bh_arrays(X, B, C, log_a, lam, dO, b, h):
+    Bt, T, H, G, P, N = _check(X, B, C, log_a, lam)
+    g = _group_of(h, H, G)
+    return (np.cumsum(np.asarray(log_a[b, :, h], dtype=F64)),
+            np.asarray(X[b, :, h, :], dtype=F64), np.asarray(B[b, :, g, :], dtype=F64),
+            np.asarray(C[b, :, g, :], dtype=F64), np.asarray(dO[b, :, h, :], dtype=F64),
+            np.asarray(lam[b, :, h, :], dtype=F64))
+
+
+def grad_key_columns(X, B, C, log_a, lam, dO, b, h, cols):
+    """dX[s] and this head's share of dB[s] for the key positions `cols`:
+    column s of S ⊙ M and of D ⊙ M over the queries t >= s."""
+    cum, Xh, Bg, Cg, dOh, lamh = _bh_arrays(X, B, C, log_a, lam, dO, b, h)
+    T = cum.shape[0]
+    dX = np.zeros((len(cols), Xh.shape[1]), F64)
+    dB = np.zeros((len(cols), Bg.shape[1]), F64)
+    for i, s in enumerate(np.asarray(cols, dtype=np.int64)):
+        t = np.arange(s, T, dtype=np.int64)
+        lev = fenwick.levels(t, np.full_like(t, s))
+        m = np.exp(cum[t] - cum[s]) * lamh[t, lev]  # M[t, s]
+        S = Cg[t] @ Bg[s]
+        D = dOh[t] @ Xh[s]
+        dX[i] = (m * S) @ dOh[t]
+        dB[i] = (m * D) @ Cg[t]
+    return dX, dB
+
+
+def grad_query_rows(X, B, C, log_a, lam, dO, b, h, rows):
+    """This head's share of dC[t] and dlambda[t, :] for the query positions
+    `rows`: row t of D ⊙ M and of E ⊙ S ⊙ D over the keys s <= t."""
+    cum, Xh, Bg, Cg, dOh, lamh = _bh_arrays(X, B, C, log_a, lam, dO, b, h)
+    L = lamh.shape[1]
+    dC = np.zeros((len(rows), Bg.shape[1]), F64)
+    dlam = np.zeros((len(rows), L), F64)
+    for i, t in enumerate(np.asarray(rows, dtype=np.int64)):
+        s = np.arange(0, t + 1, dtype=np.int64)
+        lev = fenwick.levels(np.full_like(s, t), s)
+        e = np.exp(cum[t] - cum[s])
+        S = Bg[s] @ Cg[t]
+        D = Xh[s] @ dOh[t]
+        dC[i] = (e * lamh[t, lev] * D) @ Bg[s]
+        dlam[i] = np.bincount(lev, weights=e * S * D, minlength=L)[:L]
+    return dC, dlam
+
+
+def grad_log_a_at(X, B, C, log_a, lam, dO, b, h, r):
+    """dlog_a[r] = sum over t >= r, s < r of (M ⊙ S ⊙ D)[t, s]; costs
+    (T - r) * r entries, so it is meant for r near either end."""
+    cum, Xh, Bg, Cg, dOh, lamh = _bh_arrays(X, B, C, log_a, lam, dO, b, h)
+    T = cum.shape[0]
+    if r == 0:
+        return 0.0
+    t = np.arange(r, T, dtype=np.int64)[:, None]
+    s = np.arange(0, r, dtype=np.int64)[None, :]
+    lev = fenwick.levels(t, s)
+    m = np.exp(cum[t] - cum[s]) * np.take_along_axis(lamh[t[:, 0]], lev, axis=1)
+    S = Cg[t[:, 0]] @ Bg[:r].T
+    D = dOh[t[:, 0]] @ Xh[:r].T
+    return float(np.sum(m * S * D))

@@ -25,7 +25,7 @@
 //   2. bwd_level_state_kernel   per (level, pair, piece of <= 8 chunks): the
 //                               decayed sum over the piece's chunks of the
 //                               lower half (forward) or upper half (reverse);
-//   3. bwd_level_reduce_kernel  pieces -> one state per (level, pair), io type;
+//   3. bwd_level_reduce_kernel  pieces -> one state per (level, pair), fp32;
 //   4. bwd_dq_kernel            per chunk: dC (this head) and dlambda, from the
 //                               intra block and the lower-half states;
 //   5. bwd_dkv_kernel           per chunk: dX and dB (this head), from the
@@ -53,8 +53,8 @@ struct BwdParams {
   float* atot;    // [batch*nheads, nc]
   float* part_f;  // [batch*nheads, npart, N, P] fp32, lower-half pieces
   float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
-  void* zst;      // [batch*nheads, nstate, N, P] io type, lower-half sums
-  void* rst;      // [batch*nheads, nstate, N, P] io type, upper-half sums
+  float* zst;     // [batch*nheads, nstate, N, P] fp32, lower-half sums
+  float* rst;     // [batch*nheads, nstate, N, P] fp32, upper-half sums
   float* dch;     // [batch, seqlen, nheads, N] this head's share of dC
   float* dbh;     // [batch, seqlen, nheads, N] this head's share of dB
   float* term1;   // [batch*nheads, seqlen] dO_t . O_t
@@ -128,6 +128,81 @@ __device__ inline void rows_load(const T* g, int64_t grs, T* lds, int tid) {
     if (i < PIECES) {
       const int row = i / L::NBLK, pb = i % L::NBLK;
       store16(lds + L::at(row, pb * L::VEC), load16(g + (int64_t)row * grs + pb * L::VEC));
+    }
+  }
+}
+
+// Level states enter the MFMAs as a pair of io-type tiles, hi = rnd(v) and
+// lo = rnd(v - hi), so that a bf16 product with them keeps about 16 bits of
+// the fp32 state.  dlog_a is a suffix sum over the whole sequence of
+// dO_t . O_t - X_t . dX_t, two terms formed through different states (the
+// lower-half state against dO, the upper-half state against B and X); with
+// the states rounded to bf16 their mismatch near every chunk boundary would
+// accumulate along the sequence.  For fp32 io the lo tile is not used.
+template <class T, int R, int W, int NT>
+__device__ inline void rows_load_split(const float* g, T* hi, T* lo, int tid) {
+  using L = Rows<T, W>;
+  constexpr int PIECES = R * L::NBLK;
+#pragma unroll
+  for (int i0 = 0; i0 < PIECES; i0 += NT) {
+    const int i = i0 + tid;
+    if (i < PIECES) {
+      const int row = i / L::NBLK, pb = i % L::NBLK;
+      const float* src = g + (int64_t)row * W + pb * L::VEC;
+      vec16_t<T> vh, vl;
+      if constexpr (sizeof(T) == 2) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vh[q] = (bf16)a[q];
+          vh[q + 4] = (bf16)b[q];
+          vl[q] = (bf16)(a[q] - (float)vh[q]);
+          vl[q + 4] = (bf16)(b[q] - (float)vh[q + 4]);
+        }
+        store16(lo + L::at(row, pb * L::VEC), vl);
+      } else {
+        vh = *reinterpret_cast<const f32x4*>(src);
+      }
+      store16(hi + L::at(row, pb * L::VEC), vh);
+    }
+  }
+}
+
+// One chunk's state S[n][p] += sum_t key[t][n] w[t] val[t][p] for this wave's
+// 16 columns (the forward's chunk_state_mma), with w[t] val[t][p] split into
+// hi and lo bf16 fragments for bf16 io (see rows_load_split).
+template <class T, int C, int P, int N>
+__device__ inline void chunk_state_mma_split(const T* ks, const T* vs, const float* w, f32x4* S,
+                                             int wave, int g, int r) {
+  using Tl = Tiles<T, C, P, N>;
+  using M = Mfma<T>;
+#pragma unroll
+  for (int kt = 0; kt < Tl::NKT; ++kt) {
+    if constexpr (sizeof(T) == 2) {
+      const auto f = frag_down<T, Rows<T, P>>(vs, kt * Tl::KB, 16 * wave, g, r);
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + kt * Tl::KB + 8 * g);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + kt * Tl::KB + 8 * g + 4);
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v0 = (float)f[j] * w0[j], v1 = (float)f[j + 4] * w1[j];
+        hi[j] = (bf16)v0;
+        hi[j + 4] = (bf16)v1;
+        lo[j] = (bf16)(v0 - (float)hi[j]);
+        lo[j + 4] = (bf16)(v1 - (float)hi[j + 4]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < Tl::NB; ++nb) {
+        const auto af = frag_down<T, Rows<T, N>>(ks, kt * Tl::KB, 16 * nb, g, r);
+        S[nb] = M::mma(af, hi, S[nb]);
+        S[nb] = M::mma(af, lo, S[nb]);
+      }
+    } else {
+      const auto bf = frag_down_scaled<T, Rows<T, P>>(vs, w, kt * Tl::KB, 16 * wave, g, r);
+#pragma unroll
+      for (int nb = 0; nb < Tl::NB; ++nb)
+        S[nb] = M::mma(frag_down<T, Rows<T, N>>(ks, kt * Tl::KB, 16 * nb, g, r), bf, S[nb]);
     }
   }
 }
@@ -228,7 +303,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
     const float dec = M::ex(cum[C - 1]);
 #pragma unroll
     for (int nb = 0; nb < Tl::NB; ++nb) S[nb] *= dec;
-    chunk_state_mma<T, C, P, N>(ksh, vsh, wsh, S, wave, g, r);
+    chunk_state_mma_split<T, C, P, N>(ksh, vsh, wsh, S, wave, g, r);
     __syncthreads();  // the next chunk restages the tiles
   }
   float* dst = (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
@@ -243,8 +318,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
 // grid (nstate, batch*nheads), 256 threads.  Combines the pieces of one
 // half: forward, each piece decayed from its end to the end of the half
 // (pieces from last to first); reverse, from the start of the half to the
-// piece's start (pieces in order).  Writes the state in the io type,
-// row-major [N][P].
+// piece's start (pieces in order).  Writes the fp32 state, row-major [N][P].
 template <class T, int P, int N, bool REV>
 __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
   constexpr int Q4 = N * P / 4;              // float4 groups of a state
@@ -275,7 +349,7 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
     for (int m = clo; m < chi; ++m) pt += at[m];
     run += pt;
   }
-  T* dst = static_cast<T*>(REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + blockIdx.x) * (N * P);
+  float* dst = (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + blockIdx.x) * (N * P);
 #pragma unroll
   for (int q = 0; q < EPT; ++q)
     if (q * 256 + tid < Q4) store4(dst + (q * 256 + tid) * 4, acc[q]);
@@ -287,12 +361,13 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
 // fit the 160 KB of a CU).
 template <class T, int C, int P, int N>
 constexpr int bwd_dq_lds() {
-  return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + N * P) +
+  return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
          4 * (C * (C + 1) + C * 8 + C * BWD_LMAX + 4 * 64);
 }
 template <class T, int C, int P, int N>
 constexpr int bwd_dkv_lds() {
-  return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + N * P) + 4 * (C * 8 + 3 * 64);
+  return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
+         4 * (C * (C + 1) + C * 8 + 4 * 64);
 }
 
 // S = C B^T and D = dO X^T for the query rows [16 wave, +16) of the chunk
@@ -358,6 +433,7 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
   __shared__ __attribute__((aligned(16))) T osh[C * P];
   __shared__ __attribute__((aligned(16))) T wsh[C * C];
   __shared__ __attribute__((aligned(16))) T zsh[N * P];
+  __shared__ __attribute__((aligned(16))) T zlo[sizeof(T) == 2 ? N * P : 1];
   __shared__ float esd[C][C + 1];
   __shared__ float lam_s[C][8];
   __shared__ float dlam_s[C][BWD_LMAX];
@@ -427,9 +503,8 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
     if (!((j >> (k - 1)) & 1)) continue;  // uniform
     const int h0 = (j >> (k - 1)) << (k - 1);  // first chunk of j's upper half
     const float gap = range_sum(at, h0, j, lane);
-    const T* zg = static_cast<const T*>(pr.zst) +
-                  ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, j >> k)) * (N * P);
-    rows_load<T, N, P, NT>(zg, P, zsh, tid);
+    const float* zg = pr.zst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, j >> k)) * (N * P);
+    rows_load_split<T, N, P, NT>(zg, zsh, zlo, tid);
     __syncthreads();
     f32x4 u[NB];  // u[t][n] = sum_p dO[t][p] Z[n][p]
 #pragma unroll
@@ -438,8 +513,11 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
     for (int kp = 0; kp < P / KB; ++kp) {
       const auto a = frag_along<T, LP>(osh, tw + r, kp * KB, g);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
         u[nb] = M::mma(a, frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g), u[nb]);
+        if constexpr (sizeof(T) == 2)
+          u[nb] = M::mma(a, frag_along<T, LP>(zlo, 16 * nb + r, kp * KB, g), u[nb]);
+      }
     }
     const int lv = c_log + k;
 #pragma unroll
@@ -496,6 +574,7 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
   __shared__ __attribute__((aligned(16))) T wsh[C * C];
   __shared__ __attribute__((aligned(16))) T vsh[C * C];
   __shared__ __attribute__((aligned(16))) T rsh[N * P];
+  __shared__ __attribute__((aligned(16))) T rlo[sizeof(T) == 2 ? N * P : 1];
   __shared__ float gsh[C][C + 1];
   __shared__ float lam_s[C][8];
   __shared__ float cum[64], ecum[64], wst[64], colsum[64];
@@ -560,9 +639,8 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
     const int h0 = ((i_ch >> (k - 1)) + 1) << (k - 1);  // first chunk of the upper half
     if (h0 >= pr.nc) continue;
     const float gap = range_sum(at, i_ch + 1, h0, lane);
-    const T* rg = static_cast<const T*>(pr.rst) +
-                  ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, i_ch >> k)) * (N * P);
-    rows_load<T, N, P, NT>(rg, P, rsh, tid);
+    const float* rg = pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, i_ch >> k)) * (N * P);
+    rows_load_split<T, N, P, NT>(rg, rsh, rlo, tid);
     __syncthreads();
     f32x4 tx[PB], tb[NB];
 #pragma unroll
@@ -573,15 +651,21 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
     for (int kn = 0; kn < N / KB; ++kn) {  // tx[s][p] = sum_n B[s][n] R[n][p]
       const auto a = frag_along<T, LN>(bsh, sw + r, kn * KB, g);
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb)
+      for (int pb = 0; pb < PB; ++pb) {
         tx[pb] = M::mma(a, frag_down<T, LP>(rsh, kn * KB, 16 * pb, g, r), tx[pb]);
+        if constexpr (sizeof(T) == 2)
+          tx[pb] = M::mma(a, frag_down<T, LP>(rlo, kn * KB, 16 * pb, g, r), tx[pb]);
+      }
     }
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {  // tb[s][n] = sum_p X[s][p] R[n][p]
       const auto a = frag_along<T, LP>(xsh, sw + r, kp * KB, g);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
         tb[nb] = M::mma(a, frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g), tb[nb]);
+        if constexpr (sizeof(T) == 2)
+          tb[nb] = M::mma(a, frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g), tb[nb]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

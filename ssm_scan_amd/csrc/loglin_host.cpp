@@ -149,7 +149,7 @@ loglin::BwdFn pick_bwd(int dtype, int chunk, int P, int N) {
 }
 
 // Backward workspace: chunk log-decays, the two directions' piece partials
-// (fp32) and level states (io type), the per-head dC and dB shares and the
+// and level states (fp32), the per-head dC and dB shares and the
 // two per-token terms of dlog_a; each region 256-byte aligned.
 struct BwdPlan {
   int nc, kc, ll, npart, nstate;
@@ -174,7 +174,6 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   pl->nstate = (int)nstate;
   const size_t bh = (size_t)(d->batch * d->nheads);
   const size_t pn = (size_t)(d->headdim * d->dstate);
-  const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;
   const size_t tok = (size_t)(d->batch * d->seqlen);
   size_t off = 0;
   pl->off_atot = off;
@@ -184,9 +183,9 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   pl->off_pr = off;
   off = round_up(off + bh * npart * pn * sizeof(float));
   pl->off_z = off;
-  off = round_up(off + bh * nstate * pn * esz);
+  off = round_up(off + bh * nstate * pn * sizeof(float));
   pl->off_r = off;
-  off = round_up(off + bh * nstate * pn * esz);
+  off = round_up(off + bh * nstate * pn * sizeof(float));
   pl->off_dch = off;
   off = round_up(off + tok * d->nheads * d->dstate * sizeof(float));
   pl->off_dbh = off;
@@ -385,8 +384,8 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   pr.atot = reinterpret_cast<float*>(ws + pl.off_atot);
   pr.part_f = reinterpret_cast<float*>(ws + pl.off_pf);
   pr.part_r = reinterpret_cast<float*>(ws + pl.off_pr);
-  pr.zst = ws + pl.off_z;
-  pr.rst = ws + pl.off_r;
+  pr.zst = reinterpret_cast<float*>(ws + pl.off_z);
+  pr.rst = reinterpret_cast<float*>(ws + pl.off_r);
   pr.dch = reinterpret_cast<float*>(ws + pl.off_dch);
   pr.dbh = reinterpret_cast<float*>(ws + pl.off_dbh);
   pr.term1 = reinterpret_cast<float*>(ws + pl.off_t1);

@@ -152,3 +152,22 @@ def test_planted_mistake_is_caught(name):
     want = fd_all(args, dO)
     worst = max(rel_err(got[k], want[k]) for k in want)
     assert worst > 1e-3, (name, worst)
+
+
+def test_sampled_entries_match_full_gradients():
+    """The O(T)-per-entry helpers used at full size agree with the pinned
+    full gradient oracle (every key column, query row and dlog_a entry)."""
+    X, B, C, log_a, lam = rand_problem(45, H=4, G=2, P=3, N=4, seed=11)
+    dO = np.random.default_rng(7).standard_normal(X.shape)
+    for h in range(4):
+        full = loglin_grad.loglin_grad_bh(X, B, C, log_a, lam, dO, 0, h)
+        idx = np.arange(45)
+        dX, dB = loglin_grad.grad_key_columns(X, B, C, log_a, lam, dO, 0, h, idx)
+        dC, dlam = loglin_grad.grad_query_rows(X, B, C, log_a, lam, dO, 0, h, idx)
+        assert rel_err(dX, full["dX"]) < 1e-12
+        assert rel_err(dB, full["dB_h"]) < 1e-12
+        assert rel_err(dC, full["dC_h"]) < 1e-12
+        assert rel_err(dlam, full["dlam"]) < 1e-12
+        dla = np.array([loglin_grad.grad_log_a_at(X, B, C, log_a, lam, dO, 0, h, r)
+                        for r in range(45)])
+        assert rel_err(dla, full["dlog_a"]) < 1e-12
