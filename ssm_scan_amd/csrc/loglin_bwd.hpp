@@ -21,7 +21,8 @@
 // the query); keys in the lower half receive from the upper half (reverse
 // direction: key C, value dO, and lambda[t, c + k] of the upper half's
 // tokens, which is why those states are per level).  Launches:
-//   1. bwd_atot_kernel          per-chunk total log-decay;
+//   1. bwd_atot_kernel          per-chunk total log-decay, bwd_cuma_kernel
+//                               their fp64 prefix sums;
 //   2. bwd_level_state_kernel   per (level, pair, piece of <= 8 chunks): the
 //                               decayed sum over the piece's chunks of the
 //                               lower half (forward) or upper half (reverse);
@@ -51,6 +52,7 @@ struct BwdParams {
   float* dloga;
   void* dlam;
   float* atot;    // [batch*nheads, nc]
+  double* cuma;   // [batch*nheads, nc + 1] exclusive prefix sums of atot
   float* part_f;  // [batch*nheads, npart, N, P] fp32, lower-half pieces
   float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
   float* zst;     // [batch*nheads, nstate, N, P] fp32, lower-half sums
@@ -62,6 +64,7 @@ struct BwdParams {
   int batch, seqlen, nheads, ngroups, nlevels;
   int nc, kc, ll;
   int npart, nstate;  // per (batch, head)
+  int nstate_direct;  // states of the levels whose half is one piece (listed first)
 };
 
 // Pieces of at most BWD_PIECE chunks bound the serial work of one
@@ -207,15 +210,6 @@ __device__ inline void chunk_state_mma_split(const T* ks, const T* vs, const flo
   }
 }
 
-// sum of a[lo..hi), the same bits in every lane of the wave
-__device__ inline float range_sum(const float* a, int lo, int hi, int lane) {
-  float s = 0.f;
-  for (int m = lo + lane; m < hi; m += 64) s += a[m];
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
-  return s;
-}
-
 // sum over the 16 lanes r of a lane group (MFMA result columns)
 __device__ inline float sum16(float v) {
   v += __shfl_xor(v, 1, 64);
@@ -239,6 +233,61 @@ __global__ __launch_bounds__(64) void bwd_atot_kernel(BwdParams pr) {
   if (tid == 0) pr.atot[(int64_t)bh * pr.nc + j] = cum[C - 1];
 }
 
+// grid (batch*nheads), 1024 threads: cuma[j] = sum_{m < j} atot[m] in fp64,
+// so that any range of chunk log-decays (a level's gap) is one subtraction
+// with no cancellation at fp32 resolution.
+constexpr int BWD_SCAN_NT = 1024;
+template <class T>  // (a template so that every unit's copy is a weak symbol)
+__global__ __launch_bounds__(BWD_SCAN_NT) void bwd_cuma_kernel(BwdParams pr) {
+  __shared__ double sh[BWD_SCAN_NT];
+  const int bh = blockIdx.x, tid = threadIdx.x, nc = pr.nc;
+  const int per = (nc + BWD_SCAN_NT - 1) / BWD_SCAN_NT;
+  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
+  const float* at = pr.atot + (int64_t)bh * nc;
+  double tot = 0.0;
+  for (int m = lo; m < hi; ++m) tot += at[m];
+  sh[tid] = tot;
+  __syncthreads();
+  for (int d = 1; d < BWD_SCAN_NT; d <<= 1) {  // inclusive prefix sums over threads
+    const double v = tid >= d ? sh[tid - d] : 0.0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  double run = tid ? sh[tid - 1] : 0.0;
+  double* ca = pr.cuma + (int64_t)bh * (nc + 1);
+  for (int m = lo; m < hi; ++m) {
+    ca[m] = run;
+    run += at[m];
+  }
+  if (tid == BWD_SCAN_NT - 1) ca[nc] = sh[BWD_SCAN_NT - 1];
+}
+
+// Token tiles of one chunk staged through registers: every global load of
+// the four tiles is issued before the first LDS store, so the work-group
+// waits for one memory latency instead of one per load.
+template <class T, int R, int W, int NT>
+struct RowsStage {
+  using L = Rows<T, W>;
+  static constexpr int PIECES = R * L::NBLK;
+  static constexpr int IT = (PIECES + NT - 1) / NT;
+  vec16_t<T> v[IT];
+  __device__ inline void load(const T* g, int64_t grs, int tid) {
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int i = q * NT + tid;
+      if (i < PIECES) v[q] = load16(g + (int64_t)(i / L::NBLK) * grs + (i % L::NBLK) * L::VEC);
+    }
+  }
+  __device__ inline void store(T* lds, int tid) const {
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int i = q * NT + tid;
+      if (i < PIECES) store16(lds + L::at(i / L::NBLK, (i % L::NBLK) * L::VEC), v[q]);
+    }
+  }
+};
+
 // ------------------------------------------------------------ launch 2
 
 // grid (npart, batch*nheads).  Wave w owns state columns [16 w, 16 w + 16)
@@ -248,7 +297,9 @@ __global__ __launch_bounds__(64) void bwd_atot_kernel(BwdParams pr) {
 // so the result is decayed to the end of the piece.  Reverse: chunks in
 // reverse order, key C, value dO, weight lambda[t, c + k] exp(decay from the
 // chunk start to t); acc <- exp(Atot_j) acc + chunk state, decayed to the
-// start of the piece.
+// start of the piece.  A level whose half is a single piece writes its state
+// directly; other levels write partials for bwd_level_reduce_kernel.  The
+// next chunk's rows are loaded into registers while the current one is used.
 template <class T, int C, int P, int N, bool REV>
 __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kernel(BwdParams pr) {
   using Tl = Tiles<T, C, P, N>;
@@ -274,31 +325,35 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
   f32x4 S[Tl::NB];
 #pragma unroll
   for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int step = 0; step < hi - lo; ++step) {
-    const int j = REV ? hi - 1 - step : lo + step;
+  RowsStage<T, C, N, NT> sk;
+  RowsStage<T, C, P, NT> sv;
+  // issue the loads of chunk j's rows; returns its log a and lambda values
+  // for this thread's token (by value: see the scan pass on loop-carried
+  // values held through references)
+  auto issue = [&](int j) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)j * C;
-    const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+    const T* kg = static_cast<const T*>(REV ? pr.Cm : pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N;
+    const T* vg = static_cast<const T*>(REV ? pr.dO : pr.X) + (((int64_t)b * T_ + t0) * H + h) * P;
+    sk.load(kg, (int64_t)G * N, tid);
+    sv.load(vg, (int64_t)H * P, tid);
+    const int tt = tid < C ? tid : 0;
+    f32x2 v;
+    v[0] = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tt) * H + h] : 0.f;
+    v[1] = REV ? to_f(static_cast<const T*>(pr.lam)[(((int64_t)b * T_ + t0 + tt) * H + h) * L + c_log + k])
+               : 0.f;
+    return v;
+  };
+  const int n = hi - lo;
+  f32x2 nxt = {0.f, 0.f};
+  if (n > 0) nxt = issue(REV ? hi - 1 : lo);
+  for (int step = 0; step < n; ++step) {
+    sk.store(ksh, tid);
+    sv.store(vsh, tid);
+    const float la = nxt[0], lamv = nxt[1];
+    if (step + 1 < n) nxt = issue(REV ? hi - 2 - step : lo + step + 1);
     chunk_decays<T, C>(la, cum, ecum, wst, tid);
-    if (REV) {
-      rows_load<T, C, N, NT>(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N,
-                             (int64_t)G * N, ksh, tid);
-      rows_load<T, C, P, NT>(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P,
-                             (int64_t)H * P, vsh, tid);
-    } else {
-      rows_load<T, C, N, NT>(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N,
-                             (int64_t)G * N, ksh, tid);
-      rows_load<T, C, P, NT>(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P,
-                             (int64_t)H * P, vsh, tid);
-    }
     __syncthreads();
-    if (tid < C) {
-      if (REV) {
-        const T* lr = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0 + tid) * H + h) * L;
-        wsh[tid] = to_f(lr[c_log + k]) * ecum[tid];
-      } else {
-        wsh[tid] = wst[tid];
-      }
-    }
+    if (tid < C) wsh[tid] = REV ? lamv * ecum[tid] : wst[tid];
     __syncthreads();
     const float dec = M::ex(cum[C - 1]);
 #pragma unroll
@@ -306,7 +361,9 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
     chunk_state_mma_split<T, C, P, N>(ksh, vsh, wsh, S, wave, g, r);
     __syncthreads();  // the next chunk restages the tiles
   }
-  float* dst = (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
+  float* dst = bwd_pieces(k) == 1
+                   ? (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P)
+                   : (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
 #pragma unroll
   for (int nb = 0; nb < Tl::NB; ++nb)
 #pragma unroll
@@ -324,8 +381,9 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
   constexpr int Q4 = N * P / 4;              // float4 groups of a state
   constexpr int EPT = (Q4 + 255) / 256;      // per thread
   const int bh = blockIdx.y, tid = threadIdx.x;
+  const int sidx = pr.nstate_direct + blockIdx.x;  // only levels with several pieces
   int k, pair;
-  bwd_state_of(blockIdx.x, pr.nc, pr.kc, k, pair);
+  bwd_state_of(sidx, pr.nc, pr.kc, k, pair);
   const int half = 1 << (k - 1);
   const int base = pair * 2 * half + (REV ? half : 0);
   const int np = bwd_pieces(k);
@@ -349,7 +407,7 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
     for (int m = clo; m < chi; ++m) pt += at[m];
     run += pt;
   }
-  float* dst = (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + blockIdx.x) * (N * P);
+  float* dst = (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + sidx) * (N * P);
 #pragma unroll
   for (int q = 0; q < EPT; ++q)
     if (q * 256 + tid < Q4) store4(dst + (q * 256 + tid) * 4, acc[q]);
@@ -362,12 +420,12 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
 template <class T, int C, int P, int N>
 constexpr int bwd_dq_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + C * 8 + C * BWD_LMAX + 4 * 64);
+         4 * (C * (C + 1) + 2 * C * BWD_LMAX + 4 * 64 + BWD_LMAX);
 }
 template <class T, int C, int P, int N>
 constexpr int bwd_dkv_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + C * 8 + 4 * 64);
+         4 * (C * (C + 1) + C * 8 + 4 * 64 + 4 * 64 + BWD_LMAX);
 }
 
 // S = C B^T and D = dO X^T for the query rows [16 wave, +16) of the chunk
@@ -375,9 +433,9 @@ constexpr int bwd_dkv_lds() {
 // M[t, s] = exp(cum_t - cum_s) lambda[t, level(t, s)] for s <= t:
 // wm = M ⊙ S (if WANT_WS), wd = M ⊙ D in the io type, and optionally
 // E ⊙ S ⊙ D or G = M ⊙ S ⊙ D in fp32.
-template <class T, int C, int P, int N, bool WANT_WS, bool WANT_ESD, bool WANT_G>
+template <class T, int C, int P, int N, int LW, bool WANT_WS, bool WANT_ESD, bool WANT_G>
 __device__ inline void bwd_intra_scores(const T* csh, const T* bsh, const T* xsh, const T* osh,
-                                        const float* cum, const float (*lam_s)[8], T* wm, T* wd,
+                                        const float* cum, const float (*lam_s)[LW], T* wm, T* wd,
                                         float (*esd)[C + 1], int wave, int g, int r) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
@@ -414,18 +472,74 @@ __device__ inline void bwd_intra_scores(const T* csh, const T* bsh, const T* xsh
   }
 }
 
-// grid (nc, batch*nheads), C/16 waves; wave w owns query rows [16 w, +16).
-// dC_t = sum_s (M ⊙ D)[t, s] B_s within the chunk plus, for each chunk level
-// k whose bit is set in j, lambda[t, c+k] exp(decay) (Z_k dO_t) with Z_k the
-// lower half's state; dlambda[t, l] = sum over the level-l bucket of E S D
-// inside the chunk, and exp(decay) C_t . (Z_k dO_t) at level c + k.
+// A level state (fp32 [N][P], row-major) prefetched into registers, then
+// stored to LDS as the hi / lo pair of rows_load_split.
+template <class T, int N, int P, int NT>
+struct StateStage {
+  using L = Rows<T, P>;
+  static constexpr int PIECES = N * L::NBLK;  // 16-byte io-type pieces
+  static constexpr int IT = (PIECES + NT - 1) / NT;
+  static constexpr int F4 = L::VEC / 4;  // float4 per piece
+  f32x4 v[IT][F4];
+  __device__ inline void load(const float* g, int tid) {
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int i = q * NT + tid;
+      if (i < PIECES) {
+        const float* src = g + (int64_t)(i / L::NBLK) * P + (i % L::NBLK) * L::VEC;
+#pragma unroll
+        for (int f = 0; f < F4; ++f) v[q][f] = *reinterpret_cast<const f32x4*>(src + 4 * f);
+      }
+    }
+  }
+  __device__ inline void store(T* hi, T* lo, int tid) const {
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int i = q * NT + tid;
+      if (i < PIECES) {
+        const int o = L::at(i / L::NBLK, (i % L::NBLK) * L::VEC);
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 h, l;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = v[q][e >> 2][e & 3];
+            h[e] = (bf16)x;
+            l[e] = (bf16)(x - (float)h[e]);
+          }
+          store16(hi + o, h);
+          store16(lo + o, l);
+        } else {
+          store16(hi + o, v[q][0]);
+        }
+      }
+    }
+  }
+};
+
+// Chunk passes: one work-group per (batch*head, chunk), a 1-D grid dealt to
+// the XCDs in contiguous ranges (xcd_tile), so the chunks that read the same
+// level state run on one L2.
+__device__ inline bool bwd_chunk_tile(const BwdParams& pr, int& bh, int& j) {
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  if (tile >= pr.batch * pr.nheads * pr.nc) return false;
+  bh = tile / pr.nc;
+  j = tile % pr.nc;
+  return true;
+}
+
+// Wave w owns query rows [16 w, +16).  dC_t = sum_s (M ⊙ D)[t, s] B_s within
+// the chunk plus, for each chunk level k whose bit is set in j,
+// lambda[t, c+k] exp(decay) (Z_k dO_t) with Z_k the lower half's state;
+// dlambda[t, l] = the level-l bucket sum of E S D inside the chunk, and
+// exp(decay) C_t . (Z_k dO_t) at level c + k.  The next level's state is
+// loaded into registers while the current one is used.
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  constexpr int NT = C / 16 * 64, KB = M::KB, NB = N / 16;
+  constexpr int NW = C / 16, NT = NW * 64, KB = M::KB, NB = N / 16;
   constexpr int c_log = ilog2c(C);
   __shared__ __attribute__((aligned(16))) T csh[C * N];
   __shared__ __attribute__((aligned(16))) T bsh[C * N];
@@ -435,54 +549,90 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
   __shared__ __attribute__((aligned(16))) T zsh[N * P];
   __shared__ __attribute__((aligned(16))) T zlo[sizeof(T) == 2 ? N * P : 1];
   __shared__ float esd[C][C + 1];
-  __shared__ float lam_s[C][8];
+  __shared__ float lam_s[C][BWD_LMAX];
   __shared__ float dlam_s[C][BWD_LMAX];
-  __shared__ float cum[64], ecum[64], wst[64], term_s[64];
+  __shared__ float cum[64], ecum[64], wst[64], term_s[64], gap_s[BWD_LMAX];
+  int bh, j;
+  if (!bwd_chunk_tile(pr, bh, j)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = blockIdx.x, bh = blockIdx.y;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
   const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
-  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N,
-                         (int64_t)G * N, csh, tid);
-  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N,
-                         (int64_t)G * N, bsh, tid);
-  rows_load<T, C, P, NT>(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P,
-                         (int64_t)H * P, xsh, tid);
-  rows_load<T, C, P, NT>(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P,
-                         (int64_t)H * P, osh, tid);
-  for (int i = tid; i < C * (c_log + 1); i += NT) {
-    const int t = i / (c_log + 1), l = i % (c_log + 1);
-    lam_s[t][l] = to_f(lg[(int64_t)t * H * L + l]);
+  const unsigned act0 = (unsigned)j & ((1u << pr.kc) - 1u);  // active chunk levels (bit k-1)
+
+  RowsStage<T, C, N, NT> sc, sb;
+  RowsStage<T, C, P, NT> sx, so;
+  sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+  sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+  sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+  so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+  // lambda rows: every level the sequence reaches (ll <= BWD_LMAX)
+  constexpr int LIT = (C * BWD_LMAX + NT - 1) / NT;
+  const int ll = pr.ll;
+  float lv_[LIT];
+#pragma unroll
+  for (int q = 0; q < LIT; ++q) {
+    const int i = q * NT + tid;
+    lv_[q] = i < C * ll ? to_f(lg[(int64_t)(i / ll) * H * L + i % ll]) : 0.f;
   }
-  for (int i = tid; i < C * pr.ll; i += NT) dlam_s[i / pr.ll][i % pr.ll] = 0.f;
   const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+  // level k's gap: log-decay from the end of the lower half to chunk j
+  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
+  float gap = 0.f;
+  if (tid < pr.kc && ((act0 >> tid) & 1u)) {
+    const int h0 = (j >> tid) << tid;  // first chunk of j's upper half at level tid + 1
+    gap = (float)(ca[j] - ca[h0]);
+  }
+  // the states of the first two active levels are requested now, each later
+  // one two levels ahead of its use
+  StateStage<T, N, P, NT> st0, st1;  // two named buffers: no runtime array index
+  auto state_of = [&](int kk) {
+    return pr.zst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, kk, j >> kk)) * (N * P);
+  };
+  unsigned act = act0;
+  int k = act ? __builtin_ctz(act) + 1 : 0;
+  unsigned act2 = act ? act & (act - 1u) : 0u;
+  const int k2 = act2 ? __builtin_ctz(act2) + 1 : 0;
+  if (k) st0.load(state_of(k), tid);
+  if (k2) st1.load(state_of(k2), tid);
+
+  sc.store(csh, tid);
+  sb.store(bsh, tid);
+  sx.store(xsh, tid);
+  so.store(osh, tid);
+#pragma unroll
+  for (int q = 0; q < LIT; ++q) {
+    const int i = q * NT + tid;
+    if (i < C * ll) {
+      lam_s[i / ll][i % ll] = lv_[q];
+      dlam_s[i / ll][i % ll] = 0.f;
+    }
+  }
+  if (tid < pr.kc) gap_s[tid + 1] = gap;
   chunk_decays<T, C>(la, cum, ecum, wst, tid);
   __syncthreads();
 
-  bwd_intra_scores<T, C, P, N, false, true, false>(csh, bsh, xsh, osh, cum, lam_s, nullptr,
-                                                   wsh, esd, wave, g, r);
+  bwd_intra_scores<T, C, P, N, BWD_LMAX, false, true, false>(csh, bsh, xsh, osh, cum, lam_s,
+                                                             nullptr, wsh, esd, wave, g, r);
   __syncthreads();
 
   // intra-chunk levels: the level-l bucket of t (l >= 1) is the 2^(l-1) keys
-  // below t's aligned 2^l block boundary, present when bit l-1 of t is set
-  if (tid < C) {
-    const int t = tid;
-    float v0 = esd[t][t];
-    dlam_s[t][0] = v0;
-    float tsum = lam_s[t][0] * v0;
-    for (int l = 1; l <= c_log; ++l) {
+  // below t's aligned 2^l block boundary, present when bit l-1 of t is set;
+  // wave w sums the levels l = w mod NW
+  if (lane < C) {
+    const int t = lane;
+    for (int l = wave; l <= c_log; l += NW) {
       float v = 0.f;
-      if ((t >> (l - 1)) & 1) {
+      if (l == 0) {
+        v = esd[t][t];
+      } else if ((t >> (l - 1)) & 1) {
         const int lo = t & ~((1 << l) - 1);
         for (int s = lo; s < lo + (1 << (l - 1)); ++s) v += esd[t][s];
       }
       dlam_s[t][l] = v;
-      tsum += lam_s[t][l] * v;
     }
-    term_s[t] = tsum;
   }
 
   const int tw = 16 * wave;
@@ -496,16 +646,31 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
     for (int nb = 0; nb < NB; ++nb)
       dc[nb] = M::mma(a, frag_down<T, LN>(bsh, kt * KB, 16 * nb, g, r), dc[nb]);
   }
-  __syncthreads();  // term_s and dlam_s of the intra levels are written
+  __syncthreads();  // dlam_s of the intra levels is written
+  if (tid < C) {
+    float tsum = 0.f;
+    for (int l = 0; l <= c_log; ++l) tsum += lam_s[tid][l] * dlam_s[tid][l];
+    term_s[tid] = tsum;
+  }
+  __syncthreads();
 
-  const float* at = pr.atot + (int64_t)bh * pr.nc;
-  for (int k = 1; k <= pr.kc; ++k) {
-    if (!((j >> (k - 1)) & 1)) continue;  // uniform
-    const int h0 = (j >> (k - 1)) << (k - 1);  // first chunk of j's upper half
-    const float gap = range_sum(at, h0, j, lane);
-    const float* zg = pr.zst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, j >> k)) * (N * P);
-    rows_load_split<T, N, P, NT>(zg, zsh, zlo, tid);
+  int buf = 0;
+  while (k) {
+    if (buf == 0)  // uniform
+      st0.store(zsh, zlo, tid);
+    else
+      st1.store(zsh, zlo, tid);
     __syncthreads();
+    act &= act - 1u;
+    const int kn = act ? __builtin_ctz(act) + 1 : 0;
+    const unsigned a3 = act ? act & (act - 1u) : 0u;
+    const int k3 = a3 ? __builtin_ctz(a3) + 1 : 0;  // two levels ahead
+    if (k3) {
+      if (buf == 0)
+        st0.load(state_of(k3), tid);
+      else
+        st1.load(state_of(k3), tid);
+    }
     f32x4 u[NB];  // u[t][n] = sum_p dO[t][p] Z[n][p]
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) u[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -520,15 +685,16 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
       }
     }
     const int lv = c_log + k;
+    const float gk = gap_s[k];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tw + 4 * g + i;
-      const float wt = M::ex(cum[t] + gap);
+      const float wt = M::ex(cum[t] + gk);
       float part = 0.f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) part += u[nb][i] * to_f(csh[LN::at(t, 16 * nb + r)]);
       const float dl = wt * sum16(part);
-      const float lk = to_f(lg[(int64_t)t * H * L + lv]);
+      const float lk = lam_s[t][lv];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) dc[nb][i] += (lk * wt) * u[nb][i];
       if (r == 0) {
@@ -537,6 +703,8 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
       }
     }
     __syncthreads();  // zsh is restaged by the next level
+    k = kn;
+    buf ^= 1;
   }
 
   float* dcg = pr.dch + (((int64_t)b * T_ + t0) * H + h) * N;
@@ -544,7 +712,6 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * nb + r] = dc[nb][i];
-  __syncthreads();
   T* dlg = static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L;
   for (int i = tid; i < C * L; i += NT) {
     const int t = i / L, l = i % L;
@@ -553,19 +720,19 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
   if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid];
 }
 
-// grid (nc, batch*nheads), C/16 waves.  The mask epilogue runs per query row
-// block as in bwd_dq_kernel; then wave w owns key rows [16 w, +16):
-// dX_s = sum_t (M ⊙ S)[t, s] dO_t and dB_s = sum_t (M ⊙ D)[t, s] C_t within the
-// chunk, plus, for each chunk level k whose bit is clear in i and whose upper
-// half exists, exp(decay s -> end of the lower half) (R_k^T B_s, R_k X_s)
-// with R_k the upper half's state (lambda already on its tokens).
+// The mask epilogue runs per query row block as in bwd_dq_kernel; then wave
+// w owns key rows [16 w, +16): dX_s = sum_t (M ⊙ S)[t, s] dO_t and
+// dB_s = sum_t (M ⊙ D)[t, s] C_t within the chunk, plus, for each chunk level
+// k whose bit is clear in i and whose upper half exists,
+// exp(decay s -> end of the lower half) (R_k^T B_s, R_k X_s) with R_k the
+// upper half's state (lambda already on its tokens).
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  constexpr int NT = C / 16 * 64, KB = M::KB, NB = N / 16, PB = P / 16;
+  constexpr int NW = C / 16, NT = NW * 64, KB = M::KB, NB = N / 16, PB = P / 16;
   constexpr int c_log = ilog2c(C);
   __shared__ __attribute__((aligned(16))) T csh[C * N];
   __shared__ __attribute__((aligned(16))) T bsh[C * N];
@@ -577,43 +744,79 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
   __shared__ __attribute__((aligned(16))) T rlo[sizeof(T) == 2 ? N * P : 1];
   __shared__ float gsh[C][C + 1];
   __shared__ float lam_s[C][8];
-  __shared__ float cum[64], ecum[64], wst[64], colsum[64];
+  __shared__ float colpart[NW][64];
+  __shared__ float cum[64], ecum[64], wst[64], gap_s[BWD_LMAX];
+  int bh, i_ch;
+  if (!bwd_chunk_tile(pr, bh, i_ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int i_ch = blockIdx.x, bh = blockIdx.y;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t T_ = pr.seqlen, t0 = (int64_t)i_ch * C;
   const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
-  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N,
-                         (int64_t)G * N, csh, tid);
-  rows_load<T, C, N, NT>(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N,
-                         (int64_t)G * N, bsh, tid);
-  rows_load<T, C, P, NT>(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P,
-                         (int64_t)H * P, xsh, tid);
-  rows_load<T, C, P, NT>(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P,
-                         (int64_t)H * P, osh, tid);
-  for (int i = tid; i < C * (c_log + 1); i += NT) {
-    const int t = i / (c_log + 1), l = i % (c_log + 1);
-    lam_s[t][l] = to_f(lg[(int64_t)t * H * L + l]);
+  // active chunk levels (bit k-1): i in a lower half whose upper half exists
+  unsigned act0 = 0;
+  for (int k = 1; k <= pr.kc; ++k)
+    if (!((i_ch >> (k - 1)) & 1) && ((((i_ch >> (k - 1)) + 1) << (k - 1)) < pr.nc)) act0 |= 1u << (k - 1);
+
+  RowsStage<T, C, N, NT> sc, sb;
+  RowsStage<T, C, P, NT> sx, so;
+  sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+  sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+  sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+  so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+  constexpr int LIT = (C * (c_log + 1) + NT - 1) / NT;
+  float lv_[LIT];
+#pragma unroll
+  for (int q = 0; q < LIT; ++q) {
+    const int i = q * NT + tid;
+    lv_[q] = i < C * (c_log + 1) ? to_f(lg[(int64_t)(i / (c_log + 1)) * H * L + i % (c_log + 1)]) : 0.f;
   }
   const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+  // level k's gap: log-decay from the end of chunk i to the end of its lower half
+  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
+  float gap = 0.f;
+  if (tid < pr.kc && ((act0 >> tid) & 1u)) {
+    const int h0 = ((i_ch >> tid) + 1) << tid;  // first chunk of the upper half at level tid + 1
+    gap = (float)(ca[h0] - ca[i_ch + 1]);
+  }
+  StateStage<T, N, P, NT> st0, st1;  // two named buffers: no runtime array index
+  auto state_of = [&](int kk) {
+    return pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, kk, i_ch >> kk)) * (N * P);
+  };
+  unsigned act = act0;
+  int k = act ? __builtin_ctz(act) + 1 : 0;
+  unsigned act2 = act ? act & (act - 1u) : 0u;
+  const int k2 = act2 ? __builtin_ctz(act2) + 1 : 0;
+  if (k) st0.load(state_of(k), tid);
+  if (k2) st1.load(state_of(k2), tid);
+
+  sc.store(csh, tid);
+  sb.store(bsh, tid);
+  sx.store(xsh, tid);
+  so.store(osh, tid);
+#pragma unroll
+  for (int q = 0; q < LIT; ++q) {
+    const int i = q * NT + tid;
+    if (i < C * (c_log + 1)) lam_s[i / (c_log + 1)][i % (c_log + 1)] = lv_[q];
+  }
+  if (tid < pr.kc) gap_s[tid + 1] = gap;
   chunk_decays<T, C>(la, cum, ecum, wst, tid);
   __syncthreads();
 
-  bwd_intra_scores<T, C, P, N, true, false, true>(csh, bsh, xsh, osh, cum, lam_s, wsh, vsh,
-                                                  gsh, wave, g, r);
+  bwd_intra_scores<T, C, P, N, 8, true, false, true>(csh, bsh, xsh, osh, cum, lam_s, wsh, vsh,
+                                                     gsh, wave, g, r);
   __syncthreads();
   // X_s . dX_s within the chunk is the column sum of G: taken in fp32 from
   // the same entries whose row sums form dO_t . O_t, so that the two terms of
   // dlog_a agree where they overlap (the rounding of M ⊙ S to the io type for
-  // the dX product would otherwise enter one term and not the other).
-  if (tid < C) {
+  // the dX product would otherwise enter one term and not the other).  Wave w
+  // sums the rows t = w mod NW.
+  if (lane < C) {
     float cs = 0.f;
-    for (int t = tid; t < C; ++t) cs += gsh[t][tid];
-    colsum[tid] = cs;
+    for (int t = lane + ((wave - lane) % NW + NW) % NW; t < C; t += NW) cs += gsh[t][lane];
+    colpart[wave][lane] = cs;
   }
-  __syncthreads();  // colsum is read by every wave at the end
 
   const int sw = 16 * wave;
   f32x4 dx[PB], dxe[PB], db[NB];  // dX: intra-chunk part, chunk-level part
@@ -633,28 +836,36 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
       db[nb] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * nb, g, r), db[nb]);
   }
 
-  const float* at = pr.atot + (int64_t)bh * pr.nc;
-  for (int k = 1; k <= pr.kc; ++k) {
-    if ((i_ch >> (k - 1)) & 1) continue;  // uniform: i is in an upper half
-    const int h0 = ((i_ch >> (k - 1)) + 1) << (k - 1);  // first chunk of the upper half
-    if (h0 >= pr.nc) continue;
-    const float gap = range_sum(at, i_ch + 1, h0, lane);
-    const float* rg = pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, i_ch >> k)) * (N * P);
-    rows_load_split<T, N, P, NT>(rg, rsh, rlo, tid);
+  int buf = 0;
+  while (k) {
+    if (buf == 0)  // uniform
+      st0.store(rsh, rlo, tid);
+    else
+      st1.store(rsh, rlo, tid);
     __syncthreads();
+    act &= act - 1u;
+    const int kn = act ? __builtin_ctz(act) + 1 : 0;
+    const unsigned a3 = act ? act & (act - 1u) : 0u;
+    const int k3 = a3 ? __builtin_ctz(a3) + 1 : 0;  // two levels ahead
+    if (k3) {
+      if (buf == 0)
+        st0.load(state_of(k3), tid);
+      else
+        st1.load(state_of(k3), tid);
+    }
     f32x4 tx[PB], tb[NB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) tx[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) tb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kn = 0; kn < N / KB; ++kn) {  // tx[s][p] = sum_n B[s][n] R[n][p]
-      const auto a = frag_along<T, LN>(bsh, sw + r, kn * KB, g);
+    for (int kn2 = 0; kn2 < N / KB; ++kn2) {  // tx[s][p] = sum_n B[s][n] R[n][p]
+      const auto a = frag_along<T, LN>(bsh, sw + r, kn2 * KB, g);
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) {
-        tx[pb] = M::mma(a, frag_down<T, LP>(rsh, kn * KB, 16 * pb, g, r), tx[pb]);
+        tx[pb] = M::mma(a, frag_down<T, LP>(rsh, kn2 * KB, 16 * pb, g, r), tx[pb]);
         if constexpr (sizeof(T) == 2)
-          tx[pb] = M::mma(a, frag_down<T, LP>(rlo, kn * KB, 16 * pb, g, r), tx[pb]);
+          tx[pb] = M::mma(a, frag_down<T, LP>(rlo, kn2 * KB, 16 * pb, g, r), tx[pb]);
       }
     }
 #pragma unroll
@@ -667,17 +878,21 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
           tb[nb] = M::mma(a, frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g), tb[nb]);
       }
     }
+    const float gk = gap_s[k];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = sw + 4 * g + i;
-      const float w = M::ex(cum[C - 1] - cum[s] + gap);
+      const float w = M::ex(cum[C - 1] - cum[s] + gk);
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) dxe[pb][i] += w * tx[pb][i];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) db[nb][i] += w * tb[nb][i];
     }
     __syncthreads();  // rsh is restaged by the next level
+    k = kn;
+    buf ^= 1;
   }
+  __syncthreads();  // colpart is complete (also when no level ran)
 
   T* dxg = static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P;
   float* dbg = pr.dbh + (((int64_t)b * T_ + t0) * H + h) * N;
@@ -693,7 +908,12 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) dbg[(int64_t)s * H * N + 16 * nb + r] = db[nb][i];
     part = sum16(part);
-    if (r == 0) pr.term2[(int64_t)bh * T_ + t0 + s] = colsum[s] + part;
+    if (r == 0) {
+      float cs = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) cs += colpart[w][s];
+      pr.term2[(int64_t)bh * T_ + t0 + s] = cs + part;
+    }
   }
 }
 
@@ -724,7 +944,6 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams pr) {
 
 // grid (batch*nheads), 1024 threads: dlog_a[t] = sum_{t' >= t} (term1 - term2),
 // each thread a contiguous run of tokens, runs combined by a suffix scan.
-constexpr int BWD_SCAN_NT = 1024;
 template <class T>  // (a template so that every unit's copy is a weak symbol)
 __global__ __launch_bounds__(BWD_SCAN_NT) void bwd_dloga_kernel(BwdParams pr) {
   __shared__ float sh[BWD_SCAN_NT];
@@ -761,18 +980,22 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
   using Tl = Tiles<T, C, P, N>;
   const int bh = pr.batch * pr.nheads;
   hipLaunchKernelGGL((bwd_atot_kernel<T, C>), dim3(pr.nc, bh), dim3(64), 0, st, pr);
+  hipLaunchKernelGGL((bwd_cuma_kernel<T>), dim3(bh), dim3(BWD_SCAN_NT), 0, st, pr);
   if (pr.npart > 0) {
     hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, false>), dim3(pr.npart, bh),
                        dim3(Tl::NT), 0, st, pr);
     hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh),
                        dim3(Tl::NT), 0, st, pr);
-    hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, false>), dim3(pr.nstate, bh), dim3(256),
-                       0, st, pr);
-    hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>), dim3(pr.nstate, bh), dim3(256),
-                       0, st, pr);
+    if (pr.nstate > pr.nstate_direct) {
+      hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, false>),
+                         dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
+      hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>),
+                         dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
+    }
   }
-  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(pr.nc, bh), dim3(C / 16 * 64), 0, st, pr);
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(pr.nc, bh), dim3(C / 16 * 64), 0, st, pr);
+  const int tiles8 = (pr.nc * bh + 7) & ~7;  // xcd_tile deals whole rounds of 8
+  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(tiles8), dim3(C / 16 * 64), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(tiles8), dim3(C / 16 * 64), 0, st, pr);
   const int64_t groups4 = (int64_t)pr.batch * pr.seqlen * pr.ngroups * (N / 4);
   hipLaunchKernelGGL((bwd_group_sum_kernel<T, N>), dim3((unsigned)((groups4 + 255) / 256)),
                      dim3(256), 0, st, pr);

@@ -148,12 +148,13 @@ loglin::BwdFn pick_bwd(int dtype, int chunk, int P, int N) {
   return nullptr;
 }
 
-// Backward workspace: chunk log-decays, the two directions' piece partials
+// Backward workspace: chunk log-decays and their fp64 prefix sums, the two
+// directions' piece partials
 // and level states (fp32), the per-head dC and dB shares and the
 // two per-token terms of dlog_a; each region 256-byte aligned.
 struct BwdPlan {
-  int nc, kc, ll, npart, nstate;
-  size_t off_atot, off_pf, off_pr, off_z, off_r, off_dch, off_dbh, off_t1, off_t2, bytes;
+  int nc, kc, ll, npart, nstate, nstate_direct;
+  size_t off_atot, off_cuma, off_pf, off_pr, off_z, off_r, off_dch, off_dbh, off_t1, off_t2, bytes;
 };
 
 int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
@@ -165,11 +166,13 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   pl->nc = fp.nc;
   pl->kc = fp.kc;
   pl->ll = fp.ll;
-  int64_t npart = 0, nstate = 0;
+  int64_t npart = 0, nstate = 0, ndirect = 0;
   for (int k = 1; k <= fp.kc; ++k) {
     npart += (int64_t)loglin::bwd_pairs(fp.nc, k) * loglin::bwd_pieces(k);
     nstate += loglin::bwd_pairs(fp.nc, k);
+    if (loglin::bwd_pieces(k) == 1) ndirect += loglin::bwd_pairs(fp.nc, k);
   }
+  pl->nstate_direct = (int)ndirect;
   pl->npart = (int)npart;
   pl->nstate = (int)nstate;
   const size_t bh = (size_t)(d->batch * d->nheads);
@@ -178,6 +181,8 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   size_t off = 0;
   pl->off_atot = off;
   off = round_up(off + bh * fp.nc * sizeof(float));
+  pl->off_cuma = off;
+  off = round_up(off + bh * (fp.nc + 1) * sizeof(double));
   pl->off_pf = off;
   off = round_up(off + bh * npart * pn * sizeof(float));
   pl->off_pr = off;
@@ -382,6 +387,7 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   pr.dloga = dlog_a;
   pr.dlam = dlambda;
   pr.atot = reinterpret_cast<float*>(ws + pl.off_atot);
+  pr.cuma = reinterpret_cast<double*>(ws + pl.off_cuma);
   pr.part_f = reinterpret_cast<float*>(ws + pl.off_pf);
   pr.part_r = reinterpret_cast<float*>(ws + pl.off_pr);
   pr.zst = reinterpret_cast<float*>(ws + pl.off_z);
@@ -400,6 +406,7 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   pr.ll = pl.ll;
   pr.npart = pl.npart;
   pr.nstate = pl.nstate;
+  pr.nstate_direct = pl.nstate_direct;
   return fn(pr, static_cast<hipStream_t>(stream)) ? LOGLIN_ERR_HIP : LOGLIN_OK;
 }
 
