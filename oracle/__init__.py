@@ -10,10 +10,13 @@ example; reduction to the SSD recurrence when lambda does not depend on the
 level; reduction to the causal prefix sum (linear attention) when a = 1 and
 lambda = 1; the token-by-token Fenwick recurrence; superposition over levels
 and per-bucket brute force.  The gradients (loglin_grad) are pinned to the
-forward by finite differences and by superposition over levels.  Conventions the pages cannot fix (group
+forward by finite differences and by superposition over levels.  The
+log-linear gated DeltaNet forward (gdn_ref) is pinned to the textbook gated
+DeltaNet recurrence, a per-level Fenwick recurrence, the log-linear Mamba-2
+oracle (orthonormal keys) and closed forms.  Conventions the pages cannot fix (group
 mapping, lambda layout, dtypes) are "parity unpinned".
 """
-from . import fenwick, loglin_grad, loglin_ref, recurrent  # noqa: F401
+from . import fenwick, gdn_ref, loglin_grad, loglin_ref, recurrent  # noqa: F401
 from .loglin_grad import loglin_grad as loglin_backward  # noqa: F401
 from .loglin_ref import loglin_forward, loglin_forward_bh, loglin_rows  # noqa: F401
 from .recurrent import loglin_recurrent  # noqa: F401

@@ -13,7 +13,8 @@ per-head scalar parameterisation, log a_t = -dt_t * exp(A_log[h]).
 Every tensor is drawn in float32 from numpy PCG64 streams, in flat blocks
 of BLOCK elements; block i of tensor k uses its own stream seeded with
 SeedSequence([seed, k, i]) (k: 0 X, 1 B, 2 C, 3 dt noise, 4 lambda, 5 A_log,
-6 the output gradient dO of the backward pass).
+6 the output gradient dO of the backward pass; 7..13 the gated DeltaNet
+inputs q, k, v, dt noise, beta noise, lambda, A_log).
 The values therefore do not depend on how many threads fill the blocks.
 bf16 inputs are rounded to nearest-even from those float32 draws.
 """
@@ -33,6 +34,7 @@ __all__ = [
     "bf16_round",
     "num_levels",
     "make_grad_output",
+    "make_gdn_inputs",
 ]
 
 
@@ -230,3 +232,48 @@ def make_grad_output(cfg: Config, seed: int = 0):
     if cfg.dtype == "fp32":
         return np.ascontiguousarray(dO, dtype=np.float32), None
     raise ValueError(cfg.dtype)
+
+
+def make_gdn_inputs(cfg: Config, seed: int = 0):
+    """Seeded inputs of the log-linear gated DeltaNet forward for the shapes
+    of `cfg` (one query and key per head: q, k [Bt,T,H,N], v [Bt,T,H,P]).
+
+    Distributions follow gated DeltaNet practice: q and k L2-normalised per
+    token (so each I - beta k k^T is a contraction), v ~ N(0, 1), beta =
+    sigmoid(N(0, 1)), the Mamba-2 style decay of `cfg` for log alpha, and
+    lambda = softplus(N(0, 1)).  beta and log_alpha stay float32; q, k, v
+    and lambda are rounded to the configuration's storage type.  Returns a
+    dict of float32 arrays holding exactly the values the kernels see, plus
+    ``bits`` (uint16 patterns for bf16 configs, else None).
+    """
+    Bt, T, H, N, P, L = cfg.batch, cfg.seqlen, cfg.nheads, cfg.dstate, cfg.headdim, cfg.nlevels
+    f32 = np.float32
+
+    def unit(x):
+        return (x / np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))).astype(f32)
+
+    q = unit(_normal(seed, 7, (Bt, T, H, N)))
+    k = unit(_normal(seed, 8, (Bt, T, H, N)))
+    v = _normal(seed, 9, (Bt, T, H, P))
+    if cfg.decay == "mamba2":
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 13, 0])))
+        A_log = rng.uniform(0.0, math.log(16.0), size=(H,)).astype(f32)
+        dt = _softplus(_normal(seed, 10, (Bt, T, H)) - f32(2.0))
+        log_alpha = -(dt * np.exp(A_log)[None, None, :]).astype(f32)
+    else:
+        log_alpha = -f32(0.5) * _softplus(_normal(seed, 10, (Bt, T, H)))
+    beta = (1.0 / (1.0 + np.exp(-_normal(seed, 11, (Bt, T, H)).astype(np.float64)))).astype(f32)
+    lam = _softplus(_normal(seed, 12, (Bt, T, H, L)))
+    out = dict(log_alpha=np.ascontiguousarray(log_alpha, f32), beta=np.ascontiguousarray(beta, f32))
+    if cfg.dtype == "bf16":
+        bits = {}
+        for name, x in (("q", q), ("k", k), ("v", v), ("lam", lam)):
+            bits[name], out[name] = bf16_round(x)
+        out["bits"] = bits
+    elif cfg.dtype == "fp32":
+        for name, x in (("q", q), ("k", k), ("v", v), ("lam", lam)):
+            out[name] = np.ascontiguousarray(x, f32)
+        out["bits"] = None
+    else:
+        raise ValueError(cfg.dtype)
+    return out
