@@ -19,7 +19,9 @@ and prints its own JSON line.  --mode naive times the unfused variant: one
 whole pass per level (only that level's terms computed), summed in fp32,
 against the fused pass on the same inputs.  --mode backward times the
 backward pass (dX, dB, dC, dlog_a, dlambda for a seeded upstream gradient)
-on the same workload, and the forward + backward pair.
+on the same workload, and the forward + backward pair.  --mode gdn times
+the log-linear gated DeltaNet forward at the same sizes (one query and key
+of dimension 128 per head, values of dimension 64).
 """
 from __future__ import annotations
 
@@ -220,7 +222,7 @@ def main():
     ap.add_argument("--seg-log2", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of wall time for the CPU oracle sample (0: skip)")
-    ap.add_argument("--mode", choices=("forward", "decode", "naive", "backward"),
+    ap.add_argument("--mode", choices=("forward", "decode", "naive", "backward", "gdn"),
                     default="forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of this many MiB "
@@ -232,6 +234,8 @@ def main():
         sys.exit(2)
 
     cfg = inputs.CONFIGS[args.workload]
+    if args.mode == "gdn":
+        return main_gdn(args, cfg)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     d = inputs.make_inputs(cfg, seed=0)
     if args.mode == "decode":
@@ -499,6 +503,94 @@ def main_backward(args, cfg, t, out, ws, stream, fwd_step):
         "forward_ms": round(fwd_s * 1e3, 4),
         "fwd_plus_bwd_ms": round(pair_s * 1e3, 4),
         "fwd_plus_bwd_tokens_per_s": round(tokens / pair_s, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def gdn_algorithmic(cfg) -> dict:
+    """Compulsory bytes of the gated DeltaNet forward (q, k, v, lambda, beta,
+    log alpha read once, out written once) and the fp32 flops of its
+    chunked form per (head, chunk of 32): Q K^T and K K^T (2 C^2 N each),
+    the triangular inverse (C^3 / 3), G, U, W and Qe (C^2 and C^2 N terms),
+    and per chunk level whose bit is set, Qe Z, W Z and the update
+    (3 * 2 C N P) with P the value columns."""
+    Bt, T, H, P, N, L = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.nlevels
+    e = 2 if cfg.dtype == "bf16" else 4
+    C = 32
+    nc = T // C
+    byts = Bt * T * H * (2 * N * e + 2 * P * e + L * e + 8)
+    per_chunk = 2 * 2 * C * C * N + C ** 3 // 3 + 2 * C * C * C + 2 * 2 * C * C * N + 2 * C * C * P
+    per_level = 3 * 2 * C * N * P
+    flops = Bt * H * (nc * per_chunk + popcount_sum(nc) * per_level + nc * 2 * C * N * P)
+    return {"bytes": byts, "flops": flops}
+
+
+def main_gdn(args, cfg):
+    import torch
+
+    from ssm_scan_amd import loglin as L
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating gated DeltaNet inputs for {cfg.name}", file=sys.stderr, flush=True)
+    d = inputs.make_gdn_inputs(cfg, seed=0)
+    t = {}
+    for k in ("q", "k", "v", "lam"):
+        if cfg.dtype == "bf16":
+            t[k] = torch.from_numpy(np.ascontiguousarray(d["bits"][k]).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        else:
+            t[k] = torch.from_numpy(d[k]).to(dev)
+    t["log_alpha"] = torch.from_numpy(d["log_alpha"]).to(dev)
+    t["beta"] = torch.from_numpy(d["beta"]).to(dev)
+    del d
+    out = torch.empty_like(t["v"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        L.loglin_gdn_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["lam"], out,
+                         stream=stream)
+
+    print("[bench] gdn warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print("[bench] timed gdn steps", file=sys.stderr, flush=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_s = max(time.perf_counter() - w0, e0.elapsed_time(e1) / 1e3) / K
+    alg = gdn_algorithmic(cfg)
+    gbs = alg["bytes"] / step_s / 1e9
+    tfl = alg["flops"] / step_s / 1e12
+    res = {
+        "metric": "log-linear gated DeltaNet fwd tokens/s at T=32K, H=48",
+        "value": round(cfg.batch * cfg.seqlen / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"log-linear gated DeltaNet forward, {cfg.name} sizes",
+                   "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
+                   "key_dim": cfg.dstate, "value_dim": cfg.headdim, "chunk": 32,
+                   "nlevels": cfg.nlevels},
+        "roofline": {"bound": "hbm", "kernel": "gdn_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
+                     "alg_bytes_per_launch": alg["bytes"]},
+        "alu": {"alg_flops_per_launch": alg["flops"], "achieved": round(tfl, 3),
+                "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s (fp32 vector)",
+                "frac": round(tfl / MFMA_F32_PEAK_TFLOPS, 5)},
     }
     print(json.dumps(res), flush=True)
 

@@ -232,6 +232,37 @@ int loglin_bwd(const void* X, const void* B, const void* C,
                void* dlambda, const loglin_dims* dims, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/* ---- Log-linear gated DeltaNet forward -----------------------------------
+ *
+ * Operation (log-linear attention write-up, section "log-linear
+ * generalisation of Mamba-2 and gated DeltaNet": each model keeps its own
+ * transition and composes its attention mask with the log-linear mask):
+ * gated DeltaNet's transition A_t = alpha_t (I - beta_t k_t k_t^T) acts on
+ * every Fenwick level state, the token enters level 0 as beta_t k_t v_t^T,
+ * and o_t = sum_l lambda[t, l] S_t^(l)^T q_t.  Equivalently, per batch and
+ * head, O = (G ⊙ M^H) V with
+ *   G[t, s] = beta_s (prod_{r=s+1..t} alpha_r) q_t^T H_t ... H_{s+1} k_s,
+ *   H_r = I - beta_r k_r k_r^T,  M^H[t, s] = lambda[t, bit_length(t xor s)].
+ *
+ * dims: ngroups must equal nheads (one query and key per head); dstate N
+ * is the key dimension (16, 32, 64 or 128), headdim P the value dimension
+ * (16, 32 or 64); seqlen a multiple of 32 and at most 2^20; nlevels >=
+ * ceil(log2 seqlen) + 1.  Layouts (row-major, contiguous):
+ *   q, k      [batch, seqlen, nheads, dstate]   io dtype
+ *   v, out    [batch, seqlen, nheads, headdim]  io dtype
+ *   log_alpha [batch, seqlen, nheads]           float32 (alpha = exp)
+ *   beta      [batch, seqlen, nheads]           float32
+ *   lambda    [batch, seqlen, nheads, nlevels]  io dtype
+ * All device pointers, 16-byte aligned, owned by the caller; `out` must not
+ * alias an input.  No workspace: the chunk-level states live in registers.
+ * Accumulation is fp32; repeated calls are bit-identical.  Keys are used as
+ * given (the delta rule is stable for unit-norm keys and beta in [0, 2]).
+ * Errors as for loglin_fwd, checked on the host before any HIP call. */
+int loglin_gdn_fwd(const void* q, const void* k, const void* v,
+                   const float* log_alpha, const float* beta,
+                   const void* lambda, void* out, const loglin_dims* dims,
+                   void* stream);
+
 /* Event helpers for callers that time stages without linking HIP
  * themselves.  *event receives a hipEvent_t with timing enabled. */
 int loglin_event_create(void** event);

@@ -1,6 +1,6 @@
 """Build libloglin.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-Compiles the host C-ABI unit, the decode unit, six forward instantiation
+Compiles the host C-ABI unit, the decode and gated DeltaNet units, six forward instantiation
 units (io type x chunk) and five backward ones in parallel, then links
 ssm_scan_amd/_lib/libloglin.so.
 """
@@ -32,7 +32,8 @@ FLAGS = [
 
 def _units():
     units = [("loglin_host", os.path.join(HERE, "loglin_host.cpp"), []),
-             ("loglin_decode", os.path.join(HERE, "loglin_decode.hip"), [])]
+             ("loglin_decode", os.path.join(HERE, "loglin_decode.hip"), []),
+             ("loglin_gdn", os.path.join(HERE, "loglin_gdn.hip"), [])]
     for io in ("bf16", "f32"):
         for chunk in (16, 32, 64):
             units.append((f"loglin_inst_{io}_{chunk}",

@@ -9,6 +9,7 @@
 
 #include "loglin_bwd.hpp"
 #include "loglin_decode.hpp"
+#include "loglin_gdn.hpp"
 #include "loglin_launch.hpp"
 
 namespace {
@@ -200,6 +201,30 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   pl->off_t2 = off;
   off = round_up(off + bh * d->seqlen * sizeof(float));
   pl->bytes = off;
+  return LOGLIN_OK;
+}
+
+// Log-linear gated DeltaNet forward: one query and key per head (ngroups
+// equals nheads), chunks of GDN_C tokens, chunk levels held in registers.
+int check_gdn(const loglin_dims* d, int* ll, int* nc) {
+  if (!d) return LOGLIN_ERR_NULL;
+  if (d->reserved != 0) return LOGLIN_ERR_DIM;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->ngroups <= 0 ||
+      d->headdim <= 0 || d->dstate <= 0 || d->nlevels <= 0)
+    return LOGLIN_ERR_DIM;
+  if (d->io_dtype != LOGLIN_F32 && d->io_dtype != LOGLIN_BF16) return LOGLIN_ERR_DTYPE;
+  if (d->ngroups != d->nheads) return LOGLIN_ERR_GROUPS;
+  if (d->seqlen % loglin::GDN_C) return LOGLIN_ERR_SEQ_CHUNK;
+  if (d->seqlen > (int64_t(1) << 30) || d->nheads > 4096 || d->nlevels > 64 ||
+      d->batch * d->nheads * 4 > (int64_t(1) << 30))
+    return LOGLIN_ERR_DIM;
+  const int l = ceil_log2(d->seqlen) + 1;
+  if (d->nlevels < l) return LOGLIN_ERR_LEVELS;
+  const int64_t n = d->seqlen / loglin::GDN_C;
+  if (l > loglin::GDN_LMAX || ceil_log2(n) > loglin::GDN_KMAX - 1) return LOGLIN_ERR_DIM;
+  if (!loglin::lookup_gdn(d->io_dtype, (int)d->dstate, (int)d->headdim)) return LOGLIN_ERR_SHAPE;
+  *ll = l;
+  *nc = (int)n;
   return LOGLIN_OK;
 }
 
@@ -407,6 +432,34 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   pr.npart = pl.npart;
   pr.nstate = pl.nstate;
   pr.nstate_direct = pl.nstate_direct;
+  return fn(pr, static_cast<hipStream_t>(stream)) ? LOGLIN_ERR_HIP : LOGLIN_OK;
+}
+
+int loglin_gdn_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                   const float* beta, const void* lambda, void* out, const loglin_dims* dims,
+                   void* stream) {
+  int ll = 0, nc = 0;
+  int rc = check_gdn(dims, &ll, &nc);
+  if (rc) return rc;
+  if (!q || !k || !v || !log_alpha || !beta || !lambda || !out) return LOGLIN_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_alpha) ||
+      misaligned(beta) || misaligned(lambda) || misaligned(out))
+    return LOGLIN_ERR_ALIGN;
+  loglin::GdnParams pr{};
+  pr.q = q;
+  pr.k = k;
+  pr.v = v;
+  pr.log_alpha = log_alpha;
+  pr.beta = beta;
+  pr.lam = lambda;
+  pr.out = out;
+  pr.batch = (int)dims->batch;
+  pr.seqlen = (int)dims->seqlen;
+  pr.nheads = (int)dims->nheads;
+  pr.nlevels = (int)dims->nlevels;
+  pr.ll = ll;
+  pr.nc = nc;
+  loglin::GdnFn fn = loglin::lookup_gdn(dims->io_dtype, (int)dims->dstate, (int)dims->headdim);
   return fn(pr, static_cast<hipStream_t>(stream)) ? LOGLIN_ERR_HIP : LOGLIN_OK;
 }
 

@@ -202,3 +202,21 @@ def test_decode_null_and_misaligned(name):
         assert decode_step(decode_dims(), ptrs={name: FAKE + 4}) == -9
     assert decode_step(decode_dims(), state=None) == -1
     assert decode_step(decode_dims(), state=FAKE + 64) == -9
+
+
+def test_gdn_argument_errors():
+    """loglin_gdn_fwd rejects bad dims on the host (no GPU needed)."""
+    import ctypes
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x10000)
+    def call(dims, ptr=fake):
+        return lib.loglin_gdn_fwd(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ctypes.byref(dims), None)
+    ok = L.make_dims(1, 64, 2, 2, 64, 128, 7, L.LOGLIN_BF16)
+    assert call(L.make_dims(1, 64, 2, 1, 64, 128, 7, L.LOGLIN_BF16)) == -5  # ngroups != nheads
+    assert call(L.make_dims(1, 48, 2, 2, 64, 128, 7, L.LOGLIN_BF16)) == -4  # T % 32
+    assert call(L.make_dims(1, 64, 2, 2, 64, 128, 6, L.LOGLIN_BF16)) == -6  # too few levels
+    assert call(L.make_dims(1, 64, 2, 2, 48, 128, 7, L.LOGLIN_BF16)) == -10  # headdim
+    assert call(L.make_dims(1, 64, 2, 2, 64, 96, 7, L.LOGLIN_BF16)) == -10  # dstate
+    assert call(L.make_dims(1, 64, 2, 2, 64, 128, 7, 5)) == -7  # dtype
+    assert call(ok, ptr=None) == -1
+    assert call(ok, ptr=ctypes.c_void_p(0x10004)) == -9  # alignment
