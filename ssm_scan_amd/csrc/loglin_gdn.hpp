@@ -24,8 +24,11 @@
 //
 // One work-group per (batch, head, 16 value columns): the columns of a
 // delta-rule state evolve independently.  It walks the chunks in order with
-// the chunk-level states in registers (thread-owned slices of N x 16).
-// The per-chunk algebra is plain fp32 on LDS tiles.
+// the chunk-level states in registers, in the layout the state update's
+// MFMA leaves them.  Every product of the chunk is a v_mfma_f32_16x16x4f32
+// tile over XOR-swizzled fp32 LDS tiles (fp32 keeps the delta rule's
+// corrections exact to fp32); the triangular inverse is blocked (8 -> 16 ->
+// 32) so that every thread takes part.
 #pragma once
 
 #include "loglin_device.hpp"
@@ -45,28 +48,37 @@ struct GdnParams {
 
 constexpr int GDN_C = 32;     // tokens per chunk
 constexpr int GDN_PB = 16;    // value columns per work-group
-constexpr int GDN_NT = 256;   // threads per work-group
+constexpr int GDN_NT = 256;   // threads per work-group (4 waves)
 constexpr int GDN_KMAX = 16;  // chunk levels 1..GDN_KMAX-1 held in registers
 constexpr int GDN_LMAX = 32;  // token levels per lambda row
 
 template <class T, int N, int P>
 __global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
+  using M = Mfma<float>;  // 16x16x4 fp32: A row r / B column r, contraction element g
   constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_NT, c_log = 5;
-  static_assert((1 << c_log) == C, "chunk");
-  constexpr int NS = N + 1;            // padded row stride: rows read across lanes
-  constexpr int EPT = N * PB / NT;     // state elements per thread
-  constexpr int TPR = PB / EPT;        // threads per state row
-  static_assert(EPT >= 1 && PB % EPT == 0 && P % PB == 0, "state slicing");
-  __shared__ float qs[C][NS];  // q, then the effective queries Qe
-  __shared__ float ks[C][NS];
-  __shared__ float wm[C][NS];
-  __shared__ float vs[C][PB];
-  __shared__ float am[C][C + 1], lm[C][C + 1], tm[C][C + 1], gm[C][C + 1];
-  __shared__ float um[C][PB], os[C][PB];
-  __shared__ float xy[2 * C][PB];
-  __shared__ float zs[N][PB];
+  static_assert((1 << c_log) == C && PB == 16 && N % 16 == 0 && P % PB == 0, "tile shapes");
+  constexpr int NTILE = N / 16;         // 16-row blocks of a state
+  constexpr int NTW = (NTILE + 3) / 4;  // of them per wave (waves past NTILE own none)
+  using LN = Rows<float, N>;
+  using LC = Rows<float, C>;
+  using LP = Rows<float, PB>;
+  __shared__ __attribute__((aligned(16))) float qf[C * N];  // q, then Qe
+  __shared__ __attribute__((aligned(16))) float kf[C * N];
+  __shared__ __attribute__((aligned(16))) float wf[C * N];
+  __shared__ __attribute__((aligned(16))) float am[C * C];  // tril(Q K^T ⊙ Gamma)
+  __shared__ __attribute__((aligned(16))) float lm[C * C];  // L
+  __shared__ __attribute__((aligned(16))) float tm[C * C];  // Th = (I + L)^-1
+  __shared__ __attribute__((aligned(16))) float gm[C * C];  // G
+  __shared__ __attribute__((aligned(16))) float gl[C * C];  // G ⊙ lambda by level
+  __shared__ __attribute__((aligned(16))) float pt[C * C];  // block-inverse temporary
+  __shared__ __attribute__((aligned(16))) float vf[C * PB];
+  __shared__ __attribute__((aligned(16))) float vb[C * PB];  // diag(beta) V
+  __shared__ __attribute__((aligned(16))) float us[C * PB];  // U
+  __shared__ __attribute__((aligned(16))) float ys[C * PB];  // W Z of one level
+  __shared__ __attribute__((aligned(16))) float os[C * PB];  // outputs of the chunk
+  __shared__ __attribute__((aligned(16))) float zs[N * PB];  // one level state
   __shared__ float lam_s[C][GDN_LMAX];
-  __shared__ float cum[C], gam[C], bet[C], khs[C];
+  __shared__ float cum[C], gam[C], bet[C], khs[C], bg[C];
 
   const int nblk = P / PB;
   const int wg = blockIdx.x;
@@ -74,32 +86,30 @@ __global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
   const int H = pr.nheads, L = pr.nlevels, ll = pr.ll;
   const int b = bh / H, h = bh % H, p0 = pblk * PB;
   const int64_t T_ = pr.seqlen;
-  const int tid = threadIdx.x;
-  const int zn = tid / TPR, zp = (tid % TPR) * EPT;  // this thread's state slice
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const T* qg = static_cast<const T*>(pr.q);
   const T* kg = static_cast<const T*>(pr.k);
   const T* vg = static_cast<const T*>(pr.v);
   const T* lg = static_cast<const T*>(pr.lam);
   T* og = static_cast<T*>(pr.out);
 
-  float Z[GDN_KMAX][EPT];  // chunk-level states (index = level; 0 unused)
+  // chunk-level states: wave w owns rows [16 (NTW w + u), +16) of N, all 16
+  // columns, as MFMA result tiles (lane: rows 4 g + i, column r)
+  f32x4 Z[GDN_KMAX][NTW];
 #pragma unroll
   for (int m = 0; m < GDN_KMAX; ++m)
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) Z[m][e] = 0.f;
+    for (int u = 0; u < NTW; ++u) Z[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int j = 0; j < pr.nc; ++j) {
     const int64_t t0 = (int64_t)j * C;
-    // ---- this chunk's rows
+    // ---- this chunk's rows (fp32 in LDS)
     for (int i = tid; i < C * N; i += NT) {
       const int t = i / N, n = i % N;
       const int64_t row = ((int64_t)b * T_ + t0 + t) * H + h;
-      qs[t][n] = to_f(qg[row * N + n]);
-      ks[t][n] = to_f(kg[row * N + n]);
-    }
-    for (int i = tid; i < C * PB; i += NT) {
-      const int t = i / PB, p = i % PB;
-      vs[t][p] = to_f(vg[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p]);
+      qf[LN::at(t, n)] = to_f(qg[row * N + n]);
+      kf[LN::at(t, n)] = to_f(kg[row * N + n]);
     }
     for (int i = tid; i < C * ll; i += NT) {
       const int t = i / ll, l = i % ll;
@@ -113,131 +123,221 @@ __global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
         const float o = __shfl_up(x, d, 64);
         if (tid >= d) x += o;
       }
+      const float tot = __shfl(x, C - 1, 64);
       if (tid < C) {
+        const float be = pr.beta[gi];
         cum[tid] = x;
         gam[tid] = expf(x);
-        bet[tid] = pr.beta[gi];
+        bet[tid] = be;
+        bg[tid] = be * expf(x);
+        khs[tid] = expf(tot - x);  // gamma_C / gamma_t
       }
     }
     __syncthreads();
-    if (tid < C) khs[tid] = expf(cum[C - 1] - cum[tid]);  // gamma_C / gamma_t
-    // ---- tril(Q K^T ⊙ Gamma) and L = strictly lower diag(beta)(K K^T ⊙ Gamma)
-    for (int i = tid; i < C * C; i += NT) {
-      const int t = i / C, s = i % C;
-      float a = 0.f, l = 0.f;
-      if (s <= t) {
-        float dq = 0.f, dk = 0.f;
-        for (int n = 0; n < N; ++n) {
-          dq += qs[t][n] * ks[s][n];
-          dk += ks[t][n] * ks[s][n];
-        }
-        const float g = expf(cum[t] - cum[s]);
-        a = dq * g;
-        if (s < t) l = bet[t] * dk * g;
-      }
-      am[t][s] = a;
-      lm[t][s] = l;
-    }
-    __syncthreads();
-    // ---- Th = (I + L)^{-1}, one column per thread, forward substitution
-    if (tid < C) {
-      const int jc = tid;
-      for (int i = 0; i < C; ++i) {
-        float x = i == jc ? 1.f : 0.f;
-        if (i > jc)
-          for (int m = jc; m < i; ++m) x -= lm[i][m] * tm[m][jc];
-        tm[i][jc] = x;
-      }
-    }
-    __syncthreads();
-    // ---- G = tril(Q K^T ⊙ Gamma) Th diag(beta), U = Th diag(beta) V,
-    //      W = Th diag(beta gamma) K
-    for (int i = tid; i < C * C; i += NT) {
-      const int t = i / C, s = i % C;
-      float g = 0.f;
-      if (s <= t) {
-        for (int m = s; m <= t; ++m) g += am[t][m] * tm[m][s];
-        g *= bet[s];
-      }
-      gm[t][s] = g;
-    }
-    for (int i = tid; i < C * PB; i += NT) {
-      const int r = i / PB, p = i % PB;
-      float u = 0.f;
-      for (int s = 0; s <= r; ++s) u += tm[r][s] * bet[s] * vs[s][p];
-      um[r][p] = u;
-    }
-    for (int i = tid; i < C * N; i += NT) {
-      const int r = i / N, n = i % N;
-      float w = 0.f;
-      for (int s = 0; s <= r; ++s) w += tm[r][s] * (bet[s] * gam[s]) * ks[s][n];
-      wm[r][n] = w;
-    }
-    __syncthreads();
-    // ---- Qe = diag(gamma) Q - G diag(gamma) K (in place), intra outputs
-    for (int i = tid; i < C * N; i += NT) {
-      const int t = i / N, n = i % N;
-      float x = gam[t] * qs[t][n];
-      for (int s = 0; s <= t; ++s) x -= gm[t][s] * gam[s] * ks[s][n];
-      qs[t][n] = x;
-    }
     for (int i = tid; i < C * PB; i += NT) {
       const int t = i / PB, p = i % PB;
-      float o = 0.f;
-      for (int s = 0; s <= t; ++s) o += gm[t][s] * lam_s[t][bit_length((unsigned)(t ^ s))] * vs[s][p];
-      os[t][p] = o;
+      const float x = to_f(vg[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p]);
+      vf[LP::at(t, p)] = x;
+      vb[LP::at(t, p)] = bet[t] * x;
+    }
+    // ---- Q K^T and K K^T, masked: wave w owns the 16x16 tile (w >> 1, w & 1)
+    {
+      const int tb = wave >> 1, sb = wave & 1;
+      f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+      if (sb <= tb) {
+#pragma unroll 8
+        for (int n0 = 0; n0 < N; n0 += 4) {
+          const float bk = frag_along<float, LN>(kf, 16 * sb + r, n0, g);
+          sq = M::mma(frag_along<float, LN>(qf, 16 * tb + r, n0, g), bk, sq);
+          sk = M::mma(frag_along<float, LN>(kf, 16 * tb + r, n0, g), bk, sk);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+        const float gr = s <= t ? expf(cum[t] - cum[s]) : 0.f;
+        am[LC::at(t, s)] = sq[i] * gr;
+        lm[LC::at(t, s)] = s < t ? bet[t] * sk[i] * gr : 0.f;
+      }
+    }
+    __syncthreads();
+    // ---- Th = (I + L)^-1, blocked: 8x8 diagonal blocks by substitution,
+    // then [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1, D^-1]] at 16, 32
+    if (tid < C) {
+      const int jc = tid, blk = jc & ~7;
+      for (int i = 0; i < C; ++i) {
+        float x = 0.f;
+        if (i == jc) {
+          x = 1.f;
+        } else if (i > jc && i < blk + 8) {
+          for (int m = jc; m < i; ++m) x -= lm[LC::at(i, m)] * tm[LC::at(m, jc)];
+        }
+        tm[LC::at(i, jc)] = x;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 8; hb < C; hb *= 2) {  // half block size: 8, then 16
+      const int cnt = (C / (2 * hb)) * hb * hb;
+      // pt = B A^-1 for every 2 hb block (rows in its lower half, columns in its upper)
+      for (int i = tid; i < cnt; i += NT) {
+        const int blk = i / (hb * hb), e = i % (hb * hb);
+        const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
+        float x = 0.f;
+        for (int m = col; m < blk * 2 * hb + hb; ++m) x += lm[LC::at(row, m)] * tm[LC::at(m, col)];
+        pt[LC::at(row, col)] = x;
+      }
+      __syncthreads();
+      for (int i = tid; i < cnt; i += NT) {  // the lower-left block: -D^-1 (B A^-1)
+        const int blk = i / (hb * hb), e = i % (hb * hb);
+        const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
+        float x = 0.f;
+        for (int m = blk * 2 * hb + hb; m <= row; ++m) x -= tm[LC::at(row, m)] * pt[LC::at(m, col)];
+        tm[LC::at(row, col)] = x;
+      }
+      __syncthreads();
+    }
+    // ---- G = tril(Q K^T ⊙ Gamma) Th diag(beta) (and G ⊙ lambda),
+    //      U = Th diag(beta) V
+    {
+      const int tb = wave >> 1, sb = wave & 1;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m0 = 0; m0 < C; m0 += 4)
+        acc = M::mma(frag_along<float, LC>(am, 16 * tb + r, m0, g),
+                     frag_down<float, LC>(tm, m0, 16 * sb, g, r), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+        const float gv = s <= t ? acc[i] * bet[s] : 0.f;
+        gm[LC::at(t, s)] = gv;
+        gl[LC::at(t, s)] = s <= t ? gv * lam_s[t][bit_length((unsigned)(t ^ s))] : 0.f;
+      }
+      if (wave < 2) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < C; s0 += 4)
+          u = M::mma(frag_along<float, LC>(tm, 16 * wave + r, s0, g),
+                     frag_down<float, LP>(vb, s0, 0, g, r), u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) us[LP::at(16 * wave + 4 * g + i, r)] = u[i];
+      }
+    }
+    // ---- W = Th diag(beta gamma) K: wave w owns row tile w & 1 and every
+    //      other column tile of N, starting at w >> 1
+    {
+      const int tb = wave & 1;
+#pragma unroll
+      for (int cb = (wave >> 1); cb < NTILE; cb += 2) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < C; s0 += 4)
+          acc = M::mma(frag_along<float, LC>(tm, 16 * tb + r, s0, g) * bg[s0 + g],
+                       frag_down<float, LN>(kf, s0, 16 * cb, g, r), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[LN::at(16 * tb + 4 * g + i, 16 * cb + r)] = acc[i];
+      }
+    }
+    __syncthreads();  // gm, gl, us, wf are complete
+    // ---- Qe = diag(gamma) Q - G diag(gamma) K (in place), intra outputs
+    {
+      const int tb = wave & 1;
+#pragma unroll
+      for (int cb = (wave >> 1); cb < NTILE; cb += 2) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < C; s0 += 4)
+          acc = M::mma(frag_along<float, LC>(gm, 16 * tb + r, s0, g) * gam[s0 + g],
+                       frag_down<float, LN>(kf, s0, 16 * cb, g, r), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tb + 4 * g + i, n = 16 * cb + r;
+          qf[LN::at(t, n)] = gam[t] * qf[LN::at(t, n)] - acc[i];
+        }
+      }
+      if (wave < 2) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < C; s0 += 4)
+          o = M::mma(frag_along<float, LC>(gl, 16 * wave + r, s0, g),
+                     frag_down<float, LP>(vf, s0, 0, g, r), o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) os[LP::at(16 * wave + 4 * g + i, r)] = o[i];
+      }
     }
     __syncthreads();
     // ---- chunk levels whose bit is set in j: outputs, then propagation.
-    // The loop body is large, so it is not unrolled; the level's state is
-    // moved in and out of zc through uniform branches with constant indices
-    // (a runtime index into Z would move Z to scratch memory).
+    // The body is not unrolled; the level's state moves in and out of zc
+    // through uniform branches with constant indices (a runtime index into
+    // Z would move Z to scratch memory).
     const float gC = gam[C - 1];
     for (unsigned act = (unsigned)j; act; act &= act - 1u) {
       const int m = __builtin_ctz(act) + 1;  // uniform
-      float zc[EPT];
+      f32x4 zc[NTW];
 #pragma unroll
       for (int m2 = 1; m2 < GDN_KMAX; ++m2)
         if (m2 == m) {
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) zc[e] = Z[m2][e];
+          for (int u = 0; u < NTW; ++u) zc[u] = Z[m2][u];
         }
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) zs[zn][zp + e] = zc[e];
-      __syncthreads();
-      for (int i = tid; i < 2 * C * PB; i += NT) {  // Qe Z (rows < C), W Z (rows >= C)
-        const int r = i / PB, p = i % PB;
-        const float* a = r < C ? qs[r] : wm[r - C];
-        float x = 0.f;
-        for (int n = 0; n < N; ++n) x += a[n] * zs[n][p];
-        xy[r][p] = x;
-      }
-      __syncthreads();
-      for (int i = tid; i < C * PB; i += NT) {
-        const int t = i / PB, p = i % PB;
-        os[t][p] += lam_s[t][c_log + m] * xy[t][p];
-      }
+      for (int u = 0; u < NTW; ++u)
+        if (NTW * wave + u < NTILE) {
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        float acc = gC * zc[e];
-        for (int r = 0; r < C; ++r) acc -= khs[r] * ks[r][zn] * xy[C + r][zp + e];
-        zc[e] = acc;
+          for (int i = 0; i < 4; ++i) zs[LP::at(16 * (NTW * wave + u) + 4 * g + i, r)] = zc[u][i];
+        }
+      __syncthreads();
+      {  // waves 0, 1: Qe Z (outputs); waves 2, 3: W Z
+        const float* a = wave < 2 ? qf : wf;
+        const int rb = wave & 1;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int n0 = 0; n0 < N; n0 += 4)
+          acc = M::mma(frag_along<float, LN>(a, 16 * rb + r, n0, g),
+                       frag_down<float, LP>(zs, n0, 0, g, r), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * rb + 4 * g + i;
+          if (wave < 2)
+            os[LP::at(t, r)] += lam_s[t][c_log + m] * acc[i];
+          else
+            ys[LP::at(t, r)] = acc[i];
+        }
+      }
+      __syncthreads();
+      // Z <- gamma_C Z - Kh^T (W Z)
+#pragma unroll
+      for (int u = 0; u < NTW; ++u) {
+        const int nb = NTW * wave + u;
+        if (nb >= NTILE) continue;  // uniform
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j0 = 0; j0 < C; j0 += 4)
+          acc = M::mma(frag_down<float, LN>(kf, j0, 16 * nb, g, r) * khs[j0 + g],
+                       frag_down<float, LP>(ys, j0, 0, g, r), acc);
+        zc[u] = gC * zc[u] - acc;
       }
 #pragma unroll
       for (int m2 = 1; m2 < GDN_KMAX; ++m2)
         if (m2 == m) {
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) Z[m2][e] = zc[e];
+          for (int u = 0; u < NTW; ++u) Z[m2][u] = zc[u];
         }
-      __syncthreads();  // zs and xy are reused by the next level
+      __syncthreads();  // zs and ys are reused by the next level
     }
-    // ---- the chunk's own tokens, then the Fenwick merge for chunk j + 1
-    float own[EPT];
+    // ---- the chunk's own tokens (Kh^T U), then the Fenwick merge for j + 1
+    f32x4 own[NTW];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      float acc = 0.f;
-      for (int r = 0; r < C; ++r) acc += khs[r] * ks[r][zn] * um[r][zp + e];
-      own[e] = acc;
+    for (int u = 0; u < NTW; ++u) {
+      const int nb = NTW * wave + u;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (nb < NTILE) {  // uniform
+#pragma unroll
+        for (int j0 = 0; j0 < C; j0 += 4)
+          acc = M::mma(frag_down<float, LN>(kf, j0, 16 * nb, g, r) * khs[j0 + g],
+                       frag_down<float, LP>(us, j0, 0, g, r), acc);
+      }
+      own[u] = acc;
     }
     if (j + 1 < pr.nc) {
       const int z = __builtin_ctz((unsigned)(j + 1));
@@ -245,21 +345,21 @@ __global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
       for (int m = 1; m < GDN_KMAX; ++m)
         if (m <= z) {
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) {
-            own[e] += Z[m][e];
-            Z[m][e] = 0.f;
+          for (int u = 0; u < NTW; ++u) {
+            own[u] += Z[m][u];
+            Z[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
         }
 #pragma unroll
       for (int m = 1; m < GDN_KMAX; ++m)
         if (m == z + 1) {
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) Z[m][e] = own[e];
+          for (int u = 0; u < NTW; ++u) Z[m][u] = own[u];
         }
     }
     for (int i = tid; i < C * PB; i += NT) {
       const int t = i / PB, p = i % PB;
-      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[t][p]);
+      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[LP::at(t, p)]);
     }
     __syncthreads();  // the next chunk restages every tile
   }
