@@ -546,10 +546,12 @@ def main_gdn(args, cfg):
     del d
     out = torch.empty_like(t["v"])
     stream = torch.cuda.current_stream(dev)
+    ws = torch.empty(L.loglin_gdn_workspace_bytes(L.gdn_dims(t["q"], t["v"], t["lam"])),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         L.loglin_gdn_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["lam"], out,
-                         stream=stream)
+                         workspace=ws, stream=stream)
 
     print("[bench] gdn warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

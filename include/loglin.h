@@ -254,14 +254,20 @@ int loglin_bwd(const void* X, const void* B, const void* C,
  *   beta      [batch, seqlen, nheads]           float32
  *   lambda    [batch, seqlen, nheads, nlevels]  io dtype
  * All device pointers, 16-byte aligned, owned by the caller; `out` must not
- * alias an input.  No workspace: the chunk-level states live in registers.
- * Accumulation is fp32; repeated calls are bit-identical.  Keys are used as
- * given (the delta rule is stable for unit-norm keys and beta in [0, 2]).
- * Errors as for loglin_fwd, checked on the host before any HIP call. */
+ * alias an input.  The workspace (at least loglin_gdn_workspace_bytes
+ * bytes, 256-byte aligned, contents ignored on entry; about 48 KB per
+ * head and 32 tokens at key dim 128, value dim 64) holds the per-chunk
+ * operands between the chunk-parallel pass and the level pass and must not
+ * be used by other work until the call's kernels finish.  Accumulation is
+ * fp32; repeated calls are bit-identical.  Keys are used as given (the
+ * delta rule is stable for unit-norm keys and beta in [0, 2]).  Errors as
+ * for loglin_fwd, checked on the host before any HIP call. */
+size_t loglin_gdn_workspace_bytes(const loglin_dims* dims);
+
 int loglin_gdn_fwd(const void* q, const void* k, const void* v,
                    const float* log_alpha, const float* beta,
                    const void* lambda, void* out, const loglin_dims* dims,
-                   void* stream);
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Event helpers for callers that time stages without linking HIP
  * themselves.  *event receives a hipEvent_t with timing enabled. */

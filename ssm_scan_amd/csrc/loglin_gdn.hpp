@@ -22,13 +22,19 @@
 // m holds the chunks i with bit_length(j xor i) = m for the current chunk
 // j, token level c + m), each level's state propagated like S above.
 //
-// One work-group per (batch, head, 16 value columns): the columns of a
-// delta-rule state evolve independently.  It walks the chunks in order with
-// the chunk-level states in registers, in the layout the state update's
-// MFMA leaves them.  Every product of the chunk is a v_mfma_f32_16x16x4f32
-// tile over XOR-swizzled fp32 LDS tiles (fp32 keeps the delta rule's
-// corrections exact to fp32); the triangular inverse is blocked (8 -> 16 ->
-// 32) so that every thread takes part.
+// Two passes.  gdn_chunk_kernel, one work-group per (batch, head, chunk),
+// all chunks at once: T^, G, U, W, Qe and the intra-chunk outputs, to the
+// workspace in fp32.  gdn_scan_kernel, one work-group per (batch, head, 16
+// value columns; the columns of a delta-rule state evolve independently),
+// walks the chunks in order with the chunk-level states in registers (in
+// the layout the state update's MFMA leaves them), reads each chunk's Qe,
+// W, K, U and intra outputs (loaded into registers one chunk ahead), adds
+// the level terms and writes the outputs.  Its barriers wait for LDS
+// traffic only (lds_barrier): __syncthreads() would also wait for the
+// next chunk's loads in flight.  Every product is a
+// v_mfma_f32_16x16x4f32 tile over XOR-swizzled fp32 LDS tiles (fp32 keeps
+// the delta rule's corrections exact to fp32); the triangular inverse is
+// blocked (8 -> 16 -> 32) so that every thread takes part.
 #pragma once
 
 #include "loglin_device.hpp"
@@ -43,55 +49,291 @@ struct GdnParams {
   const float* beta;
   const void* lam;
   void* out;
+  float* qe;  // [batch*nheads*nc, C, N]  effective queries
+  float* w;   // [batch*nheads*nc, C, N]  W
+  float* u;   // [batch*nheads*nc, C, P]  U
+  float* oi;  // [batch*nheads*nc, C, P]  intra-chunk outputs
+  float* kh;  // [batch*nheads*nc, C]     gamma_C / gamma_t
+  float* gc;  // [batch*nheads*nc]        gamma_C
   int batch, seqlen, nheads, nlevels, ll, nc;
 };
 
 constexpr int GDN_C = 32;     // tokens per chunk
-constexpr int GDN_PB = 16;    // value columns per work-group
+constexpr int GDN_PB = 16;    // value columns per work-group of the scan
 constexpr int GDN_NT = 256;   // threads per work-group (4 waves)
 constexpr int GDN_KMAX = 16;  // chunk levels 1..GDN_KMAX-1 held in registers
 constexpr int GDN_LMAX = 32;  // token levels per lambda row
+constexpr int GDN_LB = 4;     // chunk levels the level pass handles per batch
+
+// ------------------------------------------------------------ pass 1
 
 template <class T, int N, int P>
-__global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
+__global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
   using M = Mfma<float>;  // 16x16x4 fp32: A row r / B column r, contraction element g
-  constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_NT, c_log = 5;
-  static_assert((1 << c_log) == C && PB == 16 && N % 16 == 0 && P % PB == 0, "tile shapes");
-  constexpr int NTILE = N / 16;         // 16-row blocks of a state
-  constexpr int NTW = (NTILE + 3) / 4;  // of them per wave (waves past NTILE own none)
+  constexpr int C = GDN_C, NT = GDN_NT, c_log = 5;
+  static_assert((1 << c_log) == C && N % 16 == 0 && P % 16 == 0, "tile shapes");
+  constexpr int NTILE = N / 16, PT = P / 16;
   using LN = Rows<float, N>;
   using LC = Rows<float, C>;
-  using LP = Rows<float, PB>;
-  __shared__ __attribute__((aligned(16))) float qf[C * N];  // q, then Qe
+  using LV = Rows<float, P>;
+  __shared__ __attribute__((aligned(16))) float qf[C * N];
   __shared__ __attribute__((aligned(16))) float kf[C * N];
-  __shared__ __attribute__((aligned(16))) float wf[C * N];
   __shared__ __attribute__((aligned(16))) float am[C * C];  // tril(Q K^T ⊙ Gamma)
   __shared__ __attribute__((aligned(16))) float lm[C * C];  // L
   __shared__ __attribute__((aligned(16))) float tm[C * C];  // Th = (I + L)^-1
   __shared__ __attribute__((aligned(16))) float gm[C * C];  // G
   __shared__ __attribute__((aligned(16))) float gl[C * C];  // G ⊙ lambda by level
   __shared__ __attribute__((aligned(16))) float pt[C * C];  // block-inverse temporary
-  __shared__ __attribute__((aligned(16))) float vf[C * PB];
-  __shared__ __attribute__((aligned(16))) float vb[C * PB];  // diag(beta) V
-  __shared__ __attribute__((aligned(16))) float us[C * PB];  // U
-  __shared__ __attribute__((aligned(16))) float ys[C * PB];  // W Z of one level
-  __shared__ __attribute__((aligned(16))) float os[C * PB];  // outputs of the chunk
-  __shared__ __attribute__((aligned(16))) float zs[N * PB];  // one level state
-  __shared__ float lam_s[C][GDN_LMAX];
-  __shared__ float cum[C], gam[C], bet[C], khs[C], bg[C];
+  __shared__ __attribute__((aligned(16))) float vf[C * P];
+  __shared__ __attribute__((aligned(16))) float vb[C * P];  // diag(beta) V
+  __shared__ float lam_s[C][8];                              // intra-chunk levels 0..c
+  __shared__ float cum[C], gam[C], bet[C], bg[C];
 
-  const int nblk = P / PB;
-  const int wg = blockIdx.x;
-  const int pblk = wg % nblk, bh = wg / nblk;
-  const int H = pr.nheads, L = pr.nlevels, ll = pr.ll;
-  const int b = bh / H, h = bh % H, p0 = pblk * PB;
-  const int64_t T_ = pr.seqlen;
+  const int item = blockIdx.x;  // (batch*head) * nc + chunk
+  const int bh = item / pr.nc, j = item % pr.nc;
+  const int H = pr.nheads, L = pr.nlevels;
+  const int b = bh / H, h = bh % H;
+  const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const T* qg = static_cast<const T*>(pr.q);
   const T* kg = static_cast<const T*>(pr.k);
   const T* vg = static_cast<const T*>(pr.v);
   const T* lg = static_cast<const T*>(pr.lam);
+
+  for (int i = tid; i < C * N; i += NT) {
+    const int t = i / N, n = i % N;
+    const int64_t row = ((int64_t)b * T_ + t0 + t) * H + h;
+    qf[LN::at(t, n)] = to_f(qg[row * N + n]);
+    kf[LN::at(t, n)] = to_f(kg[row * N + n]);
+  }
+  for (int i = tid; i < C * (c_log + 1); i += NT) {
+    const int t = i / (c_log + 1), l = i % (c_log + 1);
+    lam_s[t][l] = to_f(lg[(((int64_t)b * T_ + t0 + t) * H + h) * L + l]);
+  }
+  if (tid < 64) {  // inclusive cumulative log alpha over the chunk
+    const int64_t gi = ((int64_t)b * T_ + t0 + (tid < C ? tid : 0)) * H + h;
+    float x = tid < C ? pr.log_alpha[gi] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(x, d, 64);
+      if (tid >= d) x += o;
+    }
+    const float tot = __shfl(x, C - 1, 64);
+    if (tid < C) {
+      const float be = pr.beta[gi];
+      cum[tid] = x;
+      gam[tid] = expf(x);
+      bet[tid] = be;
+      bg[tid] = be * expf(x);
+      pr.kh[(int64_t)item * C + tid] = expf(tot - x);  // gamma_C / gamma_t
+      if (tid == 0) pr.gc[item] = expf(tot);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < C * P; i += NT) {
+    const int t = i / P, p = i % P;
+    const float x = to_f(vg[(((int64_t)b * T_ + t0 + t) * H + h) * P + p]);
+    vf[LV::at(t, p)] = x;
+    vb[LV::at(t, p)] = bet[t] * x;
+  }
+  // ---- Q K^T and K K^T, masked: wave w owns the 16x16 tile (w >> 1, w & 1)
+  {
+    const int tb = wave >> 1, sb = wave & 1;
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+    if (sb <= tb) {
+#pragma unroll 8
+      for (int n0 = 0; n0 < N; n0 += 4) {
+        const float bk = frag_along<float, LN>(kf, 16 * sb + r, n0, g);
+        sq = M::mma(frag_along<float, LN>(qf, 16 * tb + r, n0, g), bk, sq);
+        sk = M::mma(frag_along<float, LN>(kf, 16 * tb + r, n0, g), bk, sk);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+      const float gr = s <= t ? expf(cum[t] - cum[s]) : 0.f;
+      am[LC::at(t, s)] = sq[i] * gr;
+      lm[LC::at(t, s)] = s < t ? bet[t] * sk[i] * gr : 0.f;
+    }
+  }
+  __syncthreads();
+  // ---- Th = (I + L)^-1, blocked: 8x8 diagonal blocks by substitution,
+  // then [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1, D^-1]] at 16, 32
+  if (tid < C) {
+    const int jc = tid, blk = jc & ~7;
+    for (int i = 0; i < C; ++i) {
+      float x = 0.f;
+      if (i == jc) {
+        x = 1.f;
+      } else if (i > jc && i < blk + 8) {
+        for (int m = jc; m < i; ++m) x -= lm[LC::at(i, m)] * tm[LC::at(m, jc)];
+      }
+      tm[LC::at(i, jc)] = x;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb = 8; hb < C; hb *= 2) {  // half block size: 8, then 16
+    const int cnt = (C / (2 * hb)) * hb * hb;
+    for (int i = tid; i < cnt; i += NT) {  // B A^-1 (rows in the lower half, columns in the upper)
+      const int blk = i / (hb * hb), e = i % (hb * hb);
+      const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
+      float x = 0.f;
+      for (int m = col; m < blk * 2 * hb + hb; ++m) x += lm[LC::at(row, m)] * tm[LC::at(m, col)];
+      pt[LC::at(row, col)] = x;
+    }
+    __syncthreads();
+    for (int i = tid; i < cnt; i += NT) {  // the lower-left block: -D^-1 (B A^-1)
+      const int blk = i / (hb * hb), e = i % (hb * hb);
+      const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
+      float x = 0.f;
+      for (int m = blk * 2 * hb + hb; m <= row; ++m) x -= tm[LC::at(row, m)] * pt[LC::at(m, col)];
+      tm[LC::at(row, col)] = x;
+    }
+    __syncthreads();
+  }
+  // ---- G = tril(Q K^T ⊙ Gamma) Th diag(beta) and G ⊙ lambda
+  {
+    const int tb = wave >> 1, sb = wave & 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m0 = 0; m0 < C; m0 += 4)
+      acc = M::mma(frag_along<float, LC>(am, 16 * tb + r, m0, g),
+                   frag_down<float, LC>(tm, m0, 16 * sb, g, r), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+      const float gv = s <= t ? acc[i] * bet[s] : 0.f;
+      gm[LC::at(t, s)] = gv;
+      gl[LC::at(t, s)] = s <= t ? gv * lam_s[t][bit_length((unsigned)(t ^ s))] : 0.f;
+    }
+  }
+  // ---- U = Th diag(beta) V and W = Th diag(beta gamma) K, straight to the
+  //      workspace (row tile tile & 1, column tile tile >> 1)
+  float* ug = pr.u + (int64_t)item * C * P;
+  float* wg = pr.w + (int64_t)item * C * N;
+  for (int tile = wave; tile < 2 * PT; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < C; s0 += 4)
+      acc = M::mma(frag_along<float, LC>(tm, 16 * tb + r, s0, g),
+                   frag_down<float, LV>(vb, s0, 16 * cb, g, r), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ug[(16 * tb + 4 * g + i) * P + 16 * cb + r] = acc[i];
+  }
+  for (int tile = wave; tile < 2 * NTILE; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < C; s0 += 4)
+      acc = M::mma(frag_along<float, LC>(tm, 16 * tb + r, s0, g) * bg[s0 + g],
+                   frag_down<float, LN>(kf, s0, 16 * cb, g, r), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wg[(16 * tb + 4 * g + i) * N + 16 * cb + r] = acc[i];
+  }
+  __syncthreads();  // gm and gl are complete
+  // ---- Qe = diag(gamma) Q - G diag(gamma) K and the intra outputs (G ⊙ lambda) V
+  float* qeg = pr.qe + (int64_t)item * C * N;
+  float* oig = pr.oi + (int64_t)item * C * P;
+  for (int tile = wave; tile < 2 * NTILE; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < C; s0 += 4)
+      acc = M::mma(frag_along<float, LC>(gm, 16 * tb + r, s0, g) * gam[s0 + g],
+                   frag_down<float, LN>(kf, s0, 16 * cb, g, r), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i, n = 16 * cb + r;
+      qeg[t * N + n] = gam[t] * qf[LN::at(t, n)] - acc[i];
+    }
+  }
+  for (int tile = wave; tile < 2 * PT; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < C; s0 += 4)
+      acc = M::mma(frag_along<float, LC>(gl, 16 * tb + r, s0, g),
+                   frag_down<float, LV>(vf, s0, 16 * cb, g, r), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oig[(16 * tb + 4 * g + i) * P + 16 * cb + r] = acc[i];
+  }
+}
+
+// ------------------------------------------------------------ pass 2
+
+// One chunk's operands of the level pass, loaded into registers one chunk
+// ahead and then stored to LDS: Qe, W and K (C x N), U and the intra outputs
+// for this work-group's 16 columns, gamma_C / gamma_t, and lambda rows.
+template <class T, int N, int P>
+struct GdnStage {
+  static constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_NT;
+  static constexpr int NQ4 = C * N / 4;  // float4 groups of a C x N tile
+  static constexpr int NQ = (NQ4 + NT - 1) / NT;  // per thread
+  static constexpr int NL = (C * GDN_LMAX + NT - 1) / NT;
+  f32x4 qe[NQ], w[NQ], k[NQ];
+  float u2[2], o2[2], lam[NL], khv, gcv;
+  __device__ inline void load(const GdnParams& pr, int item, int b, int h, int64_t t0, int p0, int tid) {
+    const float* qeg = pr.qe + (int64_t)item * C * N;
+    const float* wg = pr.w + (int64_t)item * C * N;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (q * NT + tid >= NQ4) break;
+      const int e = (q * NT + tid) * 4, t = e / N, n = e % N;
+      qe[q] = *reinterpret_cast<const f32x4*>(qeg + e);
+      w[q] = *reinterpret_cast<const f32x4*>(wg + e);
+      const T* kr = static_cast<const T*>(pr.k) + (((int64_t)b * pr.seqlen + t0 + t) * pr.nheads + h) * N + n;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) k[q][c] = to_f(kr[c]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {  // C x 16 = 512 values: two per thread
+      const int e = q * NT + tid, t = e / PB, p = e % PB;
+      u2[q] = pr.u[((int64_t)item * C + t) * P + p0 + p];
+      o2[q] = pr.oi[((int64_t)item * C + t) * P + p0 + p];
+    }
+    const T* lg = static_cast<const T*>(pr.lam);
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int e = q * NT + tid, t = e / GDN_LMAX, l = e % GDN_LMAX;
+      lam[q] = (t < C && l < pr.ll)
+                   ? to_f(lg[(((int64_t)b * pr.seqlen + t0 + t) * pr.nheads + h) * pr.nlevels + l])
+                   : 0.f;
+    }
+    khv = tid < C ? pr.kh[(int64_t)item * C + tid] : 0.f;
+    gcv = pr.gc[item];
+  }
+};
+
+template <class T, int N, int P>
+__global__ __launch_bounds__(GDN_NT) void gdn_scan_kernel(GdnParams pr) {
+  using M = Mfma<float>;
+  constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_NT, c_log = 5;
+  static_assert(PB == 16 && N % 16 == 0 && P % PB == 0, "tile shapes");
+  constexpr int NTILE = N / 16;         // 16-row blocks of a state
+  constexpr int NTW = (NTILE + 3) / 4;  // of them per wave (waves past NTILE own none)
+  using LN = Rows<float, N>;
+  using LP = Rows<float, PB>;
+  using St = GdnStage<T, N, P>;
+  __shared__ __attribute__((aligned(16))) float qf[C * N];  // Qe
+  __shared__ __attribute__((aligned(16))) float wf[C * N];  // W
+  __shared__ __attribute__((aligned(16))) float kf[C * N];  // K
+  __shared__ __attribute__((aligned(16))) float us[C * PB];  // U
+  __shared__ __attribute__((aligned(16))) float ys[GDN_LB * C * PB];  // W Z of a batch of levels
+  __shared__ __attribute__((aligned(16))) float os[C * PB];            // outputs of the chunk
+  __shared__ __attribute__((aligned(16))) float zs[GDN_LB * N * PB];  // a batch of level states
+  __shared__ float lam_s[C][GDN_LMAX];
+  __shared__ float khs[C];
+
+  const int nblk = P / PB;
+  const int pblk = blockIdx.x % nblk, bh = blockIdx.x / nblk;
+  const int H = pr.nheads;
+  const int b = bh / H, h = bh % H, p0 = pblk * PB;
+  const int64_t T_ = pr.seqlen;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   T* og = static_cast<T*>(pr.out);
 
   // chunk-level states: wave w owns rows [16 (NTW w + u), +16) of N, all 16
@@ -102,228 +344,115 @@ __global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
 #pragma unroll
     for (int u = 0; u < NTW; ++u) Z[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  St st;
+  st.load(pr, bh * pr.nc, b, h, 0, p0, tid);
   for (int j = 0; j < pr.nc; ++j) {
     const int64_t t0 = (int64_t)j * C;
-    // ---- this chunk's rows (fp32 in LDS)
-    for (int i = tid; i < C * N; i += NT) {
-      const int t = i / N, n = i % N;
-      const int64_t row = ((int64_t)b * T_ + t0 + t) * H + h;
-      qf[LN::at(t, n)] = to_f(qg[row * N + n]);
-      kf[LN::at(t, n)] = to_f(kg[row * N + n]);
-    }
-    for (int i = tid; i < C * ll; i += NT) {
-      const int t = i / ll, l = i % ll;
-      lam_s[t][l] = to_f(lg[(((int64_t)b * T_ + t0 + t) * H + h) * L + l]);
-    }
-    if (tid < 64) {  // inclusive cumulative log alpha over the chunk
-      const int64_t gi = ((int64_t)b * T_ + t0 + (tid < C ? tid : 0)) * H + h;
-      float x = tid < C ? pr.log_alpha[gi] : 0.f;
+    // ---- this chunk's operands into LDS, then the next chunk's loads
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(x, d, 64);
-        if (tid >= d) x += o;
-      }
-      const float tot = __shfl(x, C - 1, 64);
-      if (tid < C) {
-        const float be = pr.beta[gi];
-        cum[tid] = x;
-        gam[tid] = expf(x);
-        bet[tid] = be;
-        bg[tid] = be * expf(x);
-        khs[tid] = expf(tot - x);  // gamma_C / gamma_t
-      }
+    for (int q = 0; q < St::NQ; ++q) {
+      if (q * NT + tid >= St::NQ4) break;
+      const int e = (q * NT + tid) * 4, t = e / N, n = e % N;
+      store16(qf + LN::at(t, n), st.qe[q]);
+      store16(wf + LN::at(t, n), st.w[q]);
+      store16(kf + LN::at(t, n), st.k[q]);
     }
-    __syncthreads();
-    for (int i = tid; i < C * PB; i += NT) {
-      const int t = i / PB, p = i % PB;
-      const float x = to_f(vg[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p]);
-      vf[LP::at(t, p)] = x;
-      vb[LP::at(t, p)] = bet[t] * x;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = q * NT + tid, t = e / PB, p = e % PB;
+      us[LP::at(t, p)] = st.u2[q];
+      os[LP::at(t, p)] = st.o2[q];
     }
-    // ---- Q K^T and K K^T, masked: wave w owns the 16x16 tile (w >> 1, w & 1)
-    {
-      const int tb = wave >> 1, sb = wave & 1;
-      f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
-      if (sb <= tb) {
-#pragma unroll 8
-        for (int n0 = 0; n0 < N; n0 += 4) {
-          const float bk = frag_along<float, LN>(kf, 16 * sb + r, n0, g);
-          sq = M::mma(frag_along<float, LN>(qf, 16 * tb + r, n0, g), bk, sq);
-          sk = M::mma(frag_along<float, LN>(kf, 16 * tb + r, n0, g), bk, sk);
+#pragma unroll
+    for (int q = 0; q < St::NL; ++q) {
+      const int e = q * NT + tid;
+      if (e < C * GDN_LMAX) lam_s[e / GDN_LMAX][e % GDN_LMAX] = st.lam[q];
+    }
+    if (tid < C) khs[tid] = st.khv;
+    const float gC = st.gcv;
+    lds_barrier();
+    if (j + 1 < pr.nc) st.load(pr, bh * pr.nc + j + 1, b, h, t0 + C, p0, tid);
+
+    // ---- chunk levels whose bit is set in j, up to GDN_LB at a time (three
+    // barriers per batch): their states to LDS, then Qe Z (outputs) and W Z,
+    // then the propagation.  The body is not unrolled; a level's state moves
+    // in and out of registers through uniform branches with constant indices
+    // (a runtime index into Z would move Z to scratch memory).
+    for (unsigned act = (unsigned)j; act;) {
+      int ms[GDN_LB];
+      int nbat = 0;
+#pragma unroll
+      for (int q = 0; q < GDN_LB; ++q) {
+        ms[q] = act ? __builtin_ctz(act) + 1 : 0;  // uniform; 0: no level
+        if (act) {
+          act &= act - 1u;
+          ++nbat;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
-        const float gr = s <= t ? expf(cum[t] - cum[s]) : 0.f;
-        am[LC::at(t, s)] = sq[i] * gr;
-        lm[LC::at(t, s)] = s < t ? bet[t] * sk[i] * gr : 0.f;
+      for (int q = 0; q < GDN_LB; ++q) {
+        if (q >= nbat) break;
+#pragma unroll
+        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+          if (m2 == ms[q]) {
+#pragma unroll
+            for (int u = 0; u < NTW; ++u)
+              if (NTW * wave + u < NTILE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  zs[q * N * PB + LP::at(16 * (NTW * wave + u) + 4 * g + i, r)] = Z[m2][u][i];
+              }
+          }
       }
-    }
-    __syncthreads();
-    // ---- Th = (I + L)^-1, blocked: 8x8 diagonal blocks by substitution,
-    // then [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1, D^-1]] at 16, 32
-    if (tid < C) {
-      const int jc = tid, blk = jc & ~7;
-      for (int i = 0; i < C; ++i) {
-        float x = 0.f;
-        if (i == jc) {
-          x = 1.f;
-        } else if (i > jc && i < blk + 8) {
-          for (int m = jc; m < i; ++m) x -= lm[LC::at(i, m)] * tm[LC::at(m, jc)];
-        }
-        tm[LC::at(i, jc)] = x;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hb = 8; hb < C; hb *= 2) {  // half block size: 8, then 16
-      const int cnt = (C / (2 * hb)) * hb * hb;
-      // pt = B A^-1 for every 2 hb block (rows in its lower half, columns in its upper)
-      for (int i = tid; i < cnt; i += NT) {
-        const int blk = i / (hb * hb), e = i % (hb * hb);
-        const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
-        float x = 0.f;
-        for (int m = col; m < blk * 2 * hb + hb; ++m) x += lm[LC::at(row, m)] * tm[LC::at(m, col)];
-        pt[LC::at(row, col)] = x;
-      }
-      __syncthreads();
-      for (int i = tid; i < cnt; i += NT) {  // the lower-left block: -D^-1 (B A^-1)
-        const int blk = i / (hb * hb), e = i % (hb * hb);
-        const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
-        float x = 0.f;
-        for (int m = blk * 2 * hb + hb; m <= row; ++m) x -= tm[LC::at(row, m)] * pt[LC::at(m, col)];
-        tm[LC::at(row, col)] = x;
-      }
-      __syncthreads();
-    }
-    // ---- G = tril(Q K^T ⊙ Gamma) Th diag(beta) (and G ⊙ lambda),
-    //      U = Th diag(beta) V
-    {
-      const int tb = wave >> 1, sb = wave & 1;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m0 = 0; m0 < C; m0 += 4)
-        acc = M::mma(frag_along<float, LC>(am, 16 * tb + r, m0, g),
-                     frag_down<float, LC>(tm, m0, 16 * sb, g, r), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
-        const float gv = s <= t ? acc[i] * bet[s] : 0.f;
-        gm[LC::at(t, s)] = gv;
-        gl[LC::at(t, s)] = s <= t ? gv * lam_s[t][bit_length((unsigned)(t ^ s))] : 0.f;
-      }
-      if (wave < 2) {
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s0 = 0; s0 < C; s0 += 4)
-          u = M::mma(frag_along<float, LC>(tm, 16 * wave + r, s0, g),
-                     frag_down<float, LP>(vb, s0, 0, g, r), u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) us[LP::at(16 * wave + 4 * g + i, r)] = u[i];
-      }
-    }
-    // ---- W = Th diag(beta gamma) K: wave w owns row tile w & 1 and every
-    //      other column tile of N, starting at w >> 1
-    {
-      const int tb = wave & 1;
-#pragma unroll
-      for (int cb = (wave >> 1); cb < NTILE; cb += 2) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s0 = 0; s0 < C; s0 += 4)
-          acc = M::mma(frag_along<float, LC>(tm, 16 * tb + r, s0, g) * bg[s0 + g],
-                       frag_down<float, LN>(kf, s0, 16 * cb, g, r), acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wf[LN::at(16 * tb + 4 * g + i, 16 * cb + r)] = acc[i];
-      }
-    }
-    __syncthreads();  // gm, gl, us, wf are complete
-    // ---- Qe = diag(gamma) Q - G diag(gamma) K (in place), intra outputs
-    {
-      const int tb = wave & 1;
-#pragma unroll
-      for (int cb = (wave >> 1); cb < NTILE; cb += 2) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s0 = 0; s0 < C; s0 += 4)
-          acc = M::mma(frag_along<float, LC>(gm, 16 * tb + r, s0, g) * gam[s0 + g],
-                       frag_down<float, LN>(kf, s0, 16 * cb, g, r), acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * tb + 4 * g + i, n = 16 * cb + r;
-          qf[LN::at(t, n)] = gam[t] * qf[LN::at(t, n)] - acc[i];
-        }
-      }
-      if (wave < 2) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s0 = 0; s0 < C; s0 += 4)
-          o = M::mma(frag_along<float, LC>(gl, 16 * wave + r, s0, g),
-                     frag_down<float, LP>(vf, s0, 0, g, r), o);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) os[LP::at(16 * wave + 4 * g + i, r)] = o[i];
-      }
-    }
-    __syncthreads();
-    // ---- chunk levels whose bit is set in j: outputs, then propagation.
-    // The body is not unrolled; the level's state moves in and out of zc
-    // through uniform branches with constant indices (a runtime index into
-    // Z would move Z to scratch memory).
-    const float gC = gam[C - 1];
-    for (unsigned act = (unsigned)j; act; act &= act - 1u) {
-      const int m = __builtin_ctz(act) + 1;  // uniform
-      f32x4 zc[NTW];
-#pragma unroll
-      for (int m2 = 1; m2 < GDN_KMAX; ++m2)
-        if (m2 == m) {
-#pragma unroll
-          for (int u = 0; u < NTW; ++u) zc[u] = Z[m2][u];
-        }
-#pragma unroll
-      for (int u = 0; u < NTW; ++u)
-        if (NTW * wave + u < NTILE) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) zs[LP::at(16 * (NTW * wave + u) + 4 * g + i, r)] = zc[u][i];
-        }
-      __syncthreads();
+      lds_barrier();
       {  // waves 0, 1: Qe Z (outputs); waves 2, 3: W Z
         const float* a = wave < 2 ? qf : wf;
         const int rb = wave & 1;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int n0 = 0; n0 < N; n0 += 4)
-          acc = M::mma(frag_along<float, LN>(a, 16 * rb + r, n0, g),
-                       frag_down<float, LP>(zs, n0, 0, g, r), acc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * rb + 4 * g + i;
-          if (wave < 2)
-            os[LP::at(t, r)] += lam_s[t][c_log + m] * acc[i];
-          else
-            ys[LP::at(t, r)] = acc[i];
+        for (int q = 0; q < GDN_LB; ++q) {
+          if (q >= nbat) break;
+          const float* zq = zs + q * N * PB;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+          for (int n0 = 0; n0 < N; n0 += 4)
+            acc = M::mma(frag_along<float, LN>(a, 16 * rb + r, n0, g),
+                         frag_down<float, LP>(zq, n0, 0, g, r), acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * rb + 4 * g + i;
+            if (wave < 2)
+              os[LP::at(t, r)] += lam_s[t][c_log + ms[q]] * acc[i];
+            else
+              ys[q * C * PB + LP::at(t, r)] = acc[i];
+          }
         }
       }
-      __syncthreads();
+      lds_barrier();
       // Z <- gamma_C Z - Kh^T (W Z)
 #pragma unroll
-      for (int u = 0; u < NTW; ++u) {
-        const int nb = NTW * wave + u;
-        if (nb >= NTILE) continue;  // uniform
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < GDN_LB; ++q) {
+        if (q >= nbat) break;
+        f32x4 zc[NTW];
 #pragma unroll
-        for (int j0 = 0; j0 < C; j0 += 4)
-          acc = M::mma(frag_down<float, LN>(kf, j0, 16 * nb, g, r) * khs[j0 + g],
-                       frag_down<float, LP>(ys, j0, 0, g, r), acc);
-        zc[u] = gC * zc[u] - acc;
-      }
+        for (int u = 0; u < NTW; ++u) {
+          const int nb = NTW * wave + u;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (nb < NTILE) {  // uniform
 #pragma unroll
-      for (int m2 = 1; m2 < GDN_KMAX; ++m2)
-        if (m2 == m) {
-#pragma unroll
-          for (int u = 0; u < NTW; ++u) Z[m2][u] = zc[u];
+            for (int j0 = 0; j0 < C; j0 += 4)
+              acc = M::mma(frag_down<float, LN>(kf, j0, 16 * nb, g, r) * khs[j0 + g],
+                           frag_down<float, LP>(ys + q * C * PB, j0, 0, g, r), acc);
+          }
+          zc[u] = acc;
         }
-      __syncthreads();  // zs and ys are reused by the next level
+#pragma unroll
+        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+          if (m2 == ms[q]) {
+#pragma unroll
+            for (int u = 0; u < NTW; ++u) Z[m2][u] = gC * Z[m2][u] - zc[u];
+          }
+      }
+      lds_barrier();  // zs and ys are reused by the next batch
     }
     // ---- the chunk's own tokens (Kh^T U), then the Fenwick merge for j + 1
     f32x4 own[NTW];
@@ -361,7 +490,7 @@ __global__ __launch_bounds__(GDN_NT) void gdn_kernel(GdnParams pr) {
       const int t = i / PB, p = i % PB;
       og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[LP::at(t, p)]);
     }
-    __syncthreads();  // the next chunk restages every tile
+    lds_barrier();  // the next chunk restages every tile
   }
 }
 
@@ -369,8 +498,10 @@ using GdnFn = int (*)(const GdnParams&, hipStream_t);
 
 template <class T, int N, int P>
 int launch_gdn(const GdnParams& pr, hipStream_t st) {
+  const int items = pr.batch * pr.nheads * pr.nc;
+  hipLaunchKernelGGL((gdn_chunk_kernel<T, N, P>), dim3(items), dim3(GDN_NT), 0, st, pr);
   const int blocks = pr.batch * pr.nheads * (P / GDN_PB);
-  hipLaunchKernelGGL((gdn_kernel<T, N, P>), dim3(blocks), dim3(GDN_NT), 0, st, pr);
+  hipLaunchKernelGGL((gdn_scan_kernel<T, N, P>), dim3(blocks), dim3(GDN_NT), 0, st, pr);
   return (int)hipGetLastError();
 }
 

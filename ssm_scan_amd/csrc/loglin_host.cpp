@@ -206,6 +206,13 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
 
 // Log-linear gated DeltaNet forward: one query and key per head (ngroups
 // equals nheads), chunks of GDN_C tokens, chunk levels held in registers.
+// Workspace of the gated DeltaNet forward: per (batch, head, chunk) the
+// effective queries and W (C x N), U and the intra outputs (C x P), the
+// chunk's decay ratios and total decay, fp32, each region 256-byte aligned.
+struct GdnPlan {
+  size_t off_qe, off_w, off_u, off_oi, off_kh, off_gc, bytes;
+};
+
 int check_gdn(const loglin_dims* d, int* ll, int* nc) {
   if (!d) return LOGLIN_ERR_NULL;
   if (d->reserved != 0) return LOGLIN_ERR_DIM;
@@ -226,6 +233,27 @@ int check_gdn(const loglin_dims* d, int* ll, int* nc) {
   *ll = l;
   *nc = (int)n;
   return LOGLIN_OK;
+}
+
+GdnPlan gdn_plan(const loglin_dims* d, int nc) {
+  const size_t items = (size_t)(d->batch * d->nheads) * nc;
+  const size_t C = loglin::GDN_C;
+  GdnPlan pl;
+  size_t off = 0;
+  pl.off_qe = off;
+  off = round_up(off + items * C * d->dstate * sizeof(float));
+  pl.off_w = off;
+  off = round_up(off + items * C * d->dstate * sizeof(float));
+  pl.off_u = off;
+  off = round_up(off + items * C * d->headdim * sizeof(float));
+  pl.off_oi = off;
+  off = round_up(off + items * C * d->headdim * sizeof(float));
+  pl.off_kh = off;
+  off = round_up(off + items * C * sizeof(float));
+  pl.off_gc = off;
+  off = round_up(off + items * sizeof(float));
+  pl.bytes = off;
+  return pl;
 }
 
 // Decode state: level states fp32 [B, H, LL, P/4, N, 4], then the two banks of
@@ -435,9 +463,15 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   return fn(pr, static_cast<hipStream_t>(stream)) ? LOGLIN_ERR_HIP : LOGLIN_OK;
 }
 
+size_t loglin_gdn_workspace_bytes(const loglin_dims* dims) {
+  int ll = 0, nc = 0;
+  if (check_gdn(dims, &ll, &nc)) return 0;
+  return gdn_plan(dims, nc).bytes;
+}
+
 int loglin_gdn_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                    const float* beta, const void* lambda, void* out, const loglin_dims* dims,
-                   void* stream) {
+                   void* workspace, size_t workspace_bytes, void* stream) {
   int ll = 0, nc = 0;
   int rc = check_gdn(dims, &ll, &nc);
   if (rc) return rc;
@@ -445,6 +479,10 @@ int loglin_gdn_fwd(const void* q, const void* k, const void* v, const float* log
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_alpha) ||
       misaligned(beta) || misaligned(lambda) || misaligned(out))
     return LOGLIN_ERR_ALIGN;
+  const GdnPlan pl = gdn_plan(dims, nc);
+  if (!workspace || workspace_bytes < pl.bytes) return LOGLIN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return LOGLIN_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
   loglin::GdnParams pr{};
   pr.q = q;
   pr.k = k;
@@ -453,6 +491,12 @@ int loglin_gdn_fwd(const void* q, const void* k, const void* v, const float* log
   pr.beta = beta;
   pr.lam = lambda;
   pr.out = out;
+  pr.qe = reinterpret_cast<float*>(ws + pl.off_qe);
+  pr.w = reinterpret_cast<float*>(ws + pl.off_w);
+  pr.u = reinterpret_cast<float*>(ws + pl.off_u);
+  pr.oi = reinterpret_cast<float*>(ws + pl.off_oi);
+  pr.kh = reinterpret_cast<float*>(ws + pl.off_kh);
+  pr.gc = reinterpret_cast<float*>(ws + pl.off_gc);
   pr.batch = (int)dims->batch;
   pr.seqlen = (int)dims->seqlen;
   pr.nheads = (int)dims->nheads;

@@ -55,7 +55,7 @@ EXPORTS = (
     "loglin_fwd_ex", "loglin_validate", "loglin_strerror",
     "loglin_plan_seg_log2", "loglin_event_create", "loglin_event_destroy",
     "loglin_event_elapsed_ms", "loglin_decode_state_bytes", "loglin_decode_step",
-    "loglin_bwd_workspace_bytes", "loglin_bwd", "loglin_gdn_fwd",
+    "loglin_bwd_workspace_bytes", "loglin_bwd", "loglin_gdn_workspace_bytes", "loglin_gdn_fwd",
 )
 
 
@@ -99,7 +99,9 @@ def lib():
     L.loglin_bwd_workspace_bytes.restype = sz
     L.loglin_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, pd, vp, sz, vp]
     L.loglin_bwd.restype = i32
-    L.loglin_gdn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, pd, vp]
+    L.loglin_gdn_workspace_bytes.argtypes = [pd]
+    L.loglin_gdn_workspace_bytes.restype = sz
+    L.loglin_gdn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, pd, vp, sz, vp]
     L.loglin_gdn_fwd.restype = i32
     _lib = L
     return L
@@ -326,11 +328,28 @@ def loglin_bwd(X, B, C, log_a, lam, dO, chunk, dX, dB, dC, dlog_a, dlam, *, work
     return dX, dB, dC, dlog_a, dlam
 
 
-def loglin_gdn_fwd(q, k, v, log_alpha, beta, lam, out, *, stream=None):
+def gdn_dims(q, v, lam) -> loglin_dims:
+    Bt, T, H, N = q.shape
+    if q.dtype == torch.bfloat16:
+        dt = LOGLIN_BF16
+    elif q.dtype == torch.float32:
+        dt = LOGLIN_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return make_dims(Bt, T, H, H, v.shape[3], N, lam.shape[3], dt)
+
+
+def loglin_gdn_workspace_bytes(dims: loglin_dims) -> int:
+    return int(lib().loglin_gdn_workspace_bytes(ctypes.byref(dims)))
+
+
+def loglin_gdn_fwd(q, k, v, log_alpha, beta, lam, out, *, workspace=None, stream=None):
     """Enqueue the log-linear gated DeltaNet forward into `out` on `stream`.
     Tensors: q, k [Bt,T,H,N], v and out [Bt,T,H,P], log_alpha and beta
     [Bt,T,H] float32, lam [Bt,T,H,L]; q, k, v, lam and out share one dtype
-    (bfloat16 or float32), all on one GPU and contiguous.  Returns `out`."""
+    (bfloat16 or float32), all on one GPU and contiguous.  `workspace` is a
+    uint8 device tensor of at least loglin_gdn_workspace_bytes bytes
+    (allocated here when None).  Returns `out`."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("loglin_gdn_fwd needs GPU tensors")
@@ -351,9 +370,14 @@ def loglin_gdn_fwd(q, k, v, log_alpha, beta, lam, out, *, stream=None):
                               ("lam", lam, (Bt, T, H, L), io), ("out", out, (Bt, T, H, P), io)):
         _check_tensor(name, t, shape, d, dev)
     dims = make_dims(Bt, T, H, H, P, N, L, dt)
+    need = loglin_gdn_workspace_bytes(dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     rc = lib().loglin_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(lam),
-                              _ptr(out), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
+                              _ptr(out), ctypes.byref(dims), _ptr(workspace), ws_bytes,
+                              ctypes.c_void_p(stream.cuda_stream))
     _check(rc)
     return out

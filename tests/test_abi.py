@@ -209,8 +209,9 @@ def test_gdn_argument_errors():
     import ctypes
     lib = L.lib()
     fake = ctypes.c_void_p(0x10000)
-    def call(dims, ptr=fake):
-        return lib.loglin_gdn_fwd(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ctypes.byref(dims), None)
+    def call(dims, ptr=fake, ws=fake, nbytes=1 << 40):
+        return lib.loglin_gdn_fwd(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ctypes.byref(dims), ws, nbytes,
+                                  None)
     ok = L.make_dims(1, 64, 2, 2, 64, 128, 7, L.LOGLIN_BF16)
     assert call(L.make_dims(1, 64, 2, 1, 64, 128, 7, L.LOGLIN_BF16)) == -5  # ngroups != nheads
     assert call(L.make_dims(1, 48, 2, 2, 64, 128, 7, L.LOGLIN_BF16)) == -4  # T % 32
@@ -220,3 +221,11 @@ def test_gdn_argument_errors():
     assert call(L.make_dims(1, 64, 2, 2, 64, 128, 7, 5)) == -7  # dtype
     assert call(ok, ptr=None) == -1
     assert call(ok, ptr=ctypes.c_void_p(0x10004)) == -9  # alignment
+    need = lib.loglin_gdn_workspace_bytes(ctypes.byref(ok))
+    # 4 (head, chunk) items: Qe and W 32 x 128, U and intra outputs 32 x 64,
+    # 32 decay ratios, one total decay; fp32, each region 256-byte aligned
+    assert need == 2 * 4 * 32 * 128 * 4 + 2 * 4 * 32 * 64 * 4 + 4 * 32 * 4 + 256
+    assert call(ok, ws=None) == -8
+    assert call(ok, nbytes=need - 1) == -8
+    assert call(ok, ws=ctypes.c_void_p(0x10010)) == -9  # workspace alignment
+    assert lib.loglin_gdn_workspace_bytes(ctypes.byref(L.make_dims(1, 48, 2, 2, 64, 128, 7, 1))) == 0
