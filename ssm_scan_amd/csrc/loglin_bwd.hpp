@@ -420,33 +420,36 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
 template <class T, int C, int P, int N>
 constexpr int bwd_dq_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + 2 * C * BWD_LMAX + 4 * 64 + BWD_LMAX);
+         4 * (C * (C + 1) + 3 * C * BWD_LMAX + 5 * 64 + BWD_LMAX);
 }
 template <class T, int C, int P, int N>
 constexpr int bwd_dkv_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + C * 8 + 4 * 64 + 4 * 64 + BWD_LMAX);
+         4 * (C * (C + 1) + C * 8 + (C / 8) * 64 + 2 * 64 + 3 * 64 + BWD_LMAX);
 }
 
-// S = C B^T and D = dO X^T for the query rows [16 wave, +16) of the chunk
-// (score tiles above the diagonal block are skipped), then the mask
+// S = C B^T and D = dO X^T for the query rows [16 rb, +16) of the chunk,
+// the tiles sb = half, half + 2, ... (tiles above the diagonal block are
+// skipped), then the mask
 // M[t, s] = exp(cum_t - cum_s) lambda[t, level(t, s)] for s <= t:
 // wm = M ⊙ S (if WANT_WS), wd = M ⊙ D in the io type, and optionally
 // E ⊙ S ⊙ D or G = M ⊙ S ⊙ D in fp32.
 template <class T, int C, int P, int N, int LW, bool WANT_WS, bool WANT_ESD, bool WANT_G>
 __device__ inline void bwd_intra_scores(const T* csh, const T* bsh, const T* xsh, const T* osh,
                                         const float* cum, const float (*lam_s)[LW], T* wm, T* wd,
-                                        float (*esd)[C + 1], int wave, int g, int r) {
+                                        float (*esd)[C + 1], int rb, int half, int g, int r) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
   constexpr int KB = M::KB, TB = C / 16;
-  const int tw = 16 * wave;
+  const int tw = 16 * rb;
 #pragma unroll
-  for (int sb = 0; sb < TB; ++sb) {
+  for (int sb0 = 0; sb0 < TB; sb0 += 2) {
+    const int sb = sb0 + half;  // the two waves of a row block take alternate tiles
+    if (sb >= TB) break;
     f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
-    if (sb <= wave) {
+    if (sb <= rb) {
 #pragma unroll
       for (int kk = 0; kk < N / KB; ++kk)
         s4 = M::mma(frag_along<T, LN>(csh, tw + r, kk * KB, g),
@@ -527,19 +530,25 @@ __device__ inline bool bwd_chunk_tile(const BwdParams& pr, int& bh, int& j) {
   return true;
 }
 
-// Wave w owns query rows [16 w, +16).  dC_t = sum_s (M ⊙ D)[t, s] B_s within
-// the chunk plus, for each chunk level k whose bit is set in j,
+// Two waves per 16-row block: wave w owns query rows [16 (w mod C/16), +16)
+// and every other 16-column tile of N from w / (C/16) on (two waves per SIMD
+// hide more latency than one).  dC_t = sum_s (M ⊙ D)[t, s] B_s within the
+// chunk plus, for each chunk level k whose bit is set in j,
 // lambda[t, c+k] exp(decay) (Z_k dO_t) with Z_k the lower half's state;
 // dlambda[t, l] = the level-l bucket sum of E S D inside the chunk, and
-// exp(decay) C_t . (Z_k dO_t) at level c + k.  The next level's state is
-// loaded into registers while the current one is used.
+// exp(decay) C_t . (Z_k dO_t) at level c + k (each wave of a pair sums its
+// own tiles; the two partial sums are added in a fixed order at the end).
+// The next level's state is loaded into registers while the current one
+// is used.
+constexpr int bwd_chunk_threads(int C) { return C / 16 * 128; }
 template <class T, int C, int P, int N>
-__global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
+__global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams pr) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  constexpr int NW = C / 16, NT = NW * 64, KB = M::KB, NB = N / 16;
+  constexpr int NWR = C / 16, NW = 2 * NWR, NT = NW * 64, KB = M::KB, NB = N / 16;
+  constexpr int NBH = (NB + 1) / 2;  // column tiles per wave
   constexpr int c_log = ilog2c(C);
   __shared__ __attribute__((aligned(16))) T csh[C * N];
   __shared__ __attribute__((aligned(16))) T bsh[C * N];
@@ -550,12 +559,14 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
   __shared__ __attribute__((aligned(16))) T zlo[sizeof(T) == 2 ? N * P : 1];
   __shared__ float esd[C][C + 1];
   __shared__ float lam_s[C][BWD_LMAX];
-  __shared__ float dlam_s[C][BWD_LMAX];
-  __shared__ float cum[64], ecum[64], wst[64], term_s[64], gap_s[BWD_LMAX];
+  __shared__ float dlam_s[C][BWD_LMAX];  // intra levels; chunk levels: first wave of a pair
+  __shared__ float dlam_t[C][BWD_LMAX];  // chunk levels: second wave of a pair
+  __shared__ float cum[64], ecum[64], wst[64], term_s[64], term_t[64], gap_s[BWD_LMAX];
   int bh, j;
   if (!bwd_chunk_tile(pr, bh, j)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave % NWR, half = wave / NWR;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
@@ -608,14 +619,16 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
     if (i < C * ll) {
       lam_s[i / ll][i % ll] = lv_[q];
       dlam_s[i / ll][i % ll] = 0.f;
+      dlam_t[i / ll][i % ll] = 0.f;
     }
   }
   if (tid < pr.kc) gap_s[tid + 1] = gap;
+  if (tid < C) term_t[tid] = 0.f;
   chunk_decays<T, C>(la, cum, ecum, wst, tid);
   __syncthreads();
 
   bwd_intra_scores<T, C, P, N, BWD_LMAX, false, true, false>(csh, bsh, xsh, osh, cum, lam_s,
-                                                             nullptr, wsh, esd, wave, g, r);
+                                                             nullptr, wsh, esd, rb, half, g, r);
   __syncthreads();
 
   // intra-chunk levels: the level-l bucket of t (l >= 1) is the 2^(l-1) keys
@@ -635,16 +648,17 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
     }
   }
 
-  const int tw = 16 * wave;
-  f32x4 dc[NB];
+  const int tw = 16 * rb;
+  f32x4 dc[NBH];  // column tile nb = half + 2 q
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) dc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NBH; ++q) dc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < C / KB; ++kt) {  // keys s; entries with s > t are zero
     const auto a = frag_along<T, LC>(wsh, tw + r, kt * KB, g);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      dc[nb] = M::mma(a, frag_down<T, LN>(bsh, kt * KB, 16 * nb, g, r), dc[nb]);
+    for (int q = 0; q < NBH; ++q)
+      if (half + 2 * q < NB)
+        dc[q] = M::mma(a, frag_down<T, LN>(bsh, kt * KB, 16 * (half + 2 * q), g, r), dc[q]);
   }
   __syncthreads();  // dlam_s of the intra levels is written
   if (tid < C) {
@@ -671,17 +685,20 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
       else
         st1.load(state_of(k3), tid);
     }
-    f32x4 u[NB];  // u[t][n] = sum_p dO[t][p] Z[n][p]
+    f32x4 u[NBH];  // u[t][n] = sum_p dO[t][p] Z[n][p], this wave's column tiles
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) u[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NBH; ++q) u[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {
       const auto a = frag_along<T, LP>(osh, tw + r, kp * KB, g);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        u[nb] = M::mma(a, frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g), u[nb]);
-        if constexpr (sizeof(T) == 2)
-          u[nb] = M::mma(a, frag_along<T, LP>(zlo, 16 * nb + r, kp * KB, g), u[nb]);
+      for (int q = 0; q < NBH; ++q) {
+        const int nb = half + 2 * q;
+        if (nb < NB) {
+          u[q] = M::mma(a, frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g), u[q]);
+          if constexpr (sizeof(T) == 2)
+            u[q] = M::mma(a, frag_along<T, LP>(zlo, 16 * nb + r, kp * KB, g), u[q]);
+        }
       }
     }
     const int lv = c_log + k;
@@ -692,14 +709,20 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
       const float wt = M::ex(cum[t] + gk);
       float part = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) part += u[nb][i] * to_f(csh[LN::at(t, 16 * nb + r)]);
-      const float dl = wt * sum16(part);
+      for (int q = 0; q < NBH; ++q)
+        if (half + 2 * q < NB) part += u[q][i] * to_f(csh[LN::at(t, 16 * (half + 2 * q) + r)]);
+      const float dl = wt * sum16(part);  // this wave's share of dlambda[t][lv]
       const float lk = lam_s[t][lv];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) dc[nb][i] += (lk * wt) * u[nb][i];
+      for (int q = 0; q < NBH; ++q) dc[q][i] += (lk * wt) * u[q][i];
       if (r == 0) {
-        dlam_s[t][lv] = dl;
-        term_s[t] += lk * dl;
+        if (half == 0) {
+          dlam_s[t][lv] = dl;
+          term_s[t] += lk * dl;
+        } else {
+          dlam_t[t][lv] = dl;
+          term_t[t] += lk * dl;
+        }
       }
     }
     __syncthreads();  // zsh is restaged by the next level
@@ -709,30 +732,37 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dq_kernel(BwdParams pr) {
 
   float* dcg = pr.dch + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int q = 0; q < NBH; ++q)
+    if (half + 2 * q < NB) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * nb + r] = dc[nb][i];
+      for (int i = 0; i < 4; ++i)
+        dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * (half + 2 * q) + r] = dc[q][i];
+    }
   T* dlg = static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L;
   for (int i = tid; i < C * L; i += NT) {
     const int t = i / L, l = i % L;
-    dlg[(int64_t)t * H * L + l] = from_f<T>(l < pr.ll ? dlam_s[t][l] : 0.f);
+    float v = 0.f;
+    if (l < pr.ll) v = l <= c_log ? dlam_s[t][l] : dlam_s[t][l] + dlam_t[t][l];
+    dlg[(int64_t)t * H * L + l] = from_f<T>(v);
   }
-  if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid];
+  if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid] + term_t[tid];
 }
 
-// The mask epilogue runs per query row block as in bwd_dq_kernel; then wave
-// w owns key rows [16 w, +16): dX_s = sum_t (M ⊙ S)[t, s] dO_t and
+// The mask epilogue runs per query row block as in bwd_dq_kernel; then the
+// two waves w of a pair own key rows [16 (w mod C/16), +16), each every
+// other 16-column tile of P and of N: dX_s = sum_t (M ⊙ S)[t, s] dO_t and
 // dB_s = sum_t (M ⊙ D)[t, s] C_t within the chunk, plus, for each chunk level
 // k whose bit is clear in i and whose upper half exists,
 // exp(decay s -> end of the lower half) (R_k^T B_s, R_k X_s) with R_k the
 // upper half's state (lambda already on its tokens).
 template <class T, int C, int P, int N>
-__global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
+__global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams pr) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  constexpr int NW = C / 16, NT = NW * 64, KB = M::KB, NB = N / 16, PB = P / 16;
+  constexpr int NWR = C / 16, NW = 2 * NWR, NT = NW * 64, KB = M::KB, NB = N / 16, PB = P / 16;
+  constexpr int NBH = (NB + 1) / 2, PBH = (PB + 1) / 2;  // column tiles per wave
   constexpr int c_log = ilog2c(C);
   __shared__ __attribute__((aligned(16))) T csh[C * N];
   __shared__ __attribute__((aligned(16))) T bsh[C * N];
@@ -745,11 +775,13 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
   __shared__ float gsh[C][C + 1];
   __shared__ float lam_s[C][8];
   __shared__ float colpart[NW][64];
+  __shared__ float xpart[2][64];  // X_s . (chunk-level dX_s), per wave of a pair
   __shared__ float cum[64], ecum[64], wst[64], gap_s[BWD_LMAX];
   int bh, i_ch;
   if (!bwd_chunk_tile(pr, bh, i_ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave % NWR, half = wave / NWR;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t T_ = pr.seqlen, t0 = (int64_t)i_ch * C;
@@ -805,7 +837,7 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
   __syncthreads();
 
   bwd_intra_scores<T, C, P, N, 8, true, false, true>(csh, bsh, xsh, osh, cum, lam_s, wsh, vsh,
-                                                     gsh, wave, g, r);
+                                                     gsh, rb, half, g, r);
   __syncthreads();
   // X_s . dX_s within the chunk is the column sum of G: taken in fp32 from
   // the same entries whose row sums form dO_t . O_t, so that the two terms of
@@ -818,22 +850,25 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
     colpart[wave][lane] = cs;
   }
 
-  const int sw = 16 * wave;
-  f32x4 dx[PB], dxe[PB], db[NB];  // dX: intra-chunk part, chunk-level part
+  const int sw = 16 * rb;
+  // dX: intra-chunk part, chunk-level part (column tile half + 2 q of each)
+  f32x4 dx[PBH], dxe[PBH], db[NBH];
 #pragma unroll
-  for (int pb = 0; pb < PB; ++pb) dx[pb] = dxe[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < PBH; ++q) dx[q] = dxe[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) db[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NBH; ++q) db[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < C / KB; ++kt) {  // queries t; entries with t < s are zero
     const auto aw = frag_down<T, LC>(wsh, kt * KB, sw, g, r);
     const auto av = frag_down<T, LC>(vsh, kt * KB, sw, g, r);
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb)
-      dx[pb] = M::mma(aw, frag_down<T, LP>(osh, kt * KB, 16 * pb, g, r), dx[pb]);
+    for (int q = 0; q < PBH; ++q)
+      if (half + 2 * q < PB)
+        dx[q] = M::mma(aw, frag_down<T, LP>(osh, kt * KB, 16 * (half + 2 * q), g, r), dx[q]);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      db[nb] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * nb, g, r), db[nb]);
+    for (int q = 0; q < NBH; ++q)
+      if (half + 2 * q < NB)
+        db[q] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * (half + 2 * q), g, r), db[q]);
   }
 
   int buf = 0;
@@ -853,29 +888,35 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
       else
         st1.load(state_of(k3), tid);
     }
-    f32x4 tx[PB], tb[NB];
+    f32x4 tx[PBH], tb[NBH];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) tx[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < PBH; ++q) tx[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) tb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NBH; ++q) tb[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kn2 = 0; kn2 < N / KB; ++kn2) {  // tx[s][p] = sum_n B[s][n] R[n][p]
       const auto a = frag_along<T, LN>(bsh, sw + r, kn2 * KB, g);
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb) {
-        tx[pb] = M::mma(a, frag_down<T, LP>(rsh, kn2 * KB, 16 * pb, g, r), tx[pb]);
-        if constexpr (sizeof(T) == 2)
-          tx[pb] = M::mma(a, frag_down<T, LP>(rlo, kn2 * KB, 16 * pb, g, r), tx[pb]);
+      for (int q = 0; q < PBH; ++q) {
+        const int pb = half + 2 * q;
+        if (pb < PB) {
+          tx[q] = M::mma(a, frag_down<T, LP>(rsh, kn2 * KB, 16 * pb, g, r), tx[q]);
+          if constexpr (sizeof(T) == 2)
+            tx[q] = M::mma(a, frag_down<T, LP>(rlo, kn2 * KB, 16 * pb, g, r), tx[q]);
+        }
       }
     }
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {  // tb[s][n] = sum_p X[s][p] R[n][p]
       const auto a = frag_along<T, LP>(xsh, sw + r, kp * KB, g);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        tb[nb] = M::mma(a, frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g), tb[nb]);
-        if constexpr (sizeof(T) == 2)
-          tb[nb] = M::mma(a, frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g), tb[nb]);
+      for (int q = 0; q < NBH; ++q) {
+        const int nb = half + 2 * q;
+        if (nb < NB) {
+          tb[q] = M::mma(a, frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g), tb[q]);
+          if constexpr (sizeof(T) == 2)
+            tb[q] = M::mma(a, frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g), tb[q]);
+        }
       }
     }
     const float gk = gap_s[k];
@@ -884,36 +925,40 @@ __global__ __launch_bounds__(C / 16 * 64) void bwd_dkv_kernel(BwdParams pr) {
       const int s = sw + 4 * g + i;
       const float w = M::ex(cum[C - 1] - cum[s] + gk);
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb) dxe[pb][i] += w * tx[pb][i];
+      for (int q = 0; q < PBH; ++q) dxe[q][i] += w * tx[q][i];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) db[nb][i] += w * tb[nb][i];
+      for (int q = 0; q < NBH; ++q) db[q][i] += w * tb[q][i];
     }
     __syncthreads();  // rsh is restaged by the next level
     k = kn;
     buf ^= 1;
   }
-  __syncthreads();  // colpart is complete (also when no level ran)
-
   T* dxg = static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P;
   float* dbg = pr.dbh + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = sw + 4 * g + i;
-    float part = 0.f;  // X_s . (chunk-level part of dX_s)
+    float part = 0.f;  // X_s . (chunk-level part of dX_s), this wave's columns
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) {
-      part += dxe[pb][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
-      dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[pb][i] + dxe[pb][i]);
+    for (int q = 0; q < PBH; ++q) {
+      const int pb = half + 2 * q;
+      if (pb < PB) {
+        part += dxe[q][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
+        dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[q][i] + dxe[q][i]);
+      }
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) dbg[(int64_t)s * H * N + 16 * nb + r] = db[nb][i];
+    for (int q = 0; q < NBH; ++q)
+      if (half + 2 * q < NB) dbg[(int64_t)s * H * N + 16 * (half + 2 * q) + r] = db[q][i];
     part = sum16(part);
-    if (r == 0) {
-      float cs = 0.f;
+    if (r == 0) xpart[half][s] = part;
+  }
+  __syncthreads();  // colpart and xpart are complete (also when no level ran)
+  if (tid < C) {
+    float cs = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) cs += colpart[w][s];
-      pr.term2[(int64_t)bh * T_ + t0 + s] = cs + part;
-    }
+    for (int w = 0; w < NW; ++w) cs += colpart[w][tid];
+    pr.term2[(int64_t)bh * T_ + t0 + tid] = cs + (xpart[0][tid] + xpart[1][tid]);
   }
 }
 
@@ -994,8 +1039,8 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
     }
   }
   const int tiles8 = (pr.nc * bh + 7) & ~7;  // xcd_tile deals whole rounds of 8
-  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(tiles8), dim3(C / 16 * 64), 0, st, pr);
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(tiles8), dim3(C / 16 * 64), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(tiles8), dim3(bwd_chunk_threads(C)), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(tiles8), dim3(bwd_chunk_threads(C)), 0, st, pr);
   const int64_t groups4 = (int64_t)pr.batch * pr.seqlen * pr.ngroups * (N / 4);
   hipLaunchKernelGGL((bwd_group_sum_kernel<T, N>), dim3((unsigned)((groups4 + 255) / 256)),
                      dim3(256), 0, st, pr);
