@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD, choices=sorted(inputs.CONFIGS))
     ap.add_argument("--seg-log2", type=int, default=None)
+    ap.add_argument("--heads-per-block", type=int, default=None,
+                    help="heads per output-pass work-group (library default when omitted)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of wall time for the CPU oracle sample (0: skip)")
     ap.add_argument("--mode", choices=("forward", "decode", "naive", "backward", "gdn"),
@@ -269,7 +271,7 @@ def main():
     def step(events=None):
         L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], cfg.chunk, out,
                      workspace=ws, stream=stream, seg_log2=args.seg_log2,
-                     stage_events=events)
+                     stage_events=events, heads_per_block=args.heads_per_block)
 
     if args.mode == "naive":
         return main_naive(args, cfg, t, out, ws, stream, step)

@@ -352,14 +352,14 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
     const float la = nxt[0], lamv = nxt[1];
     if (step + 1 < n) nxt = issue(REV ? hi - 2 - step : lo + step + 1);
     chunk_decays<T, C>(la, cum, ecum, wst, tid);
-    __syncthreads();
+    lds_barrier();
     if (tid < C) wsh[tid] = REV ? lamv * ecum[tid] : wst[tid];
-    __syncthreads();
+    lds_barrier();
     const float dec = M::ex(cum[C - 1]);
 #pragma unroll
     for (int nb = 0; nb < Tl::NB; ++nb) S[nb] *= dec;
     chunk_state_mma_split<T, C, P, N>(ksh, vsh, wsh, S, wave, g, r);
-    __syncthreads();  // the next chunk restages the tiles
+    lds_barrier();  // the next chunk restages the tiles
   }
   float* dst = bwd_pieces(k) == 1
                    ? (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P)
@@ -447,7 +447,7 @@ __device__ inline void bwd_intra_scores(const T* csh, const T* bsh, const T* xsh
 #pragma unroll
   for (int sb0 = 0; sb0 < TB; sb0 += 2) {
     const int sb = sb0 + half;  // the two waves of a row block take alternate tiles
-    if (sb >= TB) break;
+    if (TB % 2 != 0 && sb >= TB) break;  // (never for an even tile count)
     f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
     if (sb <= rb) {
 #pragma unroll
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   if (!bwd_chunk_tile(pr, bh, j)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rb = wave % NWR, half = wave / NWR;
+  const int half = wave >= NWR ? 1 : 0, rb = wave - half * NWR;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
@@ -625,11 +625,11 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   if (tid < pr.kc) gap_s[tid + 1] = gap;
   if (tid < C) term_t[tid] = 0.f;
   chunk_decays<T, C>(la, cum, ecum, wst, tid);
-  __syncthreads();
+  lds_barrier();
 
   bwd_intra_scores<T, C, P, N, BWD_LMAX, false, true, false>(csh, bsh, xsh, osh, cum, lam_s,
                                                              nullptr, wsh, esd, rb, half, g, r);
-  __syncthreads();
+  lds_barrier();
 
   // intra-chunk levels: the level-l bucket of t (l >= 1) is the 2^(l-1) keys
   // below t's aligned 2^l block boundary, present when bit l-1 of t is set;
@@ -649,6 +649,9 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   }
 
   const int tw = 16 * rb;
+  // this wave's share of the chunk-level dlambda and dlog_a sums
+  float(*const dlam_h)[BWD_LMAX] = half ? dlam_t : dlam_s;
+  float* const term_h = half ? term_t : term_s;
   f32x4 dc[NBH];  // column tile nb = half + 2 q
 #pragma unroll
   for (int q = 0; q < NBH; ++q) dc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -657,16 +660,16 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     const auto a = frag_along<T, LC>(wsh, tw + r, kt * KB, g);
 #pragma unroll
     for (int q = 0; q < NBH; ++q)
-      if (half + 2 * q < NB)
+      if (NB % 2 == 0 || half + 2 * q < NB)
         dc[q] = M::mma(a, frag_down<T, LN>(bsh, kt * KB, 16 * (half + 2 * q), g, r), dc[q]);
   }
-  __syncthreads();  // dlam_s of the intra levels is written
+  lds_barrier();  // dlam_s of the intra levels is written
   if (tid < C) {
     float tsum = 0.f;
     for (int l = 0; l <= c_log; ++l) tsum += lam_s[tid][l] * dlam_s[tid][l];
     term_s[tid] = tsum;
   }
-  __syncthreads();
+  lds_barrier();
 
   int buf = 0;
   while (k) {
@@ -674,7 +677,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
       st0.store(zsh, zlo, tid);
     else
       st1.store(zsh, zlo, tid);
-    __syncthreads();
+    lds_barrier();
     act &= act - 1u;
     const int kn = act ? __builtin_ctz(act) + 1 : 0;
     const unsigned a3 = act ? act & (act - 1u) : 0u;
@@ -694,7 +697,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
 #pragma unroll
       for (int q = 0; q < NBH; ++q) {
         const int nb = half + 2 * q;
-        if (nb < NB) {
+        if (NB % 2 == 0 || nb < NB) {
           u[q] = M::mma(a, frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g), u[q]);
           if constexpr (sizeof(T) == 2)
             u[q] = M::mma(a, frag_along<T, LP>(zlo, 16 * nb + r, kp * KB, g), u[q]);
@@ -710,22 +713,17 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
       float part = 0.f;
 #pragma unroll
       for (int q = 0; q < NBH; ++q)
-        if (half + 2 * q < NB) part += u[q][i] * to_f(csh[LN::at(t, 16 * (half + 2 * q) + r)]);
+        if (NB % 2 == 0 || half + 2 * q < NB) part += u[q][i] * to_f(csh[LN::at(t, 16 * (half + 2 * q) + r)]);
       const float dl = wt * sum16(part);  // this wave's share of dlambda[t][lv]
       const float lk = lam_s[t][lv];
 #pragma unroll
       for (int q = 0; q < NBH; ++q) dc[q][i] += (lk * wt) * u[q][i];
       if (r == 0) {
-        if (half == 0) {
-          dlam_s[t][lv] = dl;
-          term_s[t] += lk * dl;
-        } else {
-          dlam_t[t][lv] = dl;
-          term_t[t] += lk * dl;
-        }
+        dlam_h[t][lv] = dl;
+        term_h[t] += lk * dl;
       }
     }
-    __syncthreads();  // zsh is restaged by the next level
+    lds_barrier();  // zsh is restaged by the next level
     k = kn;
     buf ^= 1;
   }
@@ -733,7 +731,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   float* dcg = pr.dch + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
   for (int q = 0; q < NBH; ++q)
-    if (half + 2 * q < NB) {
+    if (NB % 2 == 0 || half + 2 * q < NB) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * (half + 2 * q) + r] = dc[q][i];
@@ -781,7 +779,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   if (!bwd_chunk_tile(pr, bh, i_ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rb = wave % NWR, half = wave / NWR;
+  const int half = wave >= NWR ? 1 : 0, rb = wave - half * NWR;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int64_t T_ = pr.seqlen, t0 = (int64_t)i_ch * C;
@@ -834,11 +832,11 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   }
   if (tid < pr.kc) gap_s[tid + 1] = gap;
   chunk_decays<T, C>(la, cum, ecum, wst, tid);
-  __syncthreads();
+  lds_barrier();
 
   bwd_intra_scores<T, C, P, N, 8, true, false, true>(csh, bsh, xsh, osh, cum, lam_s, wsh, vsh,
                                                      gsh, rb, half, g, r);
-  __syncthreads();
+  lds_barrier();
   // X_s . dX_s within the chunk is the column sum of G: taken in fp32 from
   // the same entries whose row sums form dO_t . O_t, so that the two terms of
   // dlog_a agree where they overlap (the rounding of M ⊙ S to the io type for
@@ -863,11 +861,11 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     const auto av = frag_down<T, LC>(vsh, kt * KB, sw, g, r);
 #pragma unroll
     for (int q = 0; q < PBH; ++q)
-      if (half + 2 * q < PB)
+      if (PB % 2 == 0 || half + 2 * q < PB)
         dx[q] = M::mma(aw, frag_down<T, LP>(osh, kt * KB, 16 * (half + 2 * q), g, r), dx[q]);
 #pragma unroll
     for (int q = 0; q < NBH; ++q)
-      if (half + 2 * q < NB)
+      if (NB % 2 == 0 || half + 2 * q < NB)
         db[q] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * (half + 2 * q), g, r), db[q]);
   }
 
@@ -877,7 +875,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
       st0.store(rsh, rlo, tid);
     else
       st1.store(rsh, rlo, tid);
-    __syncthreads();
+    lds_barrier();
     act &= act - 1u;
     const int kn = act ? __builtin_ctz(act) + 1 : 0;
     const unsigned a3 = act ? act & (act - 1u) : 0u;
@@ -899,7 +897,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 #pragma unroll
       for (int q = 0; q < PBH; ++q) {
         const int pb = half + 2 * q;
-        if (pb < PB) {
+        if (PB % 2 == 0 || pb < PB) {
           tx[q] = M::mma(a, frag_down<T, LP>(rsh, kn2 * KB, 16 * pb, g, r), tx[q]);
           if constexpr (sizeof(T) == 2)
             tx[q] = M::mma(a, frag_down<T, LP>(rlo, kn2 * KB, 16 * pb, g, r), tx[q]);
@@ -912,7 +910,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 #pragma unroll
       for (int q = 0; q < NBH; ++q) {
         const int nb = half + 2 * q;
-        if (nb < NB) {
+        if (NB % 2 == 0 || nb < NB) {
           tb[q] = M::mma(a, frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g), tb[q]);
           if constexpr (sizeof(T) == 2)
             tb[q] = M::mma(a, frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g), tb[q]);
@@ -929,7 +927,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 #pragma unroll
       for (int q = 0; q < NBH; ++q) db[q][i] += w * tb[q][i];
     }
-    __syncthreads();  // rsh is restaged by the next level
+    lds_barrier();  // rsh is restaged by the next level
     k = kn;
     buf ^= 1;
   }
@@ -942,18 +940,18 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 #pragma unroll
     for (int q = 0; q < PBH; ++q) {
       const int pb = half + 2 * q;
-      if (pb < PB) {
+      if (PB % 2 == 0 || pb < PB) {
         part += dxe[q][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
         dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[q][i] + dxe[q][i]);
       }
     }
 #pragma unroll
     for (int q = 0; q < NBH; ++q)
-      if (half + 2 * q < NB) dbg[(int64_t)s * H * N + 16 * (half + 2 * q) + r] = db[q][i];
+      if (NB % 2 == 0 || half + 2 * q < NB) dbg[(int64_t)s * H * N + 16 * (half + 2 * q) + r] = db[q][i];
     part = sum16(part);
     if (r == 0) xpart[half][s] = part;
   }
-  __syncthreads();  // colpart and xpart are complete (also when no level ran)
+  lds_barrier();  // colpart and xpart are complete (also when no level ran)
   if (tid < C) {
     float cs = 0.f;
 #pragma unroll

@@ -752,8 +752,10 @@ __device__ inline void score_tile(int u, int& tb, int& sb) {
 // lanes.
 //
 // B and X rows are double-buffered in LDS (bf16): the next chunk's rows are
-// requested right after the current chunk's first barrier.  C rows are
-// single-buffered and refilled once the output tiles have read them.
+// requested right after the current chunk's first barrier.  C rows and the
+// level weights are single-buffered and refilled once the output tiles have
+// read them, except in the two-head form, where they are double-buffered and
+// requested together with B and X.
 template <class T, int C, int P, int N, int HP>
 struct OutCfg {
   using Tl = Tiles<T, C, P, N>;
@@ -765,6 +767,10 @@ struct OutCfg {
   // slots above the segment held in registers for the whole segment
   static constexpr int RZ = sizeof(T) == 2 ? 3 : 1;
   static constexpr int MIN_BLOCKS = HP == 1 ? 2 : 1;
+  // C rows and level weights double-buffered too where one work-group has
+  // the CU's LDS to itself (two heads per work-group): the next chunk's
+  // rows are then all requested one whole chunk ahead
+  static constexpr bool CB2 = NBUF == 2 && HP == 2;
 };
 
 // MASKED: only the levels in pr.lmask enter the output (a separate
@@ -792,14 +798,15 @@ void output_kernel(Params pr) {
   __shared__ __attribute__((aligned(1024))) T bsh1[NBUF == 2 ? KC * N : 1];
   __shared__ __attribute__((aligned(1024))) T xsh0[HP * KC * P];
   __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? HP * KC * P : 1];
-  __shared__ __attribute__((aligned(1024))) T csh[C * N];          // C rows
+  __shared__ __attribute__((aligned(1024))) T csh0[C * N];  // C rows
+  __shared__ __attribute__((aligned(1024))) T csh1[Cfg::CB2 ? C * N : 1];
   // W[t][s] of each head; after the intra product, the head's output tile
   // [t][P] (Rows layout) on its way to memory
   constexpr int WTS = C * Tl::XS > C * P ? C * Tl::XS : C * P;
   __shared__ __attribute__((aligned(16))) T wt[HP * WTS];
   __shared__ __attribute__((aligned(16))) float cum[HP * C], ecum[HP * C], wst[HP * KC];
   __shared__ float gap_s[HP * GS];     // gap log-decays of this segment
-  extern __shared__ unsigned lam_w[];  // [HP][C][lam_words]: level weights
+  extern __shared__ unsigned lam_w[];  // [CB2 ? 2 : 1][HP][C][lam_words]: level weights
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
@@ -902,9 +909,9 @@ void output_kernel(Params pr) {
     for (int k = 0; k < HP; ++k)
       rows_to_lds<T, C, P, NTW>(X + (r0 * H + h0 + k) * P, (int64_t)H * P, xs + k * KC * P, wave, lane);
   };
-  auto issue_c = [&](int j, int lane) __attribute__((always_inline)) {
+  auto issue_c = [&](int j, T* cs, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, NTW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, csh, wave, lane);
+    rows_to_lds<T, C, N, NTW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, cs, wave, lane);
   };
   auto issue_regs = [&](int j, int tid) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
@@ -914,7 +921,7 @@ void output_kernel(Params pr) {
   // level weights of chunk j into lam_w (the last word of the tensor bounds
   // the copy: a row's padding words may run past the end)
   const int64_t lam_last_word = ((int64_t)pr.batch * pr.seqlen * H * L * (int64_t)sizeof(T) - 4) / 4;
-  auto issue_lam = [&](int j, int lane) __attribute__((always_inline)) {
+  auto issue_lam = [&](int j, unsigned* lw, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const int words = HP * C * LW;
     for (int inst = __builtin_amdgcn_readfirstlane(wave); inst * 64 < words; inst += NTW) {
@@ -925,7 +932,7 @@ void output_kernel(Params pr) {
         const int64_t e0 = ((r0 + t) * H + h0 + k) * L;
         int64_t gw = (sizeof(T) == 4 ? e0 : (e0 >> 1)) + w;
         gw = gw < lam_last_word ? gw : lam_last_word;
-        dma_4x64(static_cast<const unsigned*>(pr.lam) + gw, lds_addr(lam_w) + inst * 256u);
+        dma_4x64(static_cast<const unsigned*>(pr.lam) + gw, lds_addr(lw) + inst * 256u);
       }
     }
   };
@@ -933,13 +940,14 @@ void output_kernel(Params pr) {
   // par: the row starts in the upper half of its first word (bf16, odd
   // level count)
   const unsigned long long lmask = MASKED ? pr.lmask : ~0ull;
-  auto lam_at = [&](int k, int t, int lvl, int par) __attribute__((always_inline)) -> float {
+  auto lam_at = [&](auto cur_c, int k, int t, int lvl, int par) __attribute__((always_inline)) -> float {
+    const unsigned* lw = lam_w + (Cfg::CB2 ? decltype(cur_c)::value * HP * C * LW : 0);
     const int row = k * C + t;
     float v;
     if constexpr (sizeof(T) == 4) {
-      v = __uint_as_float(lam_w[row * LW + lvl]);
+      v = __uint_as_float(lw[row * LW + lvl]);
     } else {
-      const unsigned short* hw = reinterpret_cast<const unsigned short*>(lam_w);
+      const unsigned short* hw = reinterpret_cast<const unsigned short*>(lw);
       v = __uint_as_float((unsigned)hw[2 * row * LW + par + lvl] << 16);
     }
     if constexpr (MASKED) return (lmask >> lvl) & 1 ? v : 0.f;  // left-out levels weigh 0
@@ -948,8 +956,8 @@ void output_kernel(Params pr) {
   const bool intra_on = !MASKED || (lmask & ((2ull << c_log) - 1)) != 0;  // levels 0..log2 C
   const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
-  issue_c(j0, tid0 & 63);
-  issue_lam(j0, tid0 & 63);
+  issue_c(j0, csh0, tid0 & 63);
+  issue_lam(j0, lam_w, tid0 & 63);
   issue_regs(j0, tid0);
 
   // one chunk per call; CUR selects the B / X buffer pair at compile time
@@ -959,6 +967,10 @@ void output_kernel(Params pr) {
     T* xsb = CUR ? xsh1 : xsh0;
     T* bs_next = NBUF == 2 ? (CUR ? bsh0 : bsh1) : bsh0;
     T* xs_next = NBUF == 2 ? (CUR ? xsh0 : xsh1) : xsh0;
+    constexpr int CURC = Cfg::CB2 ? CUR : 0;
+    T* csh = CURC ? csh1 : csh0;
+    T* cs_next = CURC ? csh0 : csh1;
+    unsigned* lw_next = lam_w + (1 - CURC) * HP * C * LW;
     const int j = j0 + jl;
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const bool need_state = jl + 1 < nch;
@@ -973,7 +985,13 @@ void output_kernel(Params pr) {
     if (wv == 0) chunk_decays<T, C>(la, cum_h, ecum_h, wst_h, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     lds_barrier();
-    if (NBUF == 2 && need_state) issue_bx(j + 1, bs_next, xs_next, lane);  // other pair is free
+    if (NBUF == 2 && need_state) {  // the other buffers are free
+      issue_bx(j + 1, bs_next, xs_next, lane);
+      if constexpr (Cfg::CB2) {
+        issue_c(j + 1, cs_next, lane);
+        issue_lam(j + 1, lw_next, lane);
+      }
+    }
     const float atot = cum_h[C - 1];
 
     // ---- intra-chunk weights W[t][s] of every head, from the shared
@@ -999,7 +1017,7 @@ void output_kernel(Params pr) {
           for (int i = 0; i < 4; ++i) {
             const int s = 16 * sb + 4 * g + i;
             wv4[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[k * C + s]) *
-                                    lam_at(k, t, bit_length(t ^ s), par)
+                                    lam_at(cur_c, k, t, bit_length(t ^ s), par)
                               : 0.f;
           }
         }
@@ -1029,7 +1047,7 @@ void output_kernel(Params pr) {
       auto level_scale = [&](int tb, int level, float eD) __attribute__((always_inline)) {
         const int t = 16 * tb + r;
         // 16 tb keeps the parity of the row start: H * 16 tb is even
-        return lam_at(hh, t, level, par_r) * ecum_h[t] * eD;
+        return lam_at(cur_c, hh, t, level, par_r) * ecum_h[t] * eD;
       };
 
       // Levels whose slots are in registers (the segment's resident ones and
@@ -1118,8 +1136,10 @@ void output_kernel(Params pr) {
     }
 
     if (need_state) {
-      issue_c(j + 1, lane);
-      issue_lam(j + 1, lane);
+      if constexpr (!Cfg::CB2) {
+        issue_c(j + 1, csh0, lane);
+        issue_lam(j + 1, lam_w, lane);
+      }
       issue_regs(j + 1, tid);  // land during the state MFMAs
 
       // ---- this chunk's state, pushed on the local Fenwick stack
