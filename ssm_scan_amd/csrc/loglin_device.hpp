@@ -325,6 +325,31 @@ __device__ inline void dma_4x64(const void* src, unsigned lds_byte) {
                : "memory", "m0");
 }
 
+// The same two copies from a uniform base address (scalar registers) plus
+// a 32-bit per-lane byte offset: the per-lane address arithmetic stays
+// 32-bit.  The base must be the same in every lane (it is read from the
+// first active one).
+__device__ inline unsigned long long uniform_addr(const void* p) {
+  const unsigned long long a = (unsigned long long)(uintptr_t)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ inline void dma_16x64_at(const void* base, unsigned off, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(uniform_addr(base)), "s"(m0)
+               : "memory", "m0");
+}
+__device__ inline void dma_4x64_at(const void* base, unsigned off, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(off), "s"(uniform_addr(base)), "s"(m0)
+               : "memory", "m0");
+}
+
 // Byte address of an LDS array element in the LDS aperture (32 bits).
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(lds_ptr_t)const_cast<void*>(p);
@@ -335,21 +360,25 @@ __device__ inline unsigned lds_addr(const void* p) {
 // instruction writes the 16 bytes at M0 + 16 i, so each instruction fills
 // 1 KB of LDS and every lane fetches the global block that belongs there.
 // The copy is asynchronous: s_waitcnt and a barrier precede any read.
+// g is uniform; R rows of the stride fit 32-bit byte offsets (the host
+// bounds heads and state sizes far below that).
 template <class T, int R, int W, int NW>
 __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, int lane) {
   using L = Rows<T, W>;
   constexpr int PIECES = R * L::NBLK;  // 16-byte pieces of the tile
   constexpr int INSTS = (PIECES + 63) / 64;
   const int ws = __builtin_amdgcn_readfirstlane(wave);  // uniform: keep it scalar
+  __builtin_assume(ws >= 0 && ws < NW);
+  const unsigned rs = (unsigned)grs * (unsigned)sizeof(T);  // row stride in bytes
 #pragma unroll
   for (int k = 0; k < (INSTS + NW - 1) / NW; ++k) {
     const int inst = ws + k * NW;
     const int piece = inst * 64 + lane;
-    if (inst < INSTS && piece < PIECES) {  // lanes past a short tile write nothing
+    if ((INSTS % NW == 0 || inst < INSTS) && (PIECES % 64 == 0 || piece < PIECES)) {
+      // (lanes past a short tile write nothing)
       const int row = piece / L::NBLK, pb = piece % L::NBLK;
       const int lb = (pb ^ row) & (L::NBLK - 1);
-      const T* src = g + (int64_t)row * grs + lb * L::VEC;
-      dma_16x64(src, lds_addr(lds) + inst * 1024u);
+      dma_16x64_at(g, (unsigned)row * rs + (unsigned)(lb * 16), lds_addr(lds) + inst * 1024u);
     }
   }
 }
@@ -752,10 +781,8 @@ __device__ inline void score_tile(int u, int& tb, int& sb) {
 // lanes.
 //
 // B and X rows are double-buffered in LDS (bf16): the next chunk's rows are
-// requested right after the current chunk's first barrier.  C rows and the
-// level weights are single-buffered and refilled once the output tiles have
-// read them, except in the two-head form, where they are double-buffered and
-// requested together with B and X.
+// requested right after the current chunk's first barrier.  C rows are
+// single-buffered and refilled once the output tiles have read them.
 template <class T, int C, int P, int N, int HP>
 struct OutCfg {
   using Tl = Tiles<T, C, P, N>;
@@ -767,10 +794,6 @@ struct OutCfg {
   // slots above the segment held in registers for the whole segment
   static constexpr int RZ = sizeof(T) == 2 ? 3 : 1;
   static constexpr int MIN_BLOCKS = HP == 1 ? 2 : 1;
-  // C rows and level weights double-buffered too where one work-group has
-  // the CU's LDS to itself (two heads per work-group): the next chunk's
-  // rows are then all requested one whole chunk ahead
-  static constexpr bool CB2 = NBUF == 2 && HP == 2;
 };
 
 // MASKED: only the levels in pr.lmask enter the output (a separate
@@ -798,15 +821,14 @@ void output_kernel(Params pr) {
   __shared__ __attribute__((aligned(1024))) T bsh1[NBUF == 2 ? KC * N : 1];
   __shared__ __attribute__((aligned(1024))) T xsh0[HP * KC * P];
   __shared__ __attribute__((aligned(1024))) T xsh1[NBUF == 2 ? HP * KC * P : 1];
-  __shared__ __attribute__((aligned(1024))) T csh0[C * N];  // C rows
-  __shared__ __attribute__((aligned(1024))) T csh1[Cfg::CB2 ? C * N : 1];
+  __shared__ __attribute__((aligned(1024))) T csh[C * N];          // C rows
   // W[t][s] of each head; after the intra product, the head's output tile
   // [t][P] (Rows layout) on its way to memory
   constexpr int WTS = C * Tl::XS > C * P ? C * Tl::XS : C * P;
   __shared__ __attribute__((aligned(16))) T wt[HP * WTS];
   __shared__ __attribute__((aligned(16))) float cum[HP * C], ecum[HP * C], wst[HP * KC];
   __shared__ float gap_s[HP * GS];     // gap log-decays of this segment
-  extern __shared__ unsigned lam_w[];  // [CB2 ? 2 : 1][HP][C][lam_words]: level weights
+  extern __shared__ unsigned lam_w[];  // [HP][C][lam_words]: level weights
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= pr.total) return;
@@ -909,9 +931,9 @@ void output_kernel(Params pr) {
     for (int k = 0; k < HP; ++k)
       rows_to_lds<T, C, P, NTW>(X + (r0 * H + h0 + k) * P, (int64_t)H * P, xs + k * KC * P, wave, lane);
   };
-  auto issue_c = [&](int j, T* cs, int lane) __attribute__((always_inline)) {
+  auto issue_c = [&](int j, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    rows_to_lds<T, C, N, NTW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, cs, wave, lane);
+    rows_to_lds<T, C, N, NTW>(Cm + (r0 * G + grp) * N, (int64_t)G * N, csh, wave, lane);
   };
   auto issue_regs = [&](int j, int tid) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
@@ -921,18 +943,26 @@ void output_kernel(Params pr) {
   // level weights of chunk j into lam_w (the last word of the tensor bounds
   // the copy: a row's padding words may run past the end)
   const int64_t lam_last_word = ((int64_t)pr.batch * pr.seqlen * H * L * (int64_t)sizeof(T) - 4) / 4;
-  auto issue_lam = [&](int j, unsigned* lw, int lane) __attribute__((always_inline)) {
+  // idx / LW in float: idx < 2^13 and the exact quotient of idx + 1/2 lies
+  // at least 1/(2 LW) from an integer, far beyond the rounding error
+  const float inv_lw = 1.f / (float)LW;
+  auto issue_lam = [&](int j, int lane) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    const int64_t eb = (r0 * H + h0) * L;  // element index of the chunk's first row
+    const int64_t wb = sizeof(T) == 4 ? eb : (eb >> 1);
+    const int par0 = sizeof(T) == 4 ? 0 : (int)(eb & 1);
+    const unsigned* base = static_cast<const unsigned*>(pr.lam) + wb;
+    const unsigned lim = (unsigned)min(lam_last_word - wb, (int64_t)0x7fffffff);
     const int words = HP * C * LW;
     for (int inst = __builtin_amdgcn_readfirstlane(wave); inst * 64 < words; inst += NTW) {
       const int idx = inst * 64 + lane;
       if (idx < words) {
-        const int tw = idx / LW, w = idx - tw * LW;  // tw = head * C + token
+        const int tw = (int)(((float)idx + 0.5f) * inv_lw), w = idx - tw * LW;  // tw = head * C + token
         const int k = tw / C, t = tw - k * C;
-        const int64_t e0 = ((r0 + t) * H + h0 + k) * L;
-        int64_t gw = (sizeof(T) == 4 ? e0 : (e0 >> 1)) + w;
-        gw = gw < lam_last_word ? gw : lam_last_word;
-        dma_4x64(static_cast<const unsigned*>(pr.lam) + gw, lds_addr(lw) + inst * 256u);
+        const int x = (t * H + k) * L;  // element offset of the row from eb
+        unsigned ow = (unsigned)((sizeof(T) == 4 ? x : ((x + par0) >> 1)) + w);
+        ow = ow < lim ? ow : lim;
+        dma_4x64_at(base, ow * 4u, lds_addr(lam_w) + inst * 256u);
       }
     }
   };
@@ -940,14 +970,13 @@ void output_kernel(Params pr) {
   // par: the row starts in the upper half of its first word (bf16, odd
   // level count)
   const unsigned long long lmask = MASKED ? pr.lmask : ~0ull;
-  auto lam_at = [&](auto cur_c, int k, int t, int lvl, int par) __attribute__((always_inline)) -> float {
-    const unsigned* lw = lam_w + (Cfg::CB2 ? decltype(cur_c)::value * HP * C * LW : 0);
+  auto lam_at = [&](int k, int t, int lvl, int par) __attribute__((always_inline)) -> float {
     const int row = k * C + t;
     float v;
     if constexpr (sizeof(T) == 4) {
-      v = __uint_as_float(lw[row * LW + lvl]);
+      v = __uint_as_float(lam_w[row * LW + lvl]);
     } else {
-      const unsigned short* hw = reinterpret_cast<const unsigned short*>(lw);
+      const unsigned short* hw = reinterpret_cast<const unsigned short*>(lam_w);
       v = __uint_as_float((unsigned)hw[2 * row * LW + par + lvl] << 16);
     }
     if constexpr (MASKED) return (lmask >> lvl) & 1 ? v : 0.f;  // left-out levels weigh 0
@@ -956,8 +985,8 @@ void output_kernel(Params pr) {
   const bool intra_on = !MASKED || (lmask & ((2ull << c_log) - 1)) != 0;  // levels 0..log2 C
   const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
-  issue_c(j0, csh0, tid0 & 63);
-  issue_lam(j0, lam_w, tid0 & 63);
+  issue_c(j0, tid0 & 63);
+  issue_lam(j0, tid0 & 63);
   issue_regs(j0, tid0);
 
   // one chunk per call; CUR selects the B / X buffer pair at compile time
@@ -967,10 +996,6 @@ void output_kernel(Params pr) {
     T* xsb = CUR ? xsh1 : xsh0;
     T* bs_next = NBUF == 2 ? (CUR ? bsh0 : bsh1) : bsh0;
     T* xs_next = NBUF == 2 ? (CUR ? xsh0 : xsh1) : xsh0;
-    constexpr int CURC = Cfg::CB2 ? CUR : 0;
-    T* csh = CURC ? csh1 : csh0;
-    T* cs_next = CURC ? csh0 : csh1;
-    unsigned* lw_next = lam_w + (1 - CURC) * HP * C * LW;
     const int j = j0 + jl;
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const bool need_state = jl + 1 < nch;
@@ -985,13 +1010,7 @@ void output_kernel(Params pr) {
     if (wv == 0) chunk_decays<T, C>(la, cum_h, ecum_h, wst_h, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     lds_barrier();
-    if (NBUF == 2 && need_state) {  // the other buffers are free
-      issue_bx(j + 1, bs_next, xs_next, lane);
-      if constexpr (Cfg::CB2) {
-        issue_c(j + 1, cs_next, lane);
-        issue_lam(j + 1, lw_next, lane);
-      }
-    }
+    if (NBUF == 2 && need_state) issue_bx(j + 1, bs_next, xs_next, lane);  // other pair is free
     const float atot = cum_h[C - 1];
 
     // ---- intra-chunk weights W[t][s] of every head, from the shared
@@ -1017,7 +1036,7 @@ void output_kernel(Params pr) {
           for (int i = 0; i < 4; ++i) {
             const int s = 16 * sb + 4 * g + i;
             wv4[i] = (s <= t) ? acc[i] * M::ex(ct_ - cum[k * C + s]) *
-                                    lam_at(cur_c, k, t, bit_length(t ^ s), par)
+                                    lam_at(k, t, bit_length(t ^ s), par)
                               : 0.f;
           }
         }
@@ -1047,7 +1066,7 @@ void output_kernel(Params pr) {
       auto level_scale = [&](int tb, int level, float eD) __attribute__((always_inline)) {
         const int t = 16 * tb + r;
         // 16 tb keeps the parity of the row start: H * 16 tb is even
-        return lam_at(cur_c, hh, t, level, par_r) * ecum_h[t] * eD;
+        return lam_at(hh, t, level, par_r) * ecum_h[t] * eD;
       };
 
       // Levels whose slots are in registers (the segment's resident ones and
@@ -1136,10 +1155,8 @@ void output_kernel(Params pr) {
     }
 
     if (need_state) {
-      if constexpr (!Cfg::CB2) {
-        issue_c(j + 1, csh0, lane);
-        issue_lam(j + 1, lam_w, lane);
-      }
+      issue_c(j + 1, lane);
+      issue_lam(j + 1, lane);
       issue_regs(j + 1, tid);  // land during the state MFMAs
 
       // ---- this chunk's state, pushed on the local Fenwick stack

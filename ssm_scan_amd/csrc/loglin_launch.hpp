@@ -17,7 +17,7 @@ template <class T, int C, int P, int N, int HP>
 void launch_output(Params pr, hipStream_t st) {
   using Cfg = OutCfg<T, C, P, N, HP>;
   pr.total = pr.batch * pr.ns * (pr.nheads / HP);
-  const size_t shm = (size_t)(Cfg::CB2 ? 2 : 1) * HP * C * lam_words(pr.ll, (int)sizeof(T)) * 4;
+  const size_t shm = (size_t)HP * C * lam_words(pr.ll, (int)sizeof(T)) * 4;
   if (pr.lmask == ~0ull)
     hipLaunchKernelGGL((output_kernel<T, C, P, N, HP, false>), dim3(pad8(pr.total)), dim3(Cfg::NT), shm, st, pr);
   else
