@@ -361,7 +361,9 @@ __device__ inline unsigned lds_addr(const void* p) {
 // 1 KB of LDS and every lane fetches the global block that belongs there.
 // The copy is asynchronous: s_waitcnt and a barrier precede any read.
 // g is uniform; R rows of the stride fit 32-bit byte offsets (the host
-// bounds heads and state sizes far below that).
+// bounds heads and state sizes far below that).  The row offset is a 24-bit
+// multiply (full rate; a 32-bit one takes four passes): rows are below 64
+// and the host's bounds keep the row stride below 2^22 bytes.
 template <class T, int R, int W, int NW>
 __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, int lane) {
   using L = Rows<T, W>;
@@ -378,7 +380,7 @@ __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, in
       // (lanes past a short tile write nothing)
       const int row = piece / L::NBLK, pb = piece % L::NBLK;
       const int lb = (pb ^ row) & (L::NBLK - 1);
-      dma_16x64_at(g, (unsigned)row * rs + (unsigned)(lb * 16), lds_addr(lds) + inst * 1024u);
+      dma_16x64_at(g, __umul24((unsigned)row, rs) + (unsigned)(lb * 16), lds_addr(lds) + inst * 1024u);
     }
   }
 }
@@ -959,7 +961,9 @@ void output_kernel(Params pr) {
       if (idx < words) {
         const int tw = (int)(((float)idx + 0.5f) * inv_lw), w = idx - tw * LW;  // tw = head * C + token
         const int k = tw / C, t = tw - k * C;
-        const int x = (t * H + k) * L;  // element offset of the row from eb
+        // element offset of the row from eb (24-bit multiplies: t < 64 and
+        // the host bounds H by 4096 and L by 64)
+        const int x = (int)__umul24((unsigned)t, (unsigned)(H * L)) + (int)__umul24((unsigned)k, (unsigned)L);
         unsigned ow = (unsigned)((sizeof(T) == 4 ? x : ((x + par0) >> 1)) + w);
         ow = ow < lim ? ow : lim;
         dma_4x64_at(base, ow * 4u, lds_addr(lam_w) + inst * 256u);
@@ -1031,7 +1035,7 @@ void output_kernel(Params pr) {
         f32x4 wv4 = {0.f, 0.f, 0.f, 0.f};
         if (sb <= tb) {
           const float ct_ = cum[k * C + t];
-          const int par = lpar & (((int)row0 + t) * H + h0 + k);
+          const int par = lpar & ((((int)row0 + t) & H) ^ (h0 + k));  // parity of (row0 + t) H + h0 + k
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int s = 16 * sb + 4 * g + i;
@@ -1048,7 +1052,7 @@ void output_kernel(Params pr) {
     // ---- output tiles: intra block, then every active inter-chunk level
     {
       T* wth = wt + hh * WTS;
-      const int par_r = lpar & (((int)row0 + r) * H + h);  // parity of token 16 tb + r
+      const int par_r = lpar & ((((int)row0 + r) & H) ^ h);  // parity of (row0 + r) H + h: token 16 tb + r
       f32x4 Y[Tl::TB];
 #pragma unroll
       for (int tb = 0; tb < Tl::TB; ++tb) {
