@@ -1033,7 +1033,17 @@ void output_kernel(Params pr) {
 #pragma unroll
       for (int k = 0; k < HP; ++k) {
         f32x4 wv4 = {0.f, 0.f, 0.f, 0.f};
-        if (sb <= tb) {
+        if (sb < tb) {
+          // Below the diagonal blocks every s precedes t, and t XOR s =
+          // 16 (tb XOR sb) + (r XOR (s mod 16)) has bit length
+          // 4 + bitlen(tb XOR sb) across the whole tile: one level weight.
+          const float ct_ = cum[k * C + t];
+          const int par = lpar & ((((int)row0 + t) & H) ^ (h0 + k));  // parity of (row0 + t) H + h0 + k
+          const float lt = lam_at(k, t, 4 + bit_length((unsigned)(tb ^ sb)), par);
+          const f32x4 cs4 = *reinterpret_cast<const f32x4*>(cum + k * C + 16 * sb + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv4[i] = acc[i] * M::ex(ct_ - cs4[i]) * lt;
+        } else if (sb == tb) {
           const float ct_ = cum[k * C + t];
           const int par = lpar & ((((int)row0 + t) & H) ^ (h0 + k));  // parity of (row0 + t) H + h0 + k
 #pragma unroll
