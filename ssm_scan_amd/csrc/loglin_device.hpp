@@ -1107,13 +1107,22 @@ void output_kernel(Params pr) {
         frag cf[Tl::NKN];  // C^T fragments of the block, in state order
 #pragma unroll
         for (int kk = 0; kk < Tl::NKN; ++kk) cf[kk] = rows_state_frag<T, N>(csh, 16 * tb + r, kk, g);
+        // Every level's scale of the block is read up front, whether or not
+        // the level is active (an inactive one reads a weight of the row,
+        // clamped to the levels it holds, and is never used), so that no
+        // product waits on a weight read issued just before it.
+        float sres[RZ], sloc[MM];
+#pragma unroll
+        for (int i = 0; i < RZ; ++i) sres[i] = level_scale(tb, min(lres[i], LL - 1), eres[i]);
+#pragma unroll
+        for (int e = 0; e < MM; ++e) sloc[e] = level_scale(tb, min(c_log + e + 1, LL - 1), eloc[e]);
 #pragma unroll
         for (int i = 0; i < RZ; ++i) {
           if (i < nres && (!MASKED || ((lmask >> lres[i]) & 1))) {
             f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zres[i][kk], cf[kk], tmp);
-            Y[tb] += level_scale(tb, lres[i], eres[i]) * tmp;
+            Y[tb] += sres[i] * tmp;
           }
         }
 #pragma unroll
@@ -1122,7 +1131,7 @@ void output_kernel(Params pr) {
             f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < Tl::NKN; ++kk) tmp = M::mma(zl[e][kk], cf[kk], tmp);
-            Y[tb] += level_scale(tb, c_log + e + 1, eloc[e]) * tmp;
+            Y[tb] += sloc[e] * tmp;
           }
         }
       }
