@@ -67,6 +67,9 @@ def test_valid_arguments_pass_validation():
     (dict(io_dtype=7), 64, -7),
     (dict(headdim=48), 64, -10), (dict(dstate=96), 64, -10),
     (dict(dstate=16), 64, -10),
+    # upper bounds the kernels' 24- and 32-bit offset arithmetic relies on
+    (dict(nheads=8192, ngroups=4096), 64, -2), (dict(nlevels=65), 64, -2),
+    (dict(batch=2048), 64, -2),
 ])
 def test_dimension_errors(kw, chunk, code):
     assert validate(good_dims(**kw), chunk=chunk, ws_bytes=1 << 40) == code
