@@ -744,24 +744,38 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
 // register stack for.
 constexpr int MAX_SEG_LOG2 = 3;
 
-// Score tiles of the intra-chunk block, causal ones (sb <= tb) first so that
-// dealing them round-robin to the waves balances the MFMA work.
-template <int TB>
+// Score tiles of the intra-chunk block in the order they are dealt
+// round-robin to the waves: the TB diagonal tiles first (the dearest: a
+// level and a causality test per element), then the tiles below them, then
+// the strictly upper tiles the intra product reads, as zeros.  With 32
+// tokens per MFMA contraction (bf16) token block tb reads columns up to the
+// end of its 32-token half, so those are (tb, tb + 1) for even tb; with 4
+// (fp32) it reads no upper tile.
+template <int TB, int KB>
+struct ScoreTiles {
+  static constexpr int NO = TB * (TB - 1) / 2;       // below the diagonal
+  static constexpr int NZ = KB == 32 ? TB / 2 : 0;  // upper tiles read as zeros
+  static constexpr int N = TB + NO + NZ;
+};
+template <int TB, int KB>
 __device__ inline void score_tile(int u, int& tb, int& sb) {
-  constexpr int NCAUSAL = TB * (TB + 1) / 2;
-  if (u < NCAUSAL) {
-    tb = 0;
-    while ((tb + 1) * (tb + 2) / 2 <= u) ++tb;
-    sb = u - tb * (tb + 1) / 2;
-  } else {
-    int k = u - NCAUSAL;  // strictly upper tiles, row-major
-    tb = 0;
-    while (k >= TB - 1 - tb) {
-      k -= TB - 1 - tb;
+  static_assert(KB == 32 || KB == 4, "contraction lengths");
+  if (u < TB) {
+    tb = sb = u;
+    return;
+  }
+  u -= TB;
+  if (u < ScoreTiles<TB, KB>::NO) {  // row-major: (1,0), (2,0), (2,1), (3,0), ...
+    tb = 1;
+    while (u >= tb) {
+      u -= tb;
       ++tb;
     }
-    sb = tb + 1 + k;
+    sb = u;
+    return;
   }
+  tb = 2 * (u - ScoreTiles<TB, KB>::NO);
+  sb = tb + 1;
 }
 
 // One work-group per (batch, segment of 2^m chunks, HP heads of one group);
@@ -1019,9 +1033,10 @@ void output_kernel(Params pr) {
 
     // ---- intra-chunk weights W[t][s] of every head, from the shared
     // transposed scores B C^T
-    for (int u = intra_on ? wave : Tl::TB * Tl::TB; u < Tl::TB * Tl::TB; u += NTW) {
+    constexpr int NSC = ScoreTiles<Tl::TB, Tl::KB>::N;
+    for (int u = intra_on ? wave : NSC; u < NSC; u += NTW) {
       int tb, sb;
-      score_tile<Tl::TB>(u, tb, sb);
+      score_tile<Tl::TB, Tl::KB>(u, tb, sb);
       const int t = 16 * tb + r;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (sb <= tb) {
