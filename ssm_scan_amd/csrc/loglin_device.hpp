@@ -247,16 +247,33 @@ struct Tiles {
 //   cum[t]  inclusive prefix sum of log a over the chunk (fp32),
 //   ecum[t] = exp(cum[t])            (decay from the chunk start to t),
 //   wst[t]  = exp(cum[C-1] - cum[t]) (decay from t to the chunk end).
+// The prefix sum runs on DPP lane moves inside the wave (no LDS round
+// trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the
+// last lane of each row is added to the rows after it (row_bcast:15 and
+// row_bcast:31).  Only the first C lanes are used.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_shift_add(float v) {
+  // lanes whose source is outside the move (or whose row is masked off)
+  // add the old value 0
+  const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false);
+  return v + __builtin_bit_cast(float, t);
+}
+template <int C>
+__device__ inline float wave_prefix_sum(float v) {
+  v = dpp_shift_add<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_shift_add<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_shift_add<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_shift_add<0x118, 0xf>(v);  // row_shr:8
+  if constexpr (C > 16) v = dpp_shift_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  if constexpr (C > 32) v = dpp_shift_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 template <class T, int C>
 __device__ inline void chunk_decays(float la, float* cum, float* ecum, float* wst, int tid) {
-  if (tid < 64) {
-    float v = la;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      float o = __shfl_up(v, d, 64);
-      if (tid >= d) v += o;
-    }
-    const float tot = __shfl(v, C - 1, 64);
+  if (tid < 64) {  // one whole wave: the lane moves need every lane active
+    const float v = wave_prefix_sum<C>(la);
+    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), C - 1));
     if (tid < C) {
       cum[tid] = v;
       ecum[tid] = Mfma<T>::ex(v);
