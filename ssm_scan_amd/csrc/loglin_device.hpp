@@ -762,7 +762,8 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
 constexpr int MAX_SEG_LOG2 = 3;
 
 // Score tiles of the intra-chunk block in the order they are dealt
-// round-robin to the waves: the TB diagonal tiles first (the dearest: a
+// round-robin to the waves, so that every wave has a like share of the
+// dearest tiles before the barrier that follows: the diagonal ones (a
 // level and a causality test per element), then the tiles below them, then
 // the strictly upper tiles the intra product reads, as zeros.  With 32
 // tokens per MFMA contraction (bf16) token block tb reads columns up to the
@@ -777,6 +778,19 @@ struct ScoreTiles {
 template <int TB, int KB>
 __device__ inline void score_tile(int u, int& tb, int& sb) {
   static_assert(KB == 32 || KB == 4, "contraction lengths");
+  if constexpr (TB == 4 && KB == 32) {
+    // 64-token chunks (4 diagonal D, 6 lower O and 2 zero Z tiles): four
+    // O, the four D, then O, O, Z, Z.  Dealt to 4 waves: D+2O, D+2O,
+    // D+O+Z, D+O+Z; to 8 waves (two heads): 2O, 2O, O+Z, O+Z, D, D, D, D.
+    // (one nibble 4 tb + sb per tile, in scalar arithmetic: an indexed
+    // constant array would be a memory load whose wait also waits for the
+    // copies in flight)
+    constexpr unsigned long long order = 0xb1edfa50c984ull;
+    const unsigned e = (unsigned)(order >> (4 * u)) & 15u;
+    tb = (int)(e >> 2);
+    sb = (int)(e & 3);
+    return;
+  }
   if (u < TB) {
     tb = sb = u;
     return;
