@@ -283,16 +283,36 @@ __device__ inline void chunk_decays(float la, float* cum, float* ecum, float* ws
 }
 
 // A tile of token rows (B, C or X of one chunk) staged in LDS unpadded, W
-// elements per row; the 16-byte blocks of row t are XOR-swizzled by
-// t mod (blocks per row).  This keeps the MFMA operand loads (16 rows x one
-// block, the state-order 8-byte halves, and the transposing 8-byte reads of
-// four consecutive rows) free of bank conflicts.
+// elements per row, with the 16-byte blocks of row t XOR-swizzled by a key
+// k(t).  The reads it serves: 16 rows x one block (row-wise MFMA operands,
+// 16 lanes per LDS cycle), the state-order 8-byte halves of 16 rows, and
+// the transposing 8-byte reads of rows {R..R+3} and {R+8..R+11} x two
+// neighbouring blocks (32 lanes per LDS cycle); the output rows are written
+// 8 bytes a lane and read back 16.  For bf16 the keys keep all of these
+// free of bank conflicts (checked against a model of 64 four-byte banks):
+//   256-byte rows (16 blocks, a row spans every bank): k(t) must differ
+//     between the 16 rows of an aligned group, and k(t)/2 between the eight
+//     rows of one transposing read: k = 2 (t mod 4) + 8 (t/8 mod 2) + (t/4 mod 2);
+//   128-byte rows (8 blocks, two rows per bank sweep): k must differ
+//     between the even (and between the odd) rows of an aligned group of
+//     16, and k/2 between the even (odd) rows of one transposing read:
+//     k = 2 (t/2 mod 2) + 4 (t/8 mod 2) + (t/4 mod 2).
+// Other shapes use k(t) = t mod (blocks per row).
 template <class T, int W>
 struct Rows {
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int NBLK = W / VEC;
+  // physical 16-byte block of logical block b in row `row` (an involution)
+  __device__ static inline int blk(int row, int b) {
+    if constexpr (sizeof(T) == 2 && NBLK == 16)
+      return b ^ (((row & 3) << 1) | (((row >> 3) & 1) << 3) | ((row >> 2) & 1));
+    else if constexpr (sizeof(T) == 2 && NBLK == 8)
+      return b ^ ((((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2) | ((row >> 2) & 1));
+    else
+      return (b ^ row) & (NBLK - 1);
+  }
   __device__ static inline int at(int row, int c) {
-    return row * W + ((((c / VEC) ^ row) & (NBLK - 1)) * VEC) + (c % VEC);
+    return row * W + blk(row, c / VEC) * VEC + (c % VEC);
   }
 };
 
@@ -396,7 +416,7 @@ __device__ inline void rows_to_lds(const T* g, int64_t grs, T* lds, int wave, in
     if ((INSTS % NW == 0 || inst < INSTS) && (PIECES % 64 == 0 || piece < PIECES)) {
       // (lanes past a short tile write nothing)
       const int row = piece / L::NBLK, pb = piece % L::NBLK;
-      const int lb = (pb ^ row) & (L::NBLK - 1);
+      const int lb = L::blk(row, pb);  // logical block that lands in physical block pb
       dma_16x64_at(g, __umul24((unsigned)row, rs) + (unsigned)(lb * 16), lds_addr(lds) + inst * 1024u);
     }
   }
