@@ -1005,7 +1005,8 @@ void output_kernel(Params pr) {
   auto issue_regs = [&](int j, int tid) __attribute__((always_inline)) {
     const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
     const int lane = tid & 63, r = lane & 15, g = lane >> 4;
-    la = (wv == 0 && lane < C) ? pr.log_a[(r0 + lane) * H + h] : 0.f;
+    // the last wave of each head: the first issues the odd level-weight copy
+    la = (wv == Cfg::NWH - 1 && lane < C) ? pr.log_a[(r0 + lane) * H + h] : 0.f;
   };
   // level weights of chunk j into lam_w (the last word of the tensor bounds
   // the copy: a row's padding words may run past the end)
@@ -1075,8 +1076,8 @@ void output_kernel(Params pr) {
     const int lane = tid & 63, g = lane >> 4, r = lane & 15;
     const T* xs = xsb + hh * KC * P;
 
-    // ---- per-token decays of the chunk (first wave of each head)
-    if (wv == 0) chunk_decays<T, C>(la, cum_h, ecum_h, wst_h, lane);
+    // ---- per-token decays of the chunk (last wave of each head)
+    if (wv == Cfg::NWH - 1) chunk_decays<T, C>(la, cum_h, ecum_h, wst_h, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the chunk have landed
     lds_barrier();
     if (NBUF == 2 && need_state) issue_bx(j + 1, bs_next, xs_next, lane);  // other pair is free
