@@ -140,22 +140,34 @@ def _oracle_task(args):
     from oracle import loglin_ref
     d = _ORACLE_DATA
     with threadpool_limits(1):
-        loglin_ref.loglin_rows(d["X"], d["B"], d["C"], d["log_a"], d["lam"], 0, h,
-                               np.asarray(rows))
-    return len(rows)
+        vals = loglin_ref.loglin_rows(d["X"], d["B"], d["C"], d["log_a"], d["lam"], 0, h,
+                                      np.asarray(rows))
+    return h, rows, vals
+
+
+# the GPU machine gives one GPU a 16-core share of its host, whatever
+# os.cpu_count() reports there
+CPU_SHARE = 16
 
 
 def cpu_baseline(cfg, d, budget_s: float) -> dict:
     """Time the fp64 oracle on uniformly random output rows (all heads) of
     the workload: rows cost O(t) each, so random rows give an unbiased
     per-token rate of the full O(T^2) oracle.  Runs in a fork pool before
-    the GPU is touched."""
+    the GPU is touched.  The rows it computes are kept (``check``) so that
+    the timed GPU output can be compared with them afterwards."""
     global _ORACLE_DATA
     _ORACLE_DATA = d
-    workers = max(1, min(16, os.cpu_count() or 1))
+    host = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = host
+    workers = max(1, min(CPU_SHARE, avail))
     rng = np.random.default_rng(1234)
     order = rng.permutation(cfg.seqlen)
     ctx = mp.get_context("fork")
+    check = []
     with ctx.Pool(workers) as pool:
         # warm the workers (imports), then calibrate on two rows per worker
         pool.map(_oracle_task, [(0, [0])] * workers)
@@ -171,8 +183,9 @@ def cpu_baseline(cfg, d, budget_s: float) -> dict:
                  for i in range(0, cap, blk) for h in range(cfg.nheads)]
         done = 0
         t0 = time.perf_counter()
-        for n in pool.imap_unordered(_oracle_task, tasks, chunksize=1):
-            done += n
+        for h, rows, vals in pool.imap_unordered(_oracle_task, tasks, chunksize=1):
+            done += len(rows)
+            check.append((h, rows, vals))
             if time.perf_counter() - t0 >= budget_s:
                 break
         el = time.perf_counter() - t0
@@ -183,13 +196,67 @@ def cpu_baseline(cfg, d, budget_s: float) -> dict:
         "value": tokens / el,
         "unit": "tokens/s",
         "cores": workers,
+        "host_cpus": host,
         "kind": "oracle",
         "sample": (f"{done} (head, row) outputs = {tokens:.1f} tokens of the "
                    f"{cfg.seqlen}-token workload at uniformly random rows, each "
                    f"from its full causal prefix (fp64 numpy, {workers} processes "
-                   f"x 1 BLAS thread, {el:.1f} s)"),
+                   f"x 1 BLAS thread; the pool is capped at the {CPU_SHARE}-core "
+                   f"share of the host a GPU gets, the host has {host} CPUs; "
+                   f"{el:.1f} s)"),
         "seconds": el,
+        "check": check,
     }
+
+
+def check_against_sample(out, check, max_pairs=4096) -> dict:
+    """Max relative error of the timed output at the oracle rows the CPU
+    baseline computed: per head, max |out - ref| / max |ref| over its
+    sampled rows; the worst head is reported."""
+    import torch
+
+    by_head = {}
+    n = 0
+    for h, rows, vals in check:
+        if n >= max_pairs:
+            break
+        by_head.setdefault(h, []).append((rows, vals))
+        n += len(rows)
+    worst, rows_used = 0.0, 0
+    for h, items in by_head.items():
+        rows = np.concatenate([np.asarray(r) for r, _ in items])
+        ref = np.concatenate([v for _, v in items], axis=0)
+        got = out[0, torch.from_numpy(rows).to(out.device), h, :].float().cpu().numpy()
+        if not np.isfinite(got).all():
+            return {"max_rel_err": float("inf"), "rows": int(rows.size), "heads": len(by_head)}
+        worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+        rows_used += rows.size
+    return {"max_rel_err": worst, "row_heads": int(rows_used), "heads": len(by_head),
+            "tolerance": 2e-2 if out.dtype == torch.bfloat16 else 1e-4,
+            "against": "fp64 oracle rows of the cpu_baseline sample"}
+
+
+def measure_copy_gbs(dev, mib=1024, reps=10) -> float:
+    """Achieved HBM bandwidth of a plain device-to-device copy of `mib` MiB
+    (read + write bytes over its duration, HIP events on the stream)."""
+    import torch
+
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (mib << 20) / sec / 1e9
 
 
 # ----------------------------------------------------------- GPU timing
@@ -286,6 +353,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    print("[bench] plain copy bandwidth", file=sys.stderr, flush=True)
+    copy_gbs = measure_copy_gbs(dev)
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -320,17 +389,32 @@ def main():
     achieved_gbs = alg["bytes"][dom] / dur / 1e9
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     dom_tflops = alg["flops"][dom] / dur / 1e12
+    # the bound that applies: the kernel's algorithmic flops per byte against
+    # the machine balance (peak flops over peak bytes)
+    intensity = alg["flops"][dom] / alg["bytes"][dom]
+    balance = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if intensity < balance else "mfma"
+    if bound == "hbm":
+        ach, peak, unit = achieved_gbs, HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = dom_tflops, mfma_peak, "TFLOP/s"
     roofline = {
-        "bound": "hbm",
+        "bound": bound,
         "kernel": f"{dom}_kernel",
-        "achieved": round(achieved_gbs, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "achieved": round(ach, 1),
+        "peak": peak,
+        "unit": unit,
+        "frac": round(ach / peak, 4),
         "traffic": counter_traffic(f"{dom}_kernel"),
         "alg_bytes_per_launch": alg["bytes"][dom],
+        "alg_flops_per_launch": alg["flops"][dom],
+        "intensity_flop_per_byte": round(intensity, 1),
+        "machine_balance_flop_per_byte": round(balance, 1),
         "avg_launch_ms": round(stage_ms[dom], 4),
+        "measured_copy_gbs": round(copy_gbs, 1),
+        "frac_of_measured_copy": round(achieved_gbs / copy_gbs, 4),
     }
+    check = None if cpu is None else check_against_sample(out, cpu["check"])
     path_tflops = alg["flops_total"] / step_s / 1e12
     res = {
         "metric": METRIC,
@@ -367,13 +451,19 @@ def main():
             "alg_bytes_per_step": alg["bytes_total"],
             "achieved": round(alg["bytes_total"] / step_s / 1e9, 1),
             "frac": round(alg["bytes_total"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+            "frac_of_measured_copy": round(alg["bytes_total"] / step_s / 1e9 / copy_gbs, 4),
         },
+        "parity_check": check,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "gpu_event_ms_per_step": round(gpu_s / K * 1e3, 4),
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
-                                                  ("value", "unit", "cores", "kind", "sample")},
+                                                  ("value", "unit", "cores", "host_cpus", "kind",
+                                                   "sample")},
     }
     print(json.dumps(res), flush=True)
+    if check is not None and not check["max_rel_err"] <= check["tolerance"]:
+        print(f"bench.py: the timed output misses the oracle rows: {check}", file=sys.stderr)
+        sys.exit(1)
 
 
 def main_naive(args, cfg, t, out, ws, stream, fused_step):

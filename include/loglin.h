@@ -79,7 +79,12 @@ enum {
 
 /* Problem sizes.  headdim = P (value dim), dstate = N (state dim),
  * nlevels = L (weights per token and head).  Supported: headdim in
- * {16, 32, 64}; dstate in {32, 64, 128}, plus 16 for LOGLIN_F32. */
+ * {16, 32, 64}; dstate in {32, 64, 128}, plus 16 for LOGLIN_F32.
+ * Bounds of the 32-bit index arithmetic and the launch grids (else
+ * LOGLIN_ERR_DIM): seqlen <= 2^30, nheads <= 4096, nlevels <= 64,
+ * batch * nheads <= 65535, batch * nheads * (seqlen / chunk) <= 2^30, and
+ * at most 2^16 segments of 2^seg_log2 chunks (seqlen / chunk <= 2^19 at the
+ * default depth of 8 chunks per segment). */
 typedef struct {
   int64_t batch;
   int64_t seqlen;
@@ -220,7 +225,9 @@ int loglin_decode_step(void* state, int64_t t, const void* X, const void* B,
  * Supported: bf16 with chunk 32 or 64, headdim 32 or 64, dstate 32..128;
  * float32 with chunk 16..64 and the forward's (headdim, dstate) pairs
  * except headdim 64 with dstate 128 at chunk 64 (LDS); otherwise
- * LOGLIN_ERR_SHAPE.  seqlen <= 2^31.  Errors as for loglin_fwd, all
+ * LOGLIN_ERR_SHAPE.  Size bounds as for loglin_fwd (seqlen <= 2^30, at most
+ * 2^19 chunks), else LOGLIN_ERR_DIM.
+ * Errors as for loglin_fwd, all
  * checked on the host before any HIP call.  The workspace (at least
  * loglin_bwd_workspace_bytes bytes, 256-byte aligned, contents ignored on
  * entry) must not be used by other work until the call's kernels finish. */

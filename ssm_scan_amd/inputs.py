@@ -161,6 +161,8 @@ def make_inputs(cfg: Config, seed: int = 0, *, variant: str | None = None):
       - "lam_intra": lambda zero on every level above log2(chunk)
       - "lam_inter": lambda zero on levels 0..log2(chunk)
       - "lam_ones":  lambda = 1 everywhere
+    Several modifications join with "+", applied left to right (for
+    instance "slow_decay+lam_onehot_14").
     """
     sh = cfg.shapes()
     f32 = np.float32
@@ -181,26 +183,26 @@ def make_inputs(cfg: Config, seed: int = 0, *, variant: str | None = None):
         raise ValueError(cfg.decay)
     lam = _softplus(_normal(seed, 4, sh["lam"]))
 
-    if variant is not None:
+    for mod in ([] if variant is None else variant.split("+")):
         c = cfg.chunk.bit_length() - 1
-        if variant == "slow_decay":
+        if mod == "slow_decay":
             log_a = (log_a * f32(1e-3)).astype(f32)
-        elif variant == "no_decay":
+        elif mod == "no_decay":
             log_a = np.zeros_like(log_a)
-        elif variant.startswith("lam_onehot_"):
-            lev = int(variant.rsplit("_", 1)[1])
+        elif mod.startswith("lam_onehot_"):
+            lev = int(mod.rsplit("_", 1)[1])
             lam = np.zeros_like(lam)
             lam[..., lev] = 1.0
-        elif variant == "lam_intra":
+        elif mod == "lam_intra":
             lam = lam.copy()
             lam[..., c + 1:] = 0.0
-        elif variant == "lam_inter":
+        elif mod == "lam_inter":
             lam = lam.copy()
             lam[..., :c + 1] = 0.0
-        elif variant == "lam_ones":
+        elif mod == "lam_ones":
             lam = np.ones_like(lam)
         else:
-            raise ValueError(f"unknown variant {variant!r}")
+            raise ValueError(f"unknown variant {mod!r}")
 
     out = dict(log_a=np.ascontiguousarray(log_a, dtype=f32))
     if cfg.dtype == "bf16":

@@ -198,6 +198,15 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _stream_workspace(need, dev, stream):
+    """A uint8 device buffer of `need` bytes for kernels enqueued on
+    `stream`, allocated from that stream's pool: once the caller drops it,
+    the caching allocator hands the block only to later work on the same
+    stream, which runs after those kernels."""
+    with torch.cuda.stream(stream):
+        return torch.empty(need, dtype=torch.uint8, device=dev)
+
+
 def loglin_fwd(X, B, C, log_a, lam, chunk, out, *, workspace=None, stream=None,
                seg_log2=None, stage_events=None, heads_per_block=None, level_mask=None):
     """Enqueue O = (C B^T . M^H) X into `out` on `stream` (default: torch's
@@ -222,11 +231,11 @@ def loglin_fwd(X, B, C, log_a, lam, chunk, out, *, workspace=None, stream=None,
     opts = _opts(seg_log2, stage_events, heads_per_block, level_mask)
     popts = ctypes.byref(opts) if opts is not None else None
     need = int(lib().loglin_workspace_bytes_ex(ctypes.byref(dims), int(chunk), popts))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None and need > 0:
+        workspace = _stream_workspace(need, dev, stream)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     sptr = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().loglin_fwd_ex(_ptr(X), _ptr(B), _ptr(C), _ptr(log_a), _ptr(lam), int(chunk),
                              _ptr(out), ctypes.byref(dims), _ptr(workspace), ws_bytes, sptr,
@@ -315,11 +324,11 @@ def loglin_bwd(X, B, C, log_a, lam, dO, chunk, dX, dB, dC, dlog_a, dlam, *, work
                                ("dlam", dlam, (Bt, T, H, L), io)):
         _check_tensor(name, t, shape, dt, dev)
     need = loglin_bwd_workspace_bytes(dims, chunk)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None and need > 0:
+        workspace = _stream_workspace(need, dev, stream)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().loglin_bwd(_ptr(X), _ptr(B), _ptr(C), _ptr(log_a), _ptr(lam), _ptr(dO), int(chunk),
                           _ptr(dX), _ptr(dB), _ptr(dC), _ptr(dlog_a), _ptr(dlam),
                           ctypes.byref(dims), _ptr(workspace), ws_bytes,
@@ -371,11 +380,11 @@ def loglin_gdn_fwd(q, k, v, log_alpha, beta, lam, out, *, workspace=None, stream
         _check_tensor(name, t, shape, d, dev)
     dims = make_dims(Bt, T, H, H, P, N, L, dt)
     need = loglin_gdn_workspace_bytes(dims)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None and need > 0:
+        workspace = _stream_workspace(need, dev, stream)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().loglin_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(lam),
                               _ptr(out), ctypes.byref(dims), _ptr(workspace), ws_bytes,
                               ctypes.c_void_p(stream.cuda_stream))

@@ -232,3 +232,21 @@ def test_gdn_argument_errors():
     assert call(ok, nbytes=need - 1) == -8
     assert call(ok, ws=ctypes.c_void_p(0x10010)) == -9  # workspace alignment
     assert lib.loglin_gdn_workspace_bytes(ctypes.byref(L.make_dims(1, 48, 2, 2, 64, 128, 7, 1))) == 0
+
+
+def test_seqlen_upper_bound():
+    """The header's size bounds, shared by the forward and the backward:
+    seqlen <= 2^30 and at most 2^16 segments of 8 chunks (2^19 chunks).  The
+    largest valid length plans a workspace; one chunk more is
+    LOGLIN_ERR_DIM before any device call, as is a length past 2^30."""
+    lim = 64 << 19
+    ok = good_dims(seqlen=lim, nheads=1, ngroups=1, nlevels=26)
+    for bad in (good_dims(seqlen=lim + 64, nheads=1, ngroups=1, nlevels=27),
+                good_dims(seqlen=(1 << 30) + 64, nheads=1, ngroups=1, nlevels=32)):
+        assert validate(bad, ws_bytes=1 << 62) == -2
+        assert L.lib().loglin_bwd_workspace_bytes(ctypes.byref(bad), 64) == 0
+        rc = L.lib().loglin_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, ctypes.byref(bad), FAKE, 1 << 62, None)
+        assert rc == -2
+    assert validate(ok, ws_bytes=1 << 62) == 0
+    assert L.lib().loglin_bwd_workspace_bytes(ctypes.byref(ok), 64) > 0
