@@ -33,7 +33,9 @@
  * Ownership: every pointer argument except `dims`/`opts` is a device
  * pointer owned by the caller.  The library keeps no pointer after a call
  * returns, allocates no device memory and has no global mutable state; it
- * is safe to call from several host threads on different streams.
+ * is safe to call from several host threads on different streams.  (The
+ * one exception is loglin_fwd_noalloc below, which uses a fixed scratch
+ * array of the library instead of a caller's workspace.)
  *
  * Asynchrony: loglin_fwd only enqueues kernels on `stream` (a hipStream_t,
  * NULL = the default stream) and returns.  Device faults surface at the
@@ -74,7 +76,8 @@ enum {
   LOGLIN_ERR_ALIGN = -9,       /* a pointer is not 16-byte aligned */
   LOGLIN_ERR_SHAPE = -10,      /* (headdim, dstate) not supported */
   LOGLIN_ERR_HIP = -11,        /* a HIP call failed */
-  LOGLIN_ERR_OPTS = -12        /* an option is out of range */
+  LOGLIN_ERR_OPTS = -12,       /* an option is out of range */
+  LOGLIN_ERR_SCRATCH = -13     /* workspace larger than loglin_fwd_noalloc's array */
 };
 
 /* Problem sizes.  headdim = P (value dim), dstate = N (state dim),
@@ -160,6 +163,36 @@ const char* loglin_strerror(int code);
  * error code on invalid arguments.  Host only. */
 int loglin_plan_seg_log2(const loglin_dims* dims, int chunk,
                          const loglin_opts* opts);
+
+/* ---- Forward without allocation -----------------------------------------
+ *
+ * For callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph or stream capture, tight serving loops, and hosts
+ * that forbid allocation while a step runs.  loglin_fwd_noalloc computes
+ * exactly what loglin_fwd computes (the same kernels; outputs are
+ * bit-identical) with its workspace in a fixed array of device memory of
+ * LOGLIN_NOALLOC_SCRATCH_MIB MiB that the library holds, one copy per GPU,
+ * from the first call on that GPU until the process ends.  That covers
+ * loglin_workspace_bytes up to 192 MiB: the 32K-token, 48-head, P=64,
+ * N=128 bf16 workload needs about 151 MB.  Larger problems return
+ * LOGLIN_ERR_SCRATCH (checked on the host before any HIP call, like every
+ * other argument error); loglin_noalloc_scratch_bytes gives the limit.
+ *
+ * The call makes no device allocation.  Its first call on a GPU looks up
+ * the array's address on that GPU (hipGetSymbolAddress); later calls reuse
+ * it.  The array belongs to the current device: `stream` must be a stream
+ * of the current device (or NULL).  Every call on a GPU shares that GPU's
+ * array, whose contents the forward never needs cleared: calls whose
+ * kernels overlap on one GPU (different streams, or host threads without
+ * ordering) race on it and must be serialised by the caller.  Other
+ * arguments, layouts and errors as for loglin_fwd. */
+#define LOGLIN_NOALLOC_SCRATCH_MIB 192
+
+size_t loglin_noalloc_scratch_bytes(void);
+
+int loglin_fwd_noalloc(const void* X, const void* B, const void* C,
+                       const float* log_a, const void* lambda, int chunk,
+                       void* out, const loglin_dims* dims, void* stream);
 
 /* ---- One-token decode (Fenwick recurrence) -------------------------------
  *

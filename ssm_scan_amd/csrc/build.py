@@ -33,7 +33,8 @@ FLAGS = [
 def _units():
     units = [("loglin_host", os.path.join(HERE, "loglin_host.cpp"), []),
              ("loglin_decode", os.path.join(HERE, "loglin_decode.hip"), []),
-             ("loglin_gdn", os.path.join(HERE, "loglin_gdn.hip"), [])]
+             ("loglin_gdn", os.path.join(HERE, "loglin_gdn.hip"), []),
+             ("loglin_noalloc", os.path.join(HERE, "loglin_noalloc.hip"), [])]
     for io in ("bf16", "f32"):
         for chunk in (16, 32, 64):
             units.append((f"loglin_inst_{io}_{chunk}",

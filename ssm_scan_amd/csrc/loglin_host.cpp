@@ -522,6 +522,8 @@ const char* loglin_strerror(int code) {
     case LOGLIN_ERR_SHAPE: return "unsupported (headdim, dstate) for this dtype";
     case LOGLIN_ERR_HIP: return "a HIP launch failed";
     case LOGLIN_ERR_OPTS: return "an option is out of range";
+    case LOGLIN_ERR_SCRATCH:
+      return "the workspace exceeds the fixed scratch array of loglin_fwd_noalloc";
     default: return "unknown error code";
   }
 }

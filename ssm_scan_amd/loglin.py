@@ -24,7 +24,7 @@ ERRORS = {
     -3: "LOGLIN_ERR_CHUNK", -4: "LOGLIN_ERR_SEQ_CHUNK", -5: "LOGLIN_ERR_GROUPS",
     -6: "LOGLIN_ERR_LEVELS", -7: "LOGLIN_ERR_DTYPE", -8: "LOGLIN_ERR_WORKSPACE",
     -9: "LOGLIN_ERR_ALIGN", -10: "LOGLIN_ERR_SHAPE", -11: "LOGLIN_ERR_HIP",
-    -12: "LOGLIN_ERR_OPTS",
+    -12: "LOGLIN_ERR_OPTS", -13: "LOGLIN_ERR_SCRATCH",
 }
 
 
@@ -56,6 +56,7 @@ EXPORTS = (
     "loglin_plan_seg_log2", "loglin_event_create", "loglin_event_destroy",
     "loglin_event_elapsed_ms", "loglin_decode_state_bytes", "loglin_decode_step",
     "loglin_bwd_workspace_bytes", "loglin_bwd", "loglin_gdn_workspace_bytes", "loglin_gdn_fwd",
+    "loglin_noalloc_scratch_bytes", "loglin_fwd_noalloc",
 )
 
 
@@ -103,6 +104,10 @@ def lib():
     L.loglin_gdn_workspace_bytes.restype = sz
     L.loglin_gdn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, pd, vp, sz, vp]
     L.loglin_gdn_fwd.restype = i32
+    L.loglin_noalloc_scratch_bytes.argtypes = []
+    L.loglin_noalloc_scratch_bytes.restype = sz
+    L.loglin_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, pd, vp]
+    L.loglin_fwd_noalloc.restype = i32
     _lib = L
     return L
 
@@ -240,6 +245,37 @@ def loglin_fwd(X, B, C, log_a, lam, chunk, out, *, workspace=None, stream=None,
     rc = lib().loglin_fwd_ex(_ptr(X), _ptr(B), _ptr(C), _ptr(log_a), _ptr(lam), int(chunk),
                              _ptr(out), ctypes.byref(dims), _ptr(workspace), ws_bytes, sptr,
                              popts)
+    _check(rc)
+    return out
+
+
+def loglin_noalloc_scratch_bytes() -> int:
+    return int(lib().loglin_noalloc_scratch_bytes())
+
+
+def loglin_fwd_noalloc(X, B, C, log_a, lam, chunk, out, *, stream=None):
+    """loglin_fwd with the library's fixed scratch array as the workspace:
+    nothing is allocated on the device, here or in the library.  Same
+    tensors as loglin_fwd; `stream` must belong to the current device.
+    Returns `out`."""
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("loglin_fwd_noalloc needs GPU tensors")
+    dims = dims_of(X, B, lam)
+    io = X.dtype
+    Bt, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    _check_tensor("X", X, (Bt, T, H, P), io, dev)
+    _check_tensor("B", B, (Bt, T, G, N), io, dev)
+    _check_tensor("C", C, (Bt, T, G, N), io, dev)
+    _check_tensor("log_a", log_a, (Bt, T, H), torch.float32, dev)
+    _check_tensor("lam", lam, (Bt, T, H, lam.shape[3]), io, dev)
+    _check_tensor("out", out, (Bt, T, H, P), io, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib().loglin_fwd_noalloc(_ptr(X), _ptr(B), _ptr(C), _ptr(log_a), _ptr(lam), int(chunk),
+                                  _ptr(out), ctypes.byref(dims),
+                                  ctypes.c_void_p(stream.cuda_stream))
     _check(rc)
     return out
 

@@ -158,7 +158,34 @@ def test_workspace_size_formula():
 def test_strerror_all_codes():
     for code in L.ERRORS:
         assert isinstance(L.loglin_strerror(code), str)
+        assert L.loglin_strerror(code) != "unknown error code", code
     assert L.loglin_strerror(-99) == "unknown error code"
+
+
+def test_noalloc_host_checks():
+    """loglin_fwd_noalloc validates on the host before its first HIP call:
+    argument errors as for loglin_fwd, and LOGLIN_ERR_SCRATCH for a problem
+    whose workspace exceeds the fixed array (the 32K-token, 48-head
+    workload fits)."""
+    lib = L.lib()
+    cap = lib.loglin_noalloc_scratch_bytes()
+    assert cap == 192 << 20
+    assert L.loglin_workspace_bytes(good_dims(), 64) <= cap
+    big = good_dims(seqlen=131072, nlevels=18, nheads=96, ngroups=48)
+    assert L.loglin_workspace_bytes(big, 64) > cap
+
+    def call(d, chunk=64, **ptrs):
+        p = dict(X=FAKE, B=FAKE, C=FAKE, log_a=FAKE, lam=FAKE, out=FAKE)
+        p.update(ptrs)
+        return lib.loglin_fwd_noalloc(p["X"], p["B"], p["C"], p["log_a"], p["lam"], chunk,
+                                      p["out"], ctypes.byref(d), None)
+
+    assert call(big) == -13
+    assert call(good_dims(nlevels=3)) == -6
+    assert call(good_dims(), chunk=48) == -3
+    assert call(good_dims(), X=None) == -1
+    assert call(good_dims(), out=FAKE + 8) == -9
+    assert lib.loglin_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == -1
 
 
 def decode_dims(**kw):
