@@ -46,7 +46,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_t32k_bf16.json")
-KERNEL_SOURCE = os.path.join(ROOT, "ssm_scan_amd", "csrc", "loglin_device.hpp")
+KERNEL_SOURCES = [os.path.join(ROOT, "ssm_scan_amd", "csrc", f)
+                  for f in ("loglin_device.hpp", "loglin_out2.hpp", "loglin_launch.hpp")]
 
 
 # ---------------------------------------------------------- work counting
@@ -262,13 +263,19 @@ def measure_copy_gbs(dev, mib=1024, reps=10) -> float:
 # ----------------------------------------------------------- GPU timing
 
 def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources: counters taken on other
+    sources are not reported."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    runs, if they were taken on the current kernel source; else None."""
+def counter_traffic(stage: str):
+    """HBM bytes per launch of a pass (chunk_state, level_scan, output) from
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if they were taken on the
+    current kernel sources; else None."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
@@ -276,7 +283,7 @@ def counter_traffic(kernel: str):
         return None
     if c.get("source_sha256_16") != source_hash():
         return None
-    k = c.get("kernels", {}).get(kernel)
+    k = c.get("stages", {}).get(stage)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
@@ -400,12 +407,12 @@ def main():
         ach, peak, unit = dom_tflops, mfma_peak, "TFLOP/s"
     roofline = {
         "bound": bound,
-        "kernel": f"{dom}_kernel",
+        "kernel": f"{dom} pass",
         "achieved": round(ach, 1),
         "peak": peak,
         "unit": unit,
         "frac": round(ach / peak, 4),
-        "traffic": counter_traffic(f"{dom}_kernel"),
+        "traffic": counter_traffic(dom),
         "alg_bytes_per_launch": alg["bytes"][dom],
         "alg_flops_per_launch": alg["flops"][dom],
         "intensity_flop_per_byte": round(intensity, 1),
@@ -438,7 +445,7 @@ def main():
         },
         "roofline": roofline,
         "mfma": {
-            "kernel": f"{dom}_kernel",
+            "kernel": f"{dom} pass",
             "achieved": round(dom_tflops, 2),
             "peak": mfma_peak,
             "unit": "TFLOP/s",
@@ -467,20 +474,28 @@ def main():
 
 
 def main_naive(args, cfg, t, out, ws, stream, fused_step):
+    """The unfused variant: one whole pass per level, each computing only its
+    own level's terms (a level inside the chunk runs only the intra block;
+    one inside a segment skips the state pass and the scan; one above the
+    segments skips the intra block and the local stack), written to its own
+    slice, then one fp32 sum over the slices.  The passes and the sum are
+    timed separately, next to the fused pass on the same inputs."""
     import torch
 
     from ssm_scan_amd import loglin as L
 
     LL = inputs.num_levels(cfg.seqlen)
-    acc = torch.zeros(out.shape, dtype=torch.float32, device=out.device)
-    part = torch.empty_like(out)
+    parts = torch.empty((LL,) + tuple(out.shape), dtype=out.dtype, device=out.device)
+    acc = torch.empty(out.shape, dtype=torch.float32, device=out.device)
 
-    def naive_step():
-        acc.zero_()
-        for lv in range(LL):  # one whole pass per level, only that level's terms
-            L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], cfg.chunk, part,
-                         workspace=ws, stream=stream, level_mask=1 << lv)
-            acc.add_(part.float())
+    def passes(events=None):
+        for lv in range(LL):
+            L.loglin_fwd(t["X"], t["B"], t["C"], t["log_a"], t["lam"], cfg.chunk, parts[lv],
+                         workspace=ws, stream=stream, level_mask=1 << lv,
+                         stage_events=None if events is None else events[lv])
+
+    def reduce():
+        torch.sum(parts, dim=0, dtype=torch.float32, out=acc)
 
     def timed(fn, k):
         torch.cuda.synchronize()
@@ -493,14 +508,25 @@ def main_naive(args, cfg, t, out, ws, stream, fused_step):
         return e0.elapsed_time(e1) / k
 
     for _ in range(2):
-        naive_step()
+        passes()
+        reduce()
         fused_step()
     torch.cuda.synchronize()
     ref = out.float()
     err = float(((acc - ref).abs().amax(dim=(1, 3)) / ref.abs().amax(dim=(1, 3))).max())
     K = max(1, args.steps // 5)
-    naive_ms = timed(naive_step, K)
+    passes_ms = timed(passes, K)
+    reduce_ms = timed(reduce, K)
     fused_ms = timed(fused_step, K)
+    # kernel time of each level's pass (the library's stage events)
+    evs = [[L.Event() for _ in range(L.LOGLIN_NUM_STAGES + 1)] for _ in range(LL)]
+    per_level = [0.0] * LL
+    for _ in range(K):
+        passes(evs)
+        torch.cuda.synchronize()
+        for lv in range(LL):
+            per_level[lv] += evs[lv][0].elapsed_ms(evs[lv][L.LOGLIN_NUM_STAGES]) / K
+    naive_ms = passes_ms + reduce_ms
     res = {
         "metric": "log-linear Mamba-2 fwd tokens/s at T=32K, H=48: one pass per level (unfused)",
         "value": round(cfg.batch * cfg.seqlen / (naive_ms / 1e3), 1),
@@ -508,7 +534,11 @@ def main_naive(args, cfg, t, out, ws, stream, fused_step):
         "n_gpus": 1,
         "steps": K,
         "ms_per_step": round(naive_ms, 4),
+        "passes_ms": round(passes_ms, 4),
+        "sum_of_slices_ms": round(reduce_ms, 4),
+        "per_level_pass_ms": [round(x, 4) for x in per_level],
         "fused_ms_per_step": round(fused_ms, 4),
+        "fused_over_naive_passes_speedup": round(passes_ms / fused_ms, 2),
         "fused_over_naive_speedup": round(naive_ms / fused_ms, 2),
         "passes_per_step": LL,
         "max_rel_diff_sum_vs_fused": err,

@@ -71,6 +71,7 @@ struct Params {
   int hp;     // heads per work-group of the output pass (1 or 2)
   unsigned long long lmask;  // levels the output includes (bit l: level l)
   int total;  // logical work-groups of the kernel being launched
+  int nat;    // segment states and slots in natural state order (1) or state order (0)
 };
 
 // ------------------------------------------------------------ MFMA traits
@@ -628,10 +629,15 @@ void state_kernel(Params pr) {
   }
 
   float* dst = pr.seg_state + ((int64_t)bh * pr.ns + q) * (P * N) + (16 * wv + r) * N;
+  if (pr.nat) {  // row n at position n
 #pragma unroll
-  for (int nb = 0; nb < Tl::NB; ++nb)
+    for (int nb = 0; nb < Tl::NB; ++nb) store4(dst + 16 * nb + 4 * g, S[nb]);
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[M::state_pos(16 * nb + 4 * g + i)] = S[nb][i];
+    for (int nb = 0; nb < Tl::NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[M::state_pos(16 * nb + 4 * g + i)] = S[nb][i];
+  }
   if (wv == 0 && lane == 0) pr.seg_decay[(int64_t)bh * pr.ns + q] = seg_sum;
 }
 
@@ -1053,6 +1059,8 @@ void output_kernel(Params pr) {
     return v;
   };
   const bool intra_on = !MASKED || (lmask & ((2ull << c_log) - 1)) != 0;  // levels 0..log2 C
+  // levels inside the segment (log2 C + 1 .. log2 C + m): the local stack
+  const bool local_on = !MASKED || ((lmask >> (c_log + 1)) & ((1ull << m) - 1)) != 0;
   const int lpar = sizeof(T) == 2 ? (L & 1) : 0;
   issue_bx(j0, bsh0, xsh0, tid0 & 63);
   issue_c(j0, tid0 & 63);
@@ -1068,7 +1076,7 @@ void output_kernel(Params pr) {
     T* xs_next = NBUF == 2 ? (CUR ? xsh0 : xsh1) : xsh0;
     const int j = j0 + jl;
     const int64_t row0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
-    const bool need_state = jl + 1 < nch;
+    const bool need_state = jl + 1 < nch;  // a next chunk: prefetch it, push this one's state
     // Recompute lane-dependent LDS addresses inside the loop instead of
     // keeping dozens of them live across it (they would be spilled).
     int tid = tid0;
@@ -1248,7 +1256,8 @@ void output_kernel(Params pr) {
       issue_c(j + 1, lane);
       issue_lam(j + 1, lane);
       issue_regs(j + 1, tid);  // land during the state MFMAs
-
+    }
+    if (need_state && local_on) {
       // ---- this chunk's state, pushed on the local Fenwick stack
       f32x4 S[Tl::NB];
 #pragma unroll

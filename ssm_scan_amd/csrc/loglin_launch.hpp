@@ -2,6 +2,7 @@
 #pragma once
 
 #include "loglin_device.hpp"
+#include "loglin_out2.hpp"
 
 namespace loglin {
 
@@ -29,8 +30,18 @@ template <class T, int C, int P, int N>
 int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   using Tl = Tiles<T, C, P, N>;
   Params pr = base;
+  // the bf16 output pass for 64-token chunks and 64 columns reads slots in
+  // natural state order; the other instantiations in state order
+  constexpr bool OUT2 = sizeof(T) == 2 && C == 64 && P == 64 && (N == 64 || N == 128);
+  const bool use2 = OUT2 && pr.hp != 2;
+  pr.nat = use2 ? 1 : 0;
   record(ev, 0, st);
-  if (pr.ns > 1) {
+  // Levels above a segment (c + m + 1 and up) need the state pass and the
+  // scan; a level mask without them (the unfused per-level variant) skips
+  // both.
+  const int c_log = __builtin_ctz(C);
+  const bool above = (c_log + pr.m + 1 >= 64) ? false : (pr.lmask >> (c_log + pr.m + 1)) != 0;
+  if (pr.ns > 1 && above) {
     // bf16 heads of one group share their B rows in one work-group
     constexpr bool SPAIRS = sizeof(T) == 2;
     if (SPAIRS && (pr.nheads / pr.ngroups) % 2 == 0) {
@@ -55,7 +66,15 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   // pairs of heads of one group (shared B, C and scores) where requested;
   // the host only accepts that for bf16 with 64 columns
   constexpr bool PAIRS = sizeof(T) == 2 && P == 64;
-  if (PAIRS && pr.hp == 2)
+  if (use2) {
+    constexpr int NN = OUT2 ? N : 128;
+    pr.total = pr.batch * pr.ns * pr.nheads;
+    const size_t shm = (size_t)C * lam_words(pr.ll, 2) * 4;
+    if (pr.lmask == ~0ull)
+      hipLaunchKernelGGL((output2_kernel<NN, false>), dim3(pad8(pr.total)), dim3(256), shm, st, pr);
+    else
+      hipLaunchKernelGGL((output2_kernel<NN, true>), dim3(pad8(pr.total)), dim3(256), shm, st, pr);
+  } else if (PAIRS && pr.hp == 2)
     launch_output<T, C, P, N, PAIRS ? 2 : 1>(pr, st);
   else
     launch_output<T, C, P, N, 1>(pr, st);
