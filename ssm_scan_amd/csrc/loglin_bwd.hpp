@@ -57,8 +57,8 @@ struct BwdParams {
   float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
   float* zst;     // [batch*nheads, nstate, N, P] fp32, lower-half sums
   float* rst;     // [batch*nheads, nstate, N, P] fp32, upper-half sums
-  float* dch;     // [batch, seqlen, nheads, N] this head's share of dC
-  float* dbh;     // [batch, seqlen, nheads, N] this head's share of dB
+  void* dch;      // [batch, seqlen, nheads, N] io type: this head's share of dC
+  void* dbh;      // [batch, seqlen, nheads, N] io type: this head's share of dB
   float* term1;   // [batch*nheads, seqlen] dO_t . O_t
   float* term2;   // [batch*nheads, seqlen] X_t . dX_t
   int batch, seqlen, nheads, ngroups, nlevels;
@@ -728,13 +728,13 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     buf ^= 1;
   }
 
-  float* dcg = pr.dch + (((int64_t)b * T_ + t0) * H + h) * N;
+  T* dcg = static_cast<T*>(pr.dch) + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
   for (int q = 0; q < NBH; ++q)
     if (NB % 2 == 0 || half + 2 * q < NB) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * (half + 2 * q) + r] = dc[q][i];
+        dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * (half + 2 * q) + r] = from_f<T>(dc[q][i]);
     }
   T* dlg = static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L;
   for (int i = tid; i < C * L; i += NT) {
@@ -932,7 +932,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     buf ^= 1;
   }
   T* dxg = static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P;
-  float* dbg = pr.dbh + (((int64_t)b * T_ + t0) * H + h) * N;
+  T* dbg = static_cast<T*>(pr.dbh) + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = sw + 4 * g + i;
@@ -947,7 +947,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     }
 #pragma unroll
     for (int q = 0; q < NBH; ++q)
-      if (NB % 2 == 0 || half + 2 * q < NB) dbg[(int64_t)s * H * N + 16 * (half + 2 * q) + r] = db[q][i];
+      if (NB % 2 == 0 || half + 2 * q < NB) dbg[(int64_t)s * H * N + 16 * (half + 2 * q) + r] = from_f<T>(db[q][i]);
     part = sum16(part);
     if (r == 0) xpart[half][s] = part;
   }
@@ -962,7 +962,8 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 
 // ------------------------------------------------------------ launch 6
 
-// dB and dC: the heads of each group summed in head order; 4 elements per thread.
+// dB and dC: the heads of each group summed in head order (the per-head
+// shares are stored in the io type, summed in fp32); 4 elements per thread.
 template <class T, int N>
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams pr) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -976,8 +977,13 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams pr) {
   f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < hpg; ++k) {
     const int64_t idx = (bt * H + grp * hpg + k) * N + n;
-    sb += *reinterpret_cast<const f32x4*>(pr.dbh + idx);
-    sc += *reinterpret_cast<const f32x4*>(pr.dch + idx);
+    const T* pb = static_cast<const T*>(pr.dbh) + idx;
+    const T* pc = static_cast<const T*>(pr.dch) + idx;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sb[e] += to_f(pb[e]);
+      sc[e] += to_f(pc[e]);
+    }
   }
   store4(static_cast<T*>(pr.dB) + (bt * G + grp) * N + n, sb);
   store4(static_cast<T*>(pr.dC) + (bt * G + grp) * N + n, sc);

@@ -60,7 +60,8 @@ struct GdnParams {
 
 constexpr int GDN_C = 32;     // tokens per chunk
 constexpr int GDN_PB = 16;    // value columns per work-group of the scan
-constexpr int GDN_NT = 256;   // threads per work-group (4 waves)
+constexpr int GDN_NT = 256;   // threads per work-group of the chunk pass (4 waves)
+constexpr int GDN_SNT = 512;  // threads per work-group of the level pass (8 waves)
 constexpr int GDN_KMAX = 16;  // chunk levels 1..GDN_KMAX-1 held in registers
 constexpr int GDN_LMAX = 32;  // token levels per lambda row
 constexpr int GDN_LB = 4;     // chunk levels the level pass handles per batch
@@ -267,14 +268,15 @@ __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
 // One chunk's operands of the level pass, loaded into registers one chunk
 // ahead and then stored to LDS: Qe, W and K (C x N), U and the intra outputs
 // for this work-group's 16 columns, gamma_C / gamma_t, and lambda rows.
-template <class T, int N, int P>
+template <class T, int N, int P, int NT_>
 struct GdnStage {
-  static constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_NT;
+  static constexpr int C = GDN_C, PB = GDN_PB, NT = NT_;
+  static constexpr int NV = (C * PB + NT - 1) / NT;  // U / intra-output values per thread
   static constexpr int NQ4 = C * N / 4;  // float4 groups of a C x N tile
   static constexpr int NQ = (NQ4 + NT - 1) / NT;  // per thread
   static constexpr int NL = (C * GDN_LMAX + NT - 1) / NT;
   f32x4 qe[NQ], w[NQ], k[NQ];
-  float u2[2], o2[2], lam[NL], khv, gcv;
+  float u2[NV], o2[NV], lam[NL], khv, gcv;
   __device__ inline void load(const GdnParams& pr, int item, int b, int h, int64_t t0, int p0, int tid) {
     const float* qeg = pr.qe + (int64_t)item * C * N;
     const float* wg = pr.w + (int64_t)item * C * N;
@@ -289,10 +291,10 @@ struct GdnStage {
       for (int c = 0; c < 4; ++c) k[q][c] = to_f(kr[c]);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {  // C x 16 = 512 values: two per thread
+    for (int q = 0; q < NV; ++q) {  // C x 16 = 512 values
       const int e = q * NT + tid, t = e / PB, p = e % PB;
-      u2[q] = pr.u[((int64_t)item * C + t) * P + p0 + p];
-      o2[q] = pr.oi[((int64_t)item * C + t) * P + p0 + p];
+      u2[q] = e < C * PB ? pr.u[((int64_t)item * C + t) * P + p0 + p] : 0.f;
+      o2[q] = e < C * PB ? pr.oi[((int64_t)item * C + t) * P + p0 + p] : 0.f;
     }
     const T* lg = static_cast<const T*>(pr.lam);
 #pragma unroll
@@ -308,21 +310,25 @@ struct GdnStage {
 };
 
 template <class T, int N, int P>
-__global__ __launch_bounds__(GDN_NT) void gdn_scan_kernel(GdnParams pr) {
+__global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
   using M = Mfma<float>;
-  constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_NT, c_log = 5;
+  constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_SNT, NWV = NT / 64, c_log = 5;
   static_assert(PB == 16 && N % 16 == 0 && P % PB == 0, "tile shapes");
-  constexpr int NTILE = N / 16;         // 16-row blocks of a state
-  constexpr int NTW = (NTILE + 3) / 4;  // of them per wave (waves past NTILE own none)
+  constexpr int NTILE = N / 16;                // 16-row blocks of a state
+  constexpr int NTW = (NTILE + NWV - 1) / NWV;  // of them per wave (waves past NTILE own none)
   using LN = Rows<float, N>;
   using LP = Rows<float, PB>;
-  using St = GdnStage<T, N, P>;
+  using St = GdnStage<T, N, P, NT>;
   __shared__ __attribute__((aligned(16))) float qf[C * N];  // Qe
   __shared__ __attribute__((aligned(16))) float wf[C * N];  // W
   __shared__ __attribute__((aligned(16))) float kf[C * N];  // K
   __shared__ __attribute__((aligned(16))) float us[C * PB];  // U
   __shared__ __attribute__((aligned(16))) float ys[GDN_LB * C * PB];  // W Z of a batch of levels
-  __shared__ __attribute__((aligned(16))) float os[C * PB];            // outputs of the chunk
+  // outputs of the chunk: the intra part and the even batch slots' levels
+  // in os, the odd slots' levels in os1 (each written by one wave per row
+  // block: no two waves add to one entry)
+  __shared__ __attribute__((aligned(16))) float os[C * PB];
+  __shared__ __attribute__((aligned(16))) float os1[C * PB];
   __shared__ __attribute__((aligned(16))) float zs[GDN_LB * N * PB];  // a batch of level states
   __shared__ float lam_s[C][GDN_LMAX];
   __shared__ float khs[C];
@@ -358,10 +364,13 @@ __global__ __launch_bounds__(GDN_NT) void gdn_scan_kernel(GdnParams pr) {
       store16(kf + LN::at(t, n), st.k[q]);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < St::NV; ++q) {
       const int e = q * NT + tid, t = e / PB, p = e % PB;
-      us[LP::at(t, p)] = st.u2[q];
-      os[LP::at(t, p)] = st.o2[q];
+      if (e < C * PB) {
+        us[LP::at(t, p)] = st.u2[q];
+        os[LP::at(t, p)] = st.o2[q];
+        os1[LP::at(t, p)] = 0.f;
+      }
     }
 #pragma unroll
     for (int q = 0; q < St::NL; ++q) {
@@ -405,11 +414,14 @@ __global__ __launch_bounds__(GDN_NT) void gdn_scan_kernel(GdnParams pr) {
           }
       }
       lds_barrier();
-      {  // waves 0, 1: Qe Z (outputs); waves 2, 3: W Z
-        const float* a = wave < 2 ? qf : wf;
-        const int rb = wave & 1;
+      {  // wave w: Qe Z (outputs) for w mod 4 < 2, else W Z; row block
+         // w mod 2; batch slots q = w / 4, w / 4 + 2
+        const bool qe = (wave & 2) == 0;
+        const float* a = qe ? qf : wf;
+        const int rb = wave & 1, q0 = wave >> 2;
+        float* od = q0 ? os1 : os;
 #pragma unroll
-        for (int q = 0; q < GDN_LB; ++q) {
+        for (int q = q0; q < GDN_LB; q += 2) {
           if (q >= nbat) break;
           const float* zq = zs + q * N * PB;
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -420,8 +432,8 @@ __global__ __launch_bounds__(GDN_NT) void gdn_scan_kernel(GdnParams pr) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * rb + 4 * g + i;
-            if (wave < 2)
-              os[LP::at(t, r)] += lam_s[t][c_log + ms[q]] * acc[i];
+            if (qe)
+              od[LP::at(t, r)] += lam_s[t][c_log + ms[q]] * acc[i];
             else
               ys[q * C * PB + LP::at(t, r)] = acc[i];
           }
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(GDN_NT) void gdn_scan_kernel(GdnParams pr) {
     }
     for (int i = tid; i < C * PB; i += NT) {
       const int t = i / PB, p = i % PB;
-      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[LP::at(t, p)]);
+      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[LP::at(t, p)] + os1[LP::at(t, p)]);
     }
     lds_barrier();  // the next chunk restages every tile
   }
@@ -501,7 +513,7 @@ int launch_gdn(const GdnParams& pr, hipStream_t st) {
   const int items = pr.batch * pr.nheads * pr.nc;
   hipLaunchKernelGGL((gdn_chunk_kernel<T, N, P>), dim3(items), dim3(GDN_NT), 0, st, pr);
   const int blocks = pr.batch * pr.nheads * (P / GDN_PB);
-  hipLaunchKernelGGL((gdn_scan_kernel<T, N, P>), dim3(blocks), dim3(GDN_NT), 0, st, pr);
+  hipLaunchKernelGGL((gdn_scan_kernel<T, N, P>), dim3(blocks), dim3(GDN_SNT), 0, st, pr);
   return (int)hipGetLastError();
 }
 

@@ -192,10 +192,11 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   off = round_up(off + bh * nstate * pn * sizeof(float));
   pl->off_r = off;
   off = round_up(off + bh * nstate * pn * sizeof(float));
+  const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;  // per-head shares in the io type
   pl->off_dch = off;
-  off = round_up(off + tok * d->nheads * d->dstate * sizeof(float));
+  off = round_up(off + tok * d->nheads * d->dstate * esz);
   pl->off_dbh = off;
-  off = round_up(off + tok * d->nheads * d->dstate * sizeof(float));
+  off = round_up(off + tok * d->nheads * d->dstate * esz);
   pl->off_t1 = off;
   off = round_up(off + bh * d->seqlen * sizeof(float));
   pl->off_t2 = off;
@@ -445,8 +446,8 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   pr.part_r = reinterpret_cast<float*>(ws + pl.off_pr);
   pr.zst = reinterpret_cast<float*>(ws + pl.off_z);
   pr.rst = reinterpret_cast<float*>(ws + pl.off_r);
-  pr.dch = reinterpret_cast<float*>(ws + pl.off_dch);
-  pr.dbh = reinterpret_cast<float*>(ws + pl.off_dbh);
+  pr.dch = ws + pl.off_dch;
+  pr.dbh = ws + pl.off_dbh;
   pr.term1 = reinterpret_cast<float*>(ws + pl.off_t1);
   pr.term2 = reinterpret_cast<float*>(ws + pl.off_t2);
   pr.batch = (int)dims->batch;
