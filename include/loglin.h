@@ -174,7 +174,7 @@ int loglin_plan_seg_log2(const loglin_dims* dims, int chunk,
  * LOGLIN_NOALLOC_SCRATCH_MIB MiB that the library holds, one copy per GPU,
  * from the first call on that GPU until the process ends.  That covers
  * loglin_workspace_bytes up to 192 MiB: the 32K-token, 48-head, P=64,
- * N=128 bf16 workload needs about 151 MB.  Larger problems return
+ * N=128 bf16 workload needs about 101 MB.  Larger problems return
  * LOGLIN_ERR_SCRATCH (checked on the host before any HIP call, like every
  * other argument error); loglin_noalloc_scratch_bytes gives the limit.
  *

@@ -57,7 +57,7 @@ struct Params {
   const float* log_a;
   const void* lam;
   void* out;
-  float* seg_state;  // [batch*nheads, ns, P, N] fp32, fragment order
+  void* seg_state;   // [batch*nheads, ns, P, N] io type, natural or state order
   float* seg_decay;  // [batch*nheads, ns]
   void* slots;       // [batch*nheads, ns, P, N] io type, fragment order
   float* gap_decay;  // [batch*nheads, ns, ks + 1]
@@ -628,7 +628,9 @@ void state_kernel(Params pr) {
     if (jl + 1 < nch) step(std::integral_constant<int, 1>{}, jl + 1);
   }
 
-  float* dst = pr.seg_state + ((int64_t)bh * pr.ns + q) * (P * N) + (16 * wv + r) * N;
+  // the segment state in the io type (fp32 accumulation; the level scan
+  // sums in fp32 and its slots are stored in the io type as well)
+  T* dst = static_cast<T*>(pr.seg_state) + ((int64_t)bh * pr.ns + q) * (P * N) + (16 * wv + r) * N;
   if (pr.nat) {  // row n at position n
 #pragma unroll
     for (int nb = 0; nb < Tl::NB; ++nb) store4(dst + 16 * nb + 4 * g, S[nb]);
@@ -636,21 +638,21 @@ void state_kernel(Params pr) {
 #pragma unroll
     for (int nb = 0; nb < Tl::NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[M::state_pos(16 * nb + 4 * g + i)] = S[nb][i];
+      for (int i = 0; i < 4; ++i) dst[M::state_pos(16 * nb + 4 * g + i)] = from_f<T>(S[nb][i]);
   }
   if (wv == 0 && lane == 0) pr.seg_decay[(int64_t)bh * pr.ns + q] = seg_sum;
 }
 
 // ------------------------------------------------------------- pass 2
 
-// grid (ceil(P*N/512), batch*nheads), 128 threads.  Each thread owns four
-// consecutive state elements (16 bytes per segment) and sweeps the segments
-// in order, keeping a Fenwick stack of block sums in fp32 registers: after
-// segment q the top entry is the sum over the largest aligned block of
-// segments ending at q, decayed to q's end.  That block is the lower half a
-// later segment reads at level trailing_ones(q) + 1.  The four elements
-// share a state row, so they land in four consecutive slot positions.  D
-// bounds the stack depth: the host passes ns < 2^D.
+// grid (ceil(P*N/(128 E)), batch*nheads), 128 threads.  Each thread owns E
+// consecutive state elements (16 bytes per segment: E = 8 for bf16, 4 for
+// fp32) and sweeps the segments in order, keeping a Fenwick stack of block
+// sums in fp32 registers: after segment q the top entry is the sum over the
+// largest aligned block of segments ending at q, decayed to q's end.  That
+// block is the lower half a later segment reads at level trailing_ones(q) +
+// 1.  The E elements share a state row, so they land in E consecutive slot
+// positions.  D bounds the stack depth: the host passes ns < 2^D.
 //
 // Before segment q the live entries are the set bits of q (entry i: a block
 // of 2^i segments), so the log-decay from the start of q's 2^(k-1)-aligned
@@ -682,6 +684,7 @@ template <class T, int N, int D>
 __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
   using M = Mfma<T>;
   constexpr int U = SCAN_U;
+  constexpr int E = 16 / (int)sizeof(T);  // state elements per thread
   static_assert(SCAN_DEC % U == 0, "decay tiles hold whole batches");
   __shared__ float dec_s[SCAN_DEC];
   __shared__ f32x4 ring[SCAN_NT / 64][U][64];
@@ -690,20 +693,37 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float* dec = pr.seg_decay + (int64_t)bh * ns;
-  // pn is a multiple of 256, so a wave's 256 elements are all valid or all idle
-  const int e = (blockIdx.x * SCAN_NT + threadIdx.x) * 4;
+  // pn is a multiple of 64 E, so a wave's elements are all valid or all idle
+  const int e = (blockIdx.x * SCAN_NT + threadIdx.x) * E;
   const bool valid = e < pn;
   const bool gap_lane = blockIdx.x == 0 && (int)threadIdx.x <= pr.ks;
-  const float* src = pr.seg_state + (int64_t)bh * ns * pn;
+  const T* src = static_cast<const T*>(pr.seg_state) + (int64_t)bh * ns * pn;
   T* dst = static_cast<T*>(pr.slots) + (int64_t)bh * ns * pn;
   float* gd = pr.gap_decay + (int64_t)bh * ns * (pr.ks + 1);
   const int di = valid ? slot_index<T, N>(e / N, e % N) : 0;
 
-  f32x4 stk[D];
+  // E fp32 values of a state element run (the copy's 16 bytes widened)
+  struct Run {
+    float v[E];
+  };
+  auto widen = [](const f32x4& raw) __attribute__((always_inline)) {
+    Run x;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int c = 0; c < E; ++c) x.v[c] = (float)h[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < E; ++c) x.v[c] = raw[c];
+    }
+    return x;
+  };
+  Run stk[D];
   float stka[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    stk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < E; ++c) stk[i].v[c] = 0.f;
     stka[i] = 0.f;
   }
   // Every prefetch is issued, so that each wave's count of memory operations
@@ -721,7 +741,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
     __syncthreads();
   };
   // one segment: fold the stack entries below its level in, push, store
-  auto step = [&](f32x4 v, int q) __attribute__((always_inline)) {
+  auto step = [&](Run v, int q) __attribute__((always_inline)) {
     float acur = dec_s[q % SCAN_DEC];
     const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q (uniform)
     if (gap_lane) {  // lane k writes level k's gap; one store, no loop
@@ -740,7 +760,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
       if (i < z) {
         const float w = M::ex(acur);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = w * stk[i][c] + v[c];
+        for (int c = 0; c < E; ++c) v.v[c] = w * stk[i].v[c] + v.v[c];
         acur += stka[i];
       }
     }
@@ -751,7 +771,16 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
         stka[i] = acur;
       }
     }
-    if (valid && q < ns - 1) store4(dst + (int64_t)q * pn + di, v);
+    if (valid && q < ns - 1) {
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 o;
+#pragma unroll
+        for (int c = 0; c < E; ++c) o[c] = (bf16)v.v[c];
+        store16(dst + (int64_t)q * pn + di, o);
+      } else {
+        store4(dst + (int64_t)q * pn + di, f32x4{v.v[0], v.v[1], v.v[2], v.v[3]});
+      }
+    }
   };
 
 #pragma unroll
@@ -769,7 +798,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
         wait_vm<2 * U - 2>();
       else
         wait_vm<U - 1>();
-      const f32x4 v = ring[wv][u][lane];
+      const Run v = widen(ring[wv][u][lane]);
       step(v, q0 + u);
       prefetch(q0 + U + u, u);  // v has been used, so its slot is free
     }
@@ -778,7 +807,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
   // (or the prologue) into slots 0, 1, ...
   wait_vm<0>();
   if (nfull < ns && nfull % SCAN_DEC == 0) refill(nfull);
-  for (int q = nfull; q < ns; ++q) step(ring[wv][q - nfull][lane], q);
+  for (int q = nfull; q < ns; ++q) step(widen(ring[wv][q - nfull][lane]), q);
 }
 
 // ------------------------------------------------------------- pass 3

@@ -309,6 +309,18 @@ struct GdnStage {
   }
 };
 
+// Layout of the level pass's K tile (C x N fp32): the 16-byte blocks of row
+// t are XOR-swizzled by 4 (t mod 4), masked to the N / 4 blocks of a row.
+// Its only reads take rows j0 + g (j0 a multiple of 4) and columns
+// 16 nb + r, so for N >= 64 a wave's 64 lanes meet 64 different banks; the
+// staging writes fill whole rows.
+template <int N>
+struct KRows {
+  __device__ static inline int at(int row, int c) {
+    return row * N + ((((c >> 2) ^ (((row & 3) << 2) & (N / 4 - 1))) << 2) | (c & 3));
+  }
+};
+
 template <class T, int N, int P>
 __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
   using M = Mfma<float>;
@@ -361,7 +373,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
       const int e = (q * NT + tid) * 4, t = e / N, n = e % N;
       store16(qf + LN::at(t, n), st.qe[q]);
       store16(wf + LN::at(t, n), st.w[q]);
-      store16(kf + LN::at(t, n), st.k[q]);
+      store16(kf + KRows<N>::at(t, n), st.k[q]);
     }
 #pragma unroll
     for (int q = 0; q < St::NV; ++q) {
@@ -452,7 +464,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
           if (nb < NTILE) {  // uniform
 #pragma unroll
             for (int j0 = 0; j0 < C; j0 += 4)
-              acc = M::mma(frag_down<float, LN>(kf, j0, 16 * nb, g, r) * khs[j0 + g],
+              acc = M::mma(kf[KRows<N>::at(j0 + g, 16 * nb + r)] * khs[j0 + g],
                            frag_down<float, LP>(ys + q * C * PB, j0, 0, g, r), acc);
           }
           zc[u] = acc;
@@ -475,7 +487,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
       if (nb < NTILE) {  // uniform
 #pragma unroll
         for (int j0 = 0; j0 < C; j0 += 4)
-          acc = M::mma(frag_down<float, LN>(kf, j0, 16 * nb, g, r) * khs[j0 + g],
+          acc = M::mma(kf[KRows<N>::at(j0 + g, 16 * nb + r)] * khs[j0 + g],
                        frag_down<float, LP>(us, j0, 0, g, r), acc);
       }
       own[u] = acc;

@@ -90,7 +90,7 @@ int check_dims(const loglin_dims* d, int chunk, const loglin_opts* o, Plan* pl) 
   size_t off = 0;
   if (ns > 1) {  // levels above one segment exist
     pl->off_state = off;
-    off = round_up(off + bh * ns * pn * sizeof(float));
+    off = round_up(off + bh * ns * pn * esz);
     pl->off_decay = off;
     off = round_up(off + bh * ns * sizeof(float));
     pl->off_slots = off;
@@ -372,7 +372,7 @@ int loglin_fwd_ex(const void* X, const void* B, const void* C, const float* log_
   pr.out = out;
   char* ws = static_cast<char*>(workspace);
   if (pl.bytes > 0) {
-    pr.seg_state = reinterpret_cast<float*>(ws + pl.off_state);
+    pr.seg_state = ws + pl.off_state;
     pr.seg_decay = reinterpret_cast<float*>(ws + pl.off_decay);
     pr.slots = ws + pl.off_slots;
     pr.gap_decay = reinterpret_cast<float*>(ws + pl.off_gap);

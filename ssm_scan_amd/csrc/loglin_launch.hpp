@@ -53,8 +53,9 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
       hipLaunchKernelGGL((state_kernel<T, C, P, N, 1>), dim3(pad8(pr.total)), dim3(Tl::NT), 0, st, pr);
     }
     record(ev, 1, st);
-    static_assert((P * N) % 256 == 0, "a scan wave covers 256 state elements");
-    dim3 g2((P * N + 4 * SCAN_NT - 1) / (4 * SCAN_NT), pr.batch * pr.nheads);
+    constexpr int E = 16 / (int)sizeof(T);  // state elements per scan thread
+    static_assert((P * N) % (64 * E) == 0, "a scan wave covers 64 E state elements");
+    dim3 g2((P * N + E * SCAN_NT - 1) / (E * SCAN_NT), pr.batch * pr.nheads);
     if (pr.ns < (1 << 10))  // a stack of 10 block sums covers fewer than 2^10 segments
       hipLaunchKernelGGL((scan_kernel<T, N, 10>), g2, dim3(SCAN_NT), 0, st, pr, P * N);
     else

@@ -138,7 +138,7 @@ def test_fwd_rejects_before_any_device_call():
 
 
 def test_workspace_size_formula():
-    """Workspace: fp32 segment states + io-typed slots per (batch, head,
+    """Workspace: io-typed segment states and slots per (batch, head,
     segment), plus small decay arrays; zero when there is a single chunk."""
     d = good_dims()
     assert L.loglin_plan_seg_log2(d, 64) == 3
@@ -146,7 +146,7 @@ def test_workspace_size_formula():
         m = 3 if seg is None else seg
         need = L.loglin_workspace_bytes(d, 64, seg)
         ns = 32768 // 64 >> m
-        core = 48 * ns * 64 * 128 * (4 + 2)
+        core = 48 * ns * 64 * 128 * (2 + 2)
         assert core <= need <= core + 48 * ns * 4 * 32 + 4 * 256, (seg, need, core)
     # one chunk, or one segment: no level above a segment, no workspace
     assert L.loglin_workspace_bytes(good_dims(seqlen=64, nlevels=7), 64) == 0
