@@ -3,6 +3,11 @@
 Compiles the host C-ABI unit, the decode and gated DeltaNet units, six forward instantiation
 units (io type x chunk) and five backward ones in parallel, then links
 ssm_scan_amd/_lib/libloglin.so.
+
+build_host_asan() links a second copy, _build/asan/libloglin.so, whose host
+code (the C-ABI layer: argument checks, workspace plans, launch sequences) is
+built with AddressSanitizer; device code is the same.  The ABI tests run
+against it on the CPU with the sanitizer runtime preloaded (asan_runtime()).
 """
 from __future__ import annotations
 
@@ -74,6 +79,54 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libloglin.so")
+# host-side sanitizer only: each -fsanitize applies to the host pass
+ASAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address",
+              "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LINK = ["-Xarch_host", "-fsanitize=address"]
+ASAN_UNITS = ("loglin_host", "loglin_noalloc")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to preload)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    return res.stdout.strip()
+
+
+def build_host_asan(verbose: bool = False) -> str:
+    """Link _build/asan/libloglin.so: the host units rebuilt with
+    AddressSanitizer, every other object as built by build()."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    units = {u[0]: u for u in _units()}
+    objs = []
+    for name, src, defs in units.values():
+        if name in ASAN_UNITS:
+            obj = os.path.join(ASAN_DIR, name + ".o")
+            lang = ["-x", "hip"] if src.endswith(".cpp") else []
+            flags = [f for f in FLAGS if f != "-O3"]
+            cmd = [HIPCC, *flags, *ASAN_FLAGS, *defs, *lang, "-c", src, "-o", obj]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        else:
+            obj = os.path.join(BUILD_DIR, name + ".o")
+            if not os.path.exists(obj):
+                obj = _compile((name, src, defs))
+        objs.append(obj)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_LINK, "-o", ASAN_LIB, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
 
 
 if __name__ == "__main__":

@@ -12,7 +12,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libloglin.so")
+# LOGLIN_LIB selects another build of the same library (the host-sanitizer
+# build the ABI tests run against); by default the in-tree one.
+LIB_PATH = os.environ.get("LOGLIN_LIB") or os.path.join(_HERE, "_lib", "libloglin.so")
 
 LOGLIN_F32 = 0
 LOGLIN_BF16 = 1
