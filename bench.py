@@ -589,6 +589,7 @@ def main_backward(args, cfg, t, out, ws, stream, fwd_step):
     print("[bench] backward warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         bwd_step()
+        fwd_step()
     torch.cuda.synchronize()
     K = args.steps
     print("[bench] timed backward steps", file=sys.stderr, flush=True)

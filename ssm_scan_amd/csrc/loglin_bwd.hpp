@@ -219,6 +219,25 @@ __device__ inline float sum16(float v) {
   return v;
 }
 
+// A DPP lane move within rows of 16 lanes (every source lane in range).
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Four sums at once over the 16 lanes of each lane row: afterwards lane r
+// holds the total of v[[0, 2, 1, 3][r mod 4]].  Two exchanges inside each
+// lane quad halve the values a lane carries (quad_perm [1,0,3,2], then
+// [2,3,0,1]); two rotations of the row by 4 and 8 lanes add the four quads.
+__device__ inline float sum16x4(const f32x4& v, int r) {
+  const bool o1 = (r & 1) != 0, o2 = (r & 2) != 0;
+  const float s0 = (o1 ? v[2] : v[0]) + dpp_mov<0xb1>(o1 ? v[0] : v[2]);
+  const float s1 = (o1 ? v[3] : v[1]) + dpp_mov<0xb1>(o1 ? v[1] : v[3]);
+  float k = (o2 ? s1 : s0) + dpp_mov<0x4e>(o2 ? s0 : s1);
+  k += dpp_mov<0x124>(k);  // row_ror:4
+  k += dpp_mov<0x128>(k);  // row_ror:8
+  return k;
+}
+
 // ------------------------------------------------------------ launch 1
 
 template <class T, int C>
@@ -671,6 +690,19 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   }
   lds_barrier();
 
+  // operands every chunk level reuses: this wave's dO fragments, and its C
+  // values at the positions of u's result tiles (for dlambda)
+  typename M::frag ao[P / KB];
+#pragma unroll
+  for (int kp = 0; kp < P / KB; ++kp) ao[kp] = frag_along<T, LP>(osh, tw + r, kp * KB, g);
+  f32x4 cv[NBH];
+#pragma unroll
+  for (int q = 0; q < NBH; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      cv[q][i] = (NB % 2 == 0 || half + 2 * q < NB) ? to_f(csh[LN::at(tw + 4 * g + i, 16 * (half + 2 * q) + r)])
+                                                     : 0.f;
+
   int buf = 0;
   while (k) {
     if (buf == 0)  // uniform
@@ -693,7 +725,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     for (int q = 0; q < NBH; ++q) u[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {
-      const auto a = frag_along<T, LP>(osh, tw + r, kp * KB, g);
+      const auto a = ao[kp];
 #pragma unroll
       for (int q = 0; q < NBH; ++q) {
         const int nb = half + 2 * q;
@@ -706,21 +738,29 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     }
     const int lv = c_log + k;
     const float gk = gap_s[k];
+    f32x4 part;  // this wave's share of C_t . u_t, per row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tw + 4 * g + i;
       const float wt = M::ex(cum[t] + gk);
-      float part = 0.f;
+      float pt = 0.f;
 #pragma unroll
       for (int q = 0; q < NBH; ++q)
-        if (NB % 2 == 0 || half + 2 * q < NB) part += u[q][i] * to_f(csh[LN::at(t, 16 * (half + 2 * q) + r)]);
-      const float dl = wt * sum16(part);  // this wave's share of dlambda[t][lv]
+        if (NB % 2 == 0 || half + 2 * q < NB) pt += u[q][i] * cv[q][i];
+      part[i] = pt;
       const float lk = lam_s[t][lv];
 #pragma unroll
       for (int q = 0; q < NBH; ++q) dc[q][i] += (lk * wt) * u[q][i];
-      if (r == 0) {
+    }
+    {
+      // lanes r < 4 of lane group g hold the row sums of t = tw + 4 g +
+      // [0, 2, 1, 3][r]: this wave's share of dlambda[t][lv]
+      const float rs = sum16x4(part, r);
+      if (r < 4) {
+        const int t = tw + 4 * g + (((r & 1) << 1) | (r >> 1));
+        const float dl = M::ex(cum[t] + gk) * rs;
         dlam_h[t][lv] = dl;
-        term_h[t] += lk * dl;
+        term_h[t] += lam_s[t][lv] * dl;
       }
     }
     lds_barrier();  // zsh is restaged by the next level
@@ -869,6 +909,13 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
         db[q] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * (half + 2 * q), g, r), db[q]);
   }
 
+  // this wave's B and X row fragments, the A operands of every chunk level
+  typename M::frag abf[N / KB], axf[P / KB];
+#pragma unroll
+  for (int kn2 = 0; kn2 < N / KB; ++kn2) abf[kn2] = frag_along<T, LN>(bsh, sw + r, kn2 * KB, g);
+#pragma unroll
+  for (int kp = 0; kp < P / KB; ++kp) axf[kp] = frag_along<T, LP>(xsh, sw + r, kp * KB, g);
+
   int buf = 0;
   while (k) {
     if (buf == 0)  // uniform
@@ -893,7 +940,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     for (int q = 0; q < NBH; ++q) tb[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kn2 = 0; kn2 < N / KB; ++kn2) {  // tx[s][p] = sum_n B[s][n] R[n][p]
-      const auto a = frag_along<T, LN>(bsh, sw + r, kn2 * KB, g);
+      const auto a = abf[kn2];
 #pragma unroll
       for (int q = 0; q < PBH; ++q) {
         const int pb = half + 2 * q;
@@ -906,7 +953,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     }
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {  // tb[s][n] = sum_p X[s][p] R[n][p]
-      const auto a = frag_along<T, LP>(xsh, sw + r, kp * KB, g);
+      const auto a = axf[kp];
 #pragma unroll
       for (int q = 0; q < NBH; ++q) {
         const int nb = half + 2 * q;
