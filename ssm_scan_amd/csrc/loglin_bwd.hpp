@@ -538,16 +538,41 @@ struct StateStage {
   }
 };
 
-// Chunk passes: one work-group per (batch*head, chunk), a 1-D grid dealt to
-// the XCDs in contiguous ranges (xcd_tile), so the chunks that read the same
-// level state run on one L2.
-__device__ inline bool bwd_chunk_tile(const BwdParams& pr, int& bh, int& j) {
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  if (tile >= pr.batch * pr.nheads * pr.nc) return false;
-  bh = tile / pr.nc;
-  j = tile % pr.nc;
-  return true;
+// The thread index through an opaque move: values derived from it inside a
+// persistent loop are recomputed per iteration instead of being hoisted out
+// of the loop and held in registers across it.
+__device__ inline int opaque_tid() {
+  int v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"((int)threadIdx.x));
+  return v;
 }
+
+// Chunk passes: persistent work-groups, as many as fit on the device at
+// once (a multiple of 8).  The (batch*head, chunk) tiles are split into 8
+// contiguous ranges, one per XCD (work-group b runs on XCD b mod 8).  At
+// step m the L work-groups of an XCD take the range's tiles [m L, m L + L),
+// work-group l the tile m L + (l + m) mod L: the ones running together work
+// on neighbouring chunks of one head and share its level states in L2, and
+// each work-group meets every chunk index residue mod L in turn (a chunk's
+// level count depends on its index bits, so a fixed residue would load some
+// work-groups far more than others).  Each work-group prefetches the next
+// tile's token rows into registers while it computes the current one.
+struct ChunkTiles {
+  int base, end, L, l;
+  __device__ explicit ChunkTiles(int total) {
+    const int x = (int)(blockIdx.x & 7);
+    const int per = (total + 7) >> 3;
+    l = (int)(blockIdx.x >> 3);
+    L = (int)(gridDim.x >> 3);
+    base = x * per;
+    end = min(total, base + per);
+  }
+  __device__ bool more(int m) const { return base + m * L < end; }  // step m exists
+  __device__ int tile(int m) const {  // this work-group's tile at step m, or -1
+    const int t = base + m * L + (l + m) % L;
+    return t < end ? t : -1;
+  }
+};
 
 // Two waves per 16-row block: wave w owns query rows [16 (w mod C/16), +16)
 // and every other 16-column tile of N from w / (C/16) on (two waves per SIMD
@@ -581,33 +606,44 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   __shared__ float dlam_s[C][BWD_LMAX];  // intra levels; chunk levels: first wave of a pair
   __shared__ float dlam_t[C][BWD_LMAX];  // chunk levels: second wave of a pair
   __shared__ float cum[64], ecum[64], wst[64], term_s[64], term_t[64], gap_s[BWD_LMAX];
-  int bh, j;
-  if (!bwd_chunk_tile(pr, bh, j)) return;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int half = wave >= NWR ? 1 : 0, rb = wave - half * NWR;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
-  const int b = bh / H, h = bh % H, grp = h / (H / G);
-  const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
-  const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
-  const unsigned act0 = (unsigned)j & ((1u << pr.kc) - 1u);  // active chunk levels (bit k-1)
-
-  RowsStage<T, C, N, NT> sc, sb;
-  RowsStage<T, C, P, NT> sx, so;
-  sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
-  sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
-  sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
-  so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+  const int64_t T_ = pr.seqlen;
+  const ChunkTiles ct(pr.batch * H * pr.nc);
   // lambda rows: every level the sequence reaches (ll <= BWD_LMAX)
   constexpr int LIT = (C * BWD_LMAX + NT - 1) / NT;
   const int ll = pr.ll;
-  float lv_[LIT];
+  RowsStage<T, C, N, NT> sc, sb;
+  RowsStage<T, C, P, NT> sx, so;
+  T lv_[LIT];
+  float la = 0.f;
+  auto load_rows = [&](int tile) {  // token rows of a tile into registers
+    const int tid = opaque_tid();
+    const int bh = tile / pr.nc, j = tile % pr.nc;
+    const int b = bh / H, h = bh % H, grp = h / (H / G);
+    const int64_t t0 = (int64_t)j * C;
+    sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+    sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+    sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+    so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+    const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
 #pragma unroll
-  for (int q = 0; q < LIT; ++q) {
-    const int i = q * NT + tid;
-    lv_[q] = i < C * ll ? to_f(lg[(int64_t)(i / ll) * H * L + i % ll]) : 0.f;
-  }
-  const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+    for (int q = 0; q < LIT; ++q) {
+      const int i = q * NT + tid;
+      lv_[q] = i < C * ll ? lg[(int64_t)(i / ll) * H * L + i % ll] : from_f<T>(0.f);
+    }
+    la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+  };
+  if (ct.tile(0) >= 0) load_rows(ct.tile(0));
+  for (int m = 0; ct.more(m); ++m) {
+  const int tile = ct.tile(m), next = ct.tile(m + 1);
+  if (tile < 0) continue;  // uniform: the last step has fewer tiles than work-groups
+  const int tid = opaque_tid(), lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int bh = tile / pr.nc, j = tile % pr.nc;
+  const int b = bh / H, h = bh % H;
+  const int64_t t0 = (int64_t)j * C;
+  const unsigned act0 = (unsigned)j & ((1u << pr.kc) - 1u);  // active chunk levels (bit k-1)
   // level k's gap: log-decay from the end of the lower half to chunk j
   const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
   float gap = 0.f;
@@ -615,8 +651,26 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     const int h0 = (j >> tid) << tid;  // first chunk of j's upper half at level tid + 1
     gap = (float)(ca[j] - ca[h0]);
   }
+
+  sc.store(csh, tid);
+  sb.store(bsh, tid);
+  sx.store(xsh, tid);
+  so.store(osh, tid);
+#pragma unroll
+  for (int q = 0; q < LIT; ++q) {
+    const int i = q * NT + tid;
+    if (i < C * ll) {
+      lam_s[i / ll][i % ll] = to_f(lv_[q]);
+      dlam_s[i / ll][i % ll] = 0.f;
+      dlam_t[i / ll][i % ll] = 0.f;
+    }
+  }
+  if (tid < pr.kc) gap_s[tid + 1] = gap;
+  if (tid < C) term_t[tid] = 0.f;
+  chunk_decays<T, C>(la, cum, ecum, wst, tid);
+  lds_barrier();
   // the states of the first two active levels are requested now, each later
-  // one two levels ahead of its use
+  // one two levels ahead of its use; then the next tile's rows
   StateStage<T, N, P, NT> st0, st1;  // two named buffers: no runtime array index
   auto state_of = [&](int kk) {
     return pr.zst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, kk, j >> kk)) * (N * P);
@@ -627,24 +681,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   const int k2 = act2 ? __builtin_ctz(act2) + 1 : 0;
   if (k) st0.load(state_of(k), tid);
   if (k2) st1.load(state_of(k2), tid);
-
-  sc.store(csh, tid);
-  sb.store(bsh, tid);
-  sx.store(xsh, tid);
-  so.store(osh, tid);
-#pragma unroll
-  for (int q = 0; q < LIT; ++q) {
-    const int i = q * NT + tid;
-    if (i < C * ll) {
-      lam_s[i / ll][i % ll] = lv_[q];
-      dlam_s[i / ll][i % ll] = 0.f;
-      dlam_t[i / ll][i % ll] = 0.f;
-    }
-  }
-  if (tid < pr.kc) gap_s[tid + 1] = gap;
-  if (tid < C) term_t[tid] = 0.f;
-  chunk_decays<T, C>(la, cum, ecum, wst, tid);
-  lds_barrier();
+  if (next >= 0) load_rows(next);
 
   bwd_intra_scores<T, C, P, N, BWD_LMAX, false, true, false>(csh, bsh, xsh, osh, cum, lam_s,
                                                              nullptr, wsh, esd, rb, half, g, r);
@@ -784,6 +821,8 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     dlg[(int64_t)t * H * L + l] = from_f<T>(v);
   }
   if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid] + term_t[tid];
+  lds_barrier();  // the next tile restages every LDS array
+  }
 }
 
 // The mask epilogue runs per query row block as in bwd_dq_kernel; then the
@@ -815,34 +854,45 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   __shared__ float colpart[NW][64];
   __shared__ float xpart[2][64];  // X_s . (chunk-level dX_s), per wave of a pair
   __shared__ float cum[64], ecum[64], wst[64], gap_s[BWD_LMAX];
-  int bh, i_ch;
-  if (!bwd_chunk_tile(pr, bh, i_ch)) return;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int half = wave >= NWR ? 1 : 0, rb = wave - half * NWR;
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
-  const int b = bh / H, h = bh % H, grp = h / (H / G);
-  const int64_t T_ = pr.seqlen, t0 = (int64_t)i_ch * C;
-  const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
+  const int64_t T_ = pr.seqlen;
+  const ChunkTiles ct(pr.batch * H * pr.nc);
+  constexpr int LIT = (C * (c_log + 1) + NT - 1) / NT;
+  RowsStage<T, C, N, NT> sc, sb;
+  RowsStage<T, C, P, NT> sx, so;
+  T lv_[LIT];
+  float la = 0.f;
+  auto load_rows = [&](int tile) {  // token rows of a tile into registers
+    const int tid = opaque_tid();
+    const int bh = tile / pr.nc, ich = tile % pr.nc;
+    const int b = bh / H, h = bh % H, grp = h / (H / G);
+    const int64_t t0 = (int64_t)ich * C;
+    sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+    sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+    sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+    so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+    const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
+#pragma unroll
+    for (int q = 0; q < LIT; ++q) {
+      const int i = q * NT + tid;
+      lv_[q] = i < C * (c_log + 1) ? lg[(int64_t)(i / (c_log + 1)) * H * L + i % (c_log + 1)] : from_f<T>(0.f);
+    }
+    la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+  };
+  if (ct.tile(0) >= 0) load_rows(ct.tile(0));
+  for (int m = 0; ct.more(m); ++m) {
+  const int tile = ct.tile(m), next = ct.tile(m + 1);
+  if (tile < 0) continue;  // uniform: the last step has fewer tiles than work-groups
+  const int tid = opaque_tid(), lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int bh = tile / pr.nc, i_ch = tile % pr.nc;
+  const int b = bh / H, h = bh % H;
+  const int64_t t0 = (int64_t)i_ch * C;
   // active chunk levels (bit k-1): i in a lower half whose upper half exists
   unsigned act0 = 0;
   for (int k = 1; k <= pr.kc; ++k)
     if (!((i_ch >> (k - 1)) & 1) && ((((i_ch >> (k - 1)) + 1) << (k - 1)) < pr.nc)) act0 |= 1u << (k - 1);
-
-  RowsStage<T, C, N, NT> sc, sb;
-  RowsStage<T, C, P, NT> sx, so;
-  sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
-  sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
-  sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
-  so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
-  constexpr int LIT = (C * (c_log + 1) + NT - 1) / NT;
-  float lv_[LIT];
-#pragma unroll
-  for (int q = 0; q < LIT; ++q) {
-    const int i = q * NT + tid;
-    lv_[q] = i < C * (c_log + 1) ? to_f(lg[(int64_t)(i / (c_log + 1)) * H * L + i % (c_log + 1)]) : 0.f;
-  }
-  const float la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
   // level k's gap: log-decay from the end of chunk i to the end of its lower half
   const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
   float gap = 0.f;
@@ -850,6 +900,21 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     const int h0 = ((i_ch >> tid) + 1) << tid;  // first chunk of the upper half at level tid + 1
     gap = (float)(ca[h0] - ca[i_ch + 1]);
   }
+
+  sc.store(csh, tid);
+  sb.store(bsh, tid);
+  sx.store(xsh, tid);
+  so.store(osh, tid);
+#pragma unroll
+  for (int q = 0; q < LIT; ++q) {
+    const int i = q * NT + tid;
+    if (i < C * (c_log + 1)) lam_s[i / (c_log + 1)][i % (c_log + 1)] = to_f(lv_[q]);
+  }
+  if (tid < pr.kc) gap_s[tid + 1] = gap;
+  chunk_decays<T, C>(la, cum, ecum, wst, tid);
+  lds_barrier();
+  // the states of the first two active levels are requested now, each later
+  // one two levels ahead of its use; then the next tile's rows
   StateStage<T, N, P, NT> st0, st1;  // two named buffers: no runtime array index
   auto state_of = [&](int kk) {
     return pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, kk, i_ch >> kk)) * (N * P);
@@ -860,19 +925,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   const int k2 = act2 ? __builtin_ctz(act2) + 1 : 0;
   if (k) st0.load(state_of(k), tid);
   if (k2) st1.load(state_of(k2), tid);
-
-  sc.store(csh, tid);
-  sb.store(bsh, tid);
-  sx.store(xsh, tid);
-  so.store(osh, tid);
-#pragma unroll
-  for (int q = 0; q < LIT; ++q) {
-    const int i = q * NT + tid;
-    if (i < C * (c_log + 1)) lam_s[i / (c_log + 1)][i % (c_log + 1)] = lv_[q];
-  }
-  if (tid < pr.kc) gap_s[tid + 1] = gap;
-  chunk_decays<T, C>(la, cum, ecum, wst, tid);
-  lds_barrier();
+  if (next >= 0) load_rows(next);
 
   bwd_intra_scores<T, C, P, N, 8, true, false, true>(csh, bsh, xsh, osh, cum, lam_s, wsh, vsh,
                                                      gsh, rb, half, g, r);
@@ -1005,6 +1058,8 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     for (int w = 0; w < NW; ++w) cs += colpart[w][tid];
     pr.term2[(int64_t)bh * T_ + t0 + tid] = cs + (xpart[0][tid] + xpart[1][tid]);
   }
+  lds_barrier();  // the next tile restages every LDS array
+  }
 }
 
 // ------------------------------------------------------------ launch 6
@@ -1071,6 +1126,26 @@ __global__ __launch_bounds__(BWD_SCAN_NT) void bwd_dloga_kernel(BwdParams pr) {
 
 using BwdFn = int (*)(const BwdParams&, hipStream_t);
 
+// Grid of a persistent chunk pass: the work-groups the current device holds
+// at once (compute units x resident work-groups per unit), a multiple of 8
+// (one share per XCD), at most one per tile rounded up to 8.
+inline int bwd_chunk_grid(const void* kernel, int C, int tiles) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, bwd_chunk_threads(C), 0) != hipSuccess ||
+      per <= 0)
+    per = 1;
+  const int fill = (cus * per) & ~7;
+  const int need = (tiles + 7) & ~7;
+  return fill < 8 ? 8 : (need < fill ? need : fill);
+}
+template <class K>
+inline int bwd_chunk_grid(K* kernel, int C, int tiles) {
+  return bwd_chunk_grid(reinterpret_cast<const void*>(kernel), C, tiles);
+}
+
 template <class T, int C, int P, int N>
 int launch_backward(const BwdParams& pr, hipStream_t st) {
   using Tl = Tiles<T, C, P, N>;
@@ -1089,9 +1164,11 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
                          dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
     }
   }
-  const int tiles8 = (pr.nc * bh + 7) & ~7;  // xcd_tile deals whole rounds of 8
-  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(tiles8), dim3(bwd_chunk_threads(C)), 0, st, pr);
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(tiles8), dim3(bwd_chunk_threads(C)), 0, st, pr);
+  const int tiles = pr.nc * bh;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(bwd_chunk_grid(bwd_dq_kernel<T, C, P, N>, C, tiles)),
+                     dim3(bwd_chunk_threads(C)), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(bwd_chunk_grid(bwd_dkv_kernel<T, C, P, N>, C, tiles)),
+                     dim3(bwd_chunk_threads(C)), 0, st, pr);
   const int64_t groups4 = (int64_t)pr.batch * pr.seqlen * pr.ngroups * (N / 4);
   hipLaunchKernelGGL((bwd_group_sum_kernel<T, N>), dim3((unsigned)((groups4 + 255) / 256)),
                      dim3(256), 0, st, pr);
