@@ -268,7 +268,7 @@ __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
 // One chunk's operands of the level pass, loaded into registers one chunk
 // ahead and then stored to LDS: Qe, W and K (C x N), U and the intra outputs
 // for this work-group's 16 columns, gamma_C / gamma_t, and lambda rows.
-template <class T, int N, int P, int NT_>
+template <class T, int N, int P, int NT_, bool KS = false>
 struct GdnStage {
   static constexpr int C = GDN_C, PB = GDN_PB, NT = NT_;
   static constexpr int NV = (C * PB + NT - 1) / NT;  // U / intra-output values per thread
@@ -276,6 +276,7 @@ struct GdnStage {
   static constexpr int NQ = (NQ4 + NT - 1) / NT;  // per thread
   static constexpr int NL = (C * GDN_LMAX + NT - 1) / NT;
   f32x4 qe[NQ], w[NQ], k[NQ];
+  float ks[KS ? NQ : 1];  // gamma_C / gamma_t of each K row group (KS)
   float u2[NV], o2[NV], lam[NL], khv, gcv;
   __device__ inline void load(const GdnParams& pr, int item, int b, int h, int64_t t0, int p0, int tid) {
     const float* qeg = pr.qe + (int64_t)item * C * N;
@@ -289,6 +290,7 @@ struct GdnStage {
       const T* kr = static_cast<const T*>(pr.k) + (((int64_t)b * pr.seqlen + t0 + t) * pr.nheads + h) * N + n;
 #pragma unroll
       for (int c = 0; c < 4; ++c) k[q][c] = to_f(kr[c]);
+      if constexpr (KS) ks[q] = pr.kh[(int64_t)item * C + t];
     }
 #pragma unroll
     for (int q = 0; q < NV; ++q) {  // C x 16 = 512 values
@@ -518,6 +520,269 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
   }
 }
 
+
+// ---- the level pass for bf16 inputs: products as bf16 hi / lo pairs
+
+// 64-byte rows of bf16 (32 elements, four 16-byte blocks): block b of row
+// `row` sits at b ^ (row / 4 mod 4), so the 16 rows of an MFMA operand read
+// at one logical block meet 16 different groups of four banks.
+struct R32 {
+  __device__ static inline int at(int row, int c) {
+    return row * 32 + ((((c >> 3) ^ (row >> 2)) & 3) << 3) + (c & 7);
+  }
+};
+template <int N>
+using GdnRowsN = std::conditional_t<N == 32, R32, Rows<bf16, N>>;
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): 16 significant bits.
+__device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+__device__ inline void split_store4(bf16* hi, bf16* lo, int off, const f32x4& v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 x = (bf16)v[i];
+    h[i] = x;
+    l[i] = (bf16)(v[i] - (float)x);
+  }
+  *reinterpret_cast<bf16x4*>(hi + off) = h;
+  *reinterpret_cast<bf16x4*>(lo + off) = l;
+}
+// a . b with a = ah + al, b = bh + bl: ah bh + ah bl + al bh (the al bl term
+// is below the pair's precision)
+__device__ inline f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+  using M = Mfma<bf16>;
+  c = M::mma(ah, bh, c);
+  c = M::mma(ah, bl, c);
+  return M::mma(al, bh, c);
+}
+
+// Same walk as gdn_scan_kernel.  Every product runs on
+// v_mfma_f32_16x16x32_bf16 with each fp32 operand split into a bf16 hi / lo
+// pair (three products per step, about 16 significant bits per operand
+// instead of fp32's 24, at a twelfth of the fp32 MFMA cost per step).  The
+// operands are staged in the layouts the products read: Qe and W as token
+// rows, Kh transposed (rows of the key dimension, Kh = diag(gamma_C / gamma)
+// K folded in at staging), and the level states, W Z and U transposed (rows
+// of the 16 value columns).  The level states stay fp32 in registers; only
+// their copies for the products are split.  Each wave keeps its Qe or W
+// row fragments and its Kh^T fragments in registers for the whole chunk.
+template <int N, int P>
+__global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
+  using T = bf16;
+  using M = Mfma<bf16>;
+  using frag = bf16x8;
+  constexpr int C = GDN_C, PB = GDN_PB, NT = GDN_SNT, NWV = NT / 64, c_log = 5;
+  static_assert(C == 32 && PB == 16 && N % 32 == 0 && P % PB == 0, "tile shapes");
+  constexpr int NTILE = N / 16;                 // 16-row blocks of a state
+  constexpr int NTW = (NTILE + NWV - 1) / NWV;  // of them per wave
+  constexpr int NKK = N / 32;                   // contraction steps over the key dimension
+  using LN = GdnRowsN<N>;
+  using LP = Rows<float, PB>;
+  using St = GdnStage<T, N, P, NT, true>;
+  __shared__ __attribute__((aligned(16))) bf16 qh[C * N], ql[C * N];   // Qe
+  __shared__ __attribute__((aligned(16))) bf16 wh[C * N], wl[C * N];   // W
+  __shared__ __attribute__((aligned(16))) bf16 kth[N * C], ktl[N * C];  // Kh^T
+  __shared__ __attribute__((aligned(16))) bf16 uth[PB * C], utl[PB * C];  // U^T
+  __shared__ __attribute__((aligned(16))) bf16 zth[GDN_LB * PB * N], ztl[GDN_LB * PB * N];  // Z^T
+  __shared__ __attribute__((aligned(16))) bf16 yth[GDN_LB * PB * C], ytl[GDN_LB * PB * C];  // (W Z)^T
+  __shared__ __attribute__((aligned(16))) float os[C * PB];
+  __shared__ __attribute__((aligned(16))) float os1[C * PB];
+  __shared__ float lam_s[C][GDN_LMAX];
+
+  const int nblk = P / PB;
+  const int pblk = blockIdx.x % nblk, bh = blockIdx.x / nblk;
+  const int H = pr.nheads;
+  const int b = bh / H, h = bh % H, p0 = pblk * PB;
+  const int64_t T_ = pr.seqlen;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T* og = static_cast<T*>(pr.out);
+  // products: wave w forms Qe Z (outputs) for w mod 4 < 2, else W Z, for
+  // token rows [16 (w mod 2), +16) and batch slots w / 4, w / 4 + 2
+  const bool qe_wave = (wave & 2) == 0;
+  const int rbw = wave & 1, q0w = wave >> 2;
+
+  f32x4 Z[GDN_KMAX][NTW];
+#pragma unroll
+  for (int m = 0; m < GDN_KMAX; ++m)
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) Z[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  St st;
+  st.load(pr, bh * pr.nc, b, h, 0, p0, tid);
+  for (int j = 0; j < pr.nc; ++j) {
+    const int64_t t0 = (int64_t)j * C;
+    // ---- this chunk's operands into LDS, split; then the next chunk's loads
+#pragma unroll
+    for (int q = 0; q < St::NQ; ++q) {
+      if (q * NT + tid >= St::NQ4) break;
+      const int e = (q * NT + tid) * 4, t = e / N, n = e % N;
+      split_store4(qh, ql, LN::at(t, n), st.qe[q]);
+      split_store4(wh, wl, LN::at(t, n), st.w[q]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {  // Kh^T[n + c][t]
+        bf16 hi, lo;
+        split_bf16(st.k[q][c] * st.ks[q], hi, lo);
+        kth[R32::at(n + c, t)] = hi;
+        ktl[R32::at(n + c, t)] = lo;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < St::NV; ++q) {
+      const int e = q * NT + tid, t = e / PB, p = e % PB;
+      if (e < C * PB) {
+        bf16 hi, lo;
+        split_bf16(st.u2[q], hi, lo);
+        uth[R32::at(p, t)] = hi;
+        utl[R32::at(p, t)] = lo;
+        os[LP::at(t, p)] = st.o2[q];
+        os1[LP::at(t, p)] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < St::NL; ++q) {
+      const int e = q * NT + tid;
+      if (e < C * GDN_LMAX) lam_s[e / GDN_LMAX][e % GDN_LMAX] = st.lam[q];
+    }
+    const float gC = st.gcv;
+    lds_barrier();
+    if (j + 1 < pr.nc) st.load(pr, bh * pr.nc + j + 1, b, h, t0 + C, p0, tid);
+    // this chunk's operand fragments of the wave
+    frag ah[NKK], al[NKK];
+    {
+      const bf16* ah_s = qe_wave ? qh : wh;
+      const bf16* al_s = qe_wave ? ql : wl;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int o = LN::at(16 * rbw + r, 32 * kk + 8 * g);
+        ah[kk] = *reinterpret_cast<const frag*>(ah_s + o);
+        al[kk] = *reinterpret_cast<const frag*>(al_s + o);
+      }
+    }
+    frag kh_[NTW], kl_[NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int nb = NTW * wave + u;
+      if (nb < NTILE) {
+        const int o = R32::at(16 * nb + r, 8 * g);
+        kh_[u] = *reinterpret_cast<const frag*>(kth + o);
+        kl_[u] = *reinterpret_cast<const frag*>(ktl + o);
+      } else {
+        kh_[u] = kl_[u] = frag{};
+      }
+    }
+
+    // ---- chunk levels whose bit is set in j, up to GDN_LB at a time
+    for (unsigned act = (unsigned)j; act;) {
+      int ms[GDN_LB];
+      int nbat = 0;
+#pragma unroll
+      for (int q = 0; q < GDN_LB; ++q) {
+        ms[q] = act ? __builtin_ctz(act) + 1 : 0;  // uniform; 0: no level
+        if (act) {
+          act &= act - 1u;
+          ++nbat;
+        }
+      }
+      // level states of the batch, transposed and split
+#pragma unroll
+      for (int q = 0; q < GDN_LB; ++q) {
+        if (q >= nbat) break;
+#pragma unroll
+        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+          if (m2 == ms[q]) {
+#pragma unroll
+            for (int u = 0; u < NTW; ++u)
+              if (NTW * wave + u < NTILE)
+                split_store4(zth, ztl, q * PB * N + LN::at(r, 16 * (NTW * wave + u) + 4 * g), Z[m2][u]);
+          }
+      }
+      lds_barrier();
+      {
+        float* od = q0w ? os1 : os;
+#pragma unroll
+        for (int q = q0w; q < GDN_LB; q += 2) {
+          if (q >= nbat) break;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const int o = q * PB * N + LN::at(r, 32 * kk + 8 * g);
+            acc = mma3(ah[kk], al[kk], *reinterpret_cast<const frag*>(zth + o),
+                       *reinterpret_cast<const frag*>(ztl + o), acc);
+          }
+          if (qe_wave) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * rbw + 4 * g + i;
+              od[LP::at(t, r)] += lam_s[t][c_log + ms[q]] * acc[i];
+            }
+          } else {
+            split_store4(yth, ytl, q * PB * C + R32::at(r, 16 * rbw + 4 * g), acc);
+          }
+        }
+      }
+      lds_barrier();
+      // Z <- gamma_C Z - Kh^T (W Z)
+#pragma unroll
+      for (int q = 0; q < GDN_LB; ++q) {
+        if (q >= nbat) break;
+        const int o = q * PB * C + R32::at(r, 8 * g);
+        const frag yh = *reinterpret_cast<const frag*>(yth + o);
+        const frag yl = *reinterpret_cast<const frag*>(ytl + o);
+        f32x4 zc[NTW];
+#pragma unroll
+        for (int u = 0; u < NTW; ++u)
+          zc[u] = NTW * wave + u < NTILE ? mma3(kh_[u], kl_[u], yh, yl, f32x4{0.f, 0.f, 0.f, 0.f})
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+          if (m2 == ms[q]) {
+#pragma unroll
+            for (int u = 0; u < NTW; ++u) Z[m2][u] = gC * Z[m2][u] - zc[u];
+          }
+      }
+      lds_barrier();  // zt and yt are reused by the next batch
+    }
+    // ---- the chunk's own tokens (Kh^T U), then the Fenwick merge for j + 1
+    f32x4 own[NTW];
+    {
+      const int o = R32::at(r, 8 * g);
+      const frag uh = *reinterpret_cast<const frag*>(uth + o);
+      const frag ul = *reinterpret_cast<const frag*>(utl + o);
+#pragma unroll
+      for (int u = 0; u < NTW; ++u)
+        own[u] = NTW * wave + u < NTILE ? mma3(kh_[u], kl_[u], uh, ul, f32x4{0.f, 0.f, 0.f, 0.f})
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (j + 1 < pr.nc) {
+      const int z = __builtin_ctz((unsigned)(j + 1));
+#pragma unroll
+      for (int m = 1; m < GDN_KMAX; ++m)
+        if (m <= z) {
+#pragma unroll
+          for (int u = 0; u < NTW; ++u) {
+            own[u] += Z[m][u];
+            Z[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+      for (int m = 1; m < GDN_KMAX; ++m)
+        if (m == z + 1) {
+#pragma unroll
+          for (int u = 0; u < NTW; ++u) Z[m][u] = own[u];
+        }
+    }
+    for (int i = tid; i < C * PB; i += NT) {
+      const int t = i / PB, p = i % PB;
+      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[LP::at(t, p)] + os1[LP::at(t, p)]);
+    }
+    lds_barrier();  // the next chunk restages every tile
+  }
+}
+
 using GdnFn = int (*)(const GdnParams&, hipStream_t);
 
 template <class T, int N, int P>
@@ -525,7 +790,10 @@ int launch_gdn(const GdnParams& pr, hipStream_t st) {
   const int items = pr.batch * pr.nheads * pr.nc;
   hipLaunchKernelGGL((gdn_chunk_kernel<T, N, P>), dim3(items), dim3(GDN_NT), 0, st, pr);
   const int blocks = pr.batch * pr.nheads * (P / GDN_PB);
-  hipLaunchKernelGGL((gdn_scan_kernel<T, N, P>), dim3(blocks), dim3(GDN_SNT), 0, st, pr);
+  if constexpr (sizeof(T) == 2 && N % 32 == 0)
+    hipLaunchKernelGGL((gdn_scan_bf16_kernel<N, P>), dim3(blocks), dim3(GDN_SNT), 0, st, pr);
+  else
+    hipLaunchKernelGGL((gdn_scan_kernel<T, N, P>), dim3(blocks), dim3(GDN_SNT), 0, st, pr);
   return (int)hipGetLastError();
 }
 
