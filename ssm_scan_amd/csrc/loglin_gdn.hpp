@@ -288,8 +288,13 @@ struct GdnStage {
       qe[q] = *reinterpret_cast<const f32x4*>(qeg + e);
       w[q] = *reinterpret_cast<const f32x4*>(wg + e);
       const T* kr = static_cast<const T*>(pr.k) + (((int64_t)b * pr.seqlen + t0 + t) * pr.nheads + h) * N + n;
+      if constexpr (sizeof(T) == 2) {  // four keys: one 8-byte load
+        const bf16x4 kv = *reinterpret_cast<const bf16x4*>(kr);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) k[q][c] = to_f(kr[c]);
+        for (int c = 0; c < 4; ++c) k[q][c] = (float)kv[c];
+      } else {
+        k[q] = *reinterpret_cast<const f32x4*>(kr);
+      }
       if constexpr (KS) ks[q] = pr.kh[(int64_t)item * C + t];
     }
 #pragma unroll
@@ -404,29 +409,28 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
     for (unsigned act = (unsigned)j; act;) {
       int ms[GDN_LB];
       int nbat = 0;
+      unsigned bmask = 0;  // bit m: level m is in the batch, at slot popcount(bmask & (2^m - 1))
 #pragma unroll
       for (int q = 0; q < GDN_LB; ++q) {
         ms[q] = act ? __builtin_ctz(act) + 1 : 0;  // uniform; 0: no level
         if (act) {
+          bmask |= 1u << ms[q];
           act &= act - 1u;
           ++nbat;
         }
       }
 #pragma unroll
-      for (int q = 0; q < GDN_LB; ++q) {
-        if (q >= nbat) break;
+      for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+        if ((bmask >> m2) & 1u) {
+          const int q = __builtin_popcount(bmask & ((1u << m2) - 1u));
 #pragma unroll
-        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
-          if (m2 == ms[q]) {
+          for (int u = 0; u < NTW; ++u)
+            if (NTW * wave + u < NTILE) {
 #pragma unroll
-            for (int u = 0; u < NTW; ++u)
-              if (NTW * wave + u < NTILE) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  zs[q * N * PB + LP::at(16 * (NTW * wave + u) + 4 * g + i, r)] = Z[m2][u][i];
-              }
-          }
-      }
+              for (int i = 0; i < 4; ++i)
+                zs[q * N * PB + LP::at(16 * (NTW * wave + u) + 4 * g + i, r)] = Z[m2][u][i];
+            }
+        }
       lds_barrier();
       {  // wave w: Qe Z (outputs) for w mod 4 < 2, else W Z; row block
          // w mod 2; batch slots q = w / 4, w / 4 + 2
@@ -456,28 +460,22 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
       lds_barrier();
       // Z <- gamma_C Z - Kh^T (W Z)
 #pragma unroll
-      for (int q = 0; q < GDN_LB; ++q) {
-        if (q >= nbat) break;
-        f32x4 zc[NTW];
+      for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+        if ((bmask >> m2) & 1u) {
+          const int q = __builtin_popcount(bmask & ((1u << m2) - 1u));
 #pragma unroll
-        for (int u = 0; u < NTW; ++u) {
-          const int nb = NTW * wave + u;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          if (nb < NTILE) {  // uniform
+          for (int u = 0; u < NTW; ++u) {
+            const int nb = NTW * wave + u;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (nb < NTILE) {  // uniform
 #pragma unroll
-            for (int j0 = 0; j0 < C; j0 += 4)
-              acc = M::mma(kf[KRows<N>::at(j0 + g, 16 * nb + r)] * khs[j0 + g],
-                           frag_down<float, LP>(ys + q * C * PB, j0, 0, g, r), acc);
+              for (int j0 = 0; j0 < C; j0 += 4)
+                acc = M::mma(kf[KRows<N>::at(j0 + g, 16 * nb + r)] * khs[j0 + g],
+                             frag_down<float, LP>(ys + q * C * PB, j0, 0, g, r), acc);
+            }
+            Z[m2][u] = gC * Z[m2][u] - acc;
           }
-          zc[u] = acc;
         }
-#pragma unroll
-        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
-          if (m2 == ms[q]) {
-#pragma unroll
-            for (int u = 0; u < NTW; ++u) Z[m2][u] = gC * Z[m2][u] - zc[u];
-          }
-      }
       lds_barrier();  // zs and ys are reused by the next batch
     }
     // ---- the chunk's own tokens (Kh^T U), then the Fenwick merge for j + 1
@@ -584,7 +582,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
   using St = GdnStage<T, N, P, NT, true>;
   __shared__ __attribute__((aligned(16))) bf16 qh[C * N], ql[C * N];   // Qe
   __shared__ __attribute__((aligned(16))) bf16 wh[C * N], wl[C * N];   // W
-  __shared__ __attribute__((aligned(16))) bf16 kth[N * C], ktl[N * C];  // Kh^T
+  __shared__ __attribute__((aligned(16))) bf16 kth[C * N], ktl[C * N];  // Kh (token rows)
   __shared__ __attribute__((aligned(16))) bf16 uth[PB * C], utl[PB * C];  // U^T
   __shared__ __attribute__((aligned(16))) bf16 zth[GDN_LB * PB * N], ztl[GDN_LB * PB * N];  // Z^T
   __shared__ __attribute__((aligned(16))) bf16 yth[GDN_LB * PB * C], ytl[GDN_LB * PB * C];  // (W Z)^T
@@ -622,13 +620,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
       const int e = (q * NT + tid) * 4, t = e / N, n = e % N;
       split_store4(qh, ql, LN::at(t, n), st.qe[q]);
       split_store4(wh, wl, LN::at(t, n), st.w[q]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {  // Kh^T[n + c][t]
-        bf16 hi, lo;
-        split_bf16(st.k[q][c] * st.ks[q], hi, lo);
-        kth[R32::at(n + c, t)] = hi;
-        ktl[R32::at(n + c, t)] = lo;
-      }
+      split_store4(kth, ktl, LN::at(t, n), st.k[q] * st.ks[q]);  // Kh rows
     }
 #pragma unroll
     for (int q = 0; q < St::NV; ++q) {
@@ -662,14 +654,13 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
         al[kk] = *reinterpret_cast<const frag*>(al_s + o);
       }
     }
-    frag kh_[NTW], kl_[NTW];
+    frag kh_[NTW], kl_[NTW];  // Kh^T fragments: rows 16 nb + r of Kh^T, tokens 8 g ..
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
       const int nb = NTW * wave + u;
       if (nb < NTILE) {
-        const int o = R32::at(16 * nb + r, 8 * g);
-        kh_[u] = *reinterpret_cast<const frag*>(kth + o);
-        kl_[u] = *reinterpret_cast<const frag*>(ktl + o);
+        kh_[u] = frag_down_bf16<LN>(kth, 0, 16 * nb, g, r);
+        kl_[u] = frag_down_bf16<LN>(ktl, 0, 16 * nb, g, r);
       } else {
         kh_[u] = kl_[u] = frag{};
       }
@@ -679,27 +670,26 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
     for (unsigned act = (unsigned)j; act;) {
       int ms[GDN_LB];
       int nbat = 0;
+      unsigned bmask = 0;  // bit m: level m is in the batch, at slot popcount(bmask & (2^m - 1))
 #pragma unroll
       for (int q = 0; q < GDN_LB; ++q) {
         ms[q] = act ? __builtin_ctz(act) + 1 : 0;  // uniform; 0: no level
         if (act) {
+          bmask |= 1u << ms[q];
           act &= act - 1u;
           ++nbat;
         }
       }
       // level states of the batch, transposed and split
 #pragma unroll
-      for (int q = 0; q < GDN_LB; ++q) {
-        if (q >= nbat) break;
+      for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+        if ((bmask >> m2) & 1u) {
+          const int q = __builtin_popcount(bmask & ((1u << m2) - 1u));
 #pragma unroll
-        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
-          if (m2 == ms[q]) {
-#pragma unroll
-            for (int u = 0; u < NTW; ++u)
-              if (NTW * wave + u < NTILE)
-                split_store4(zth, ztl, q * PB * N + LN::at(r, 16 * (NTW * wave + u) + 4 * g), Z[m2][u]);
-          }
-      }
+          for (int u = 0; u < NTW; ++u)
+            if (NTW * wave + u < NTILE)
+              split_store4(zth, ztl, q * PB * N + LN::at(r, 16 * (NTW * wave + u) + 4 * g), Z[m2][u]);
+        }
       lds_barrier();
       {
         float* od = q0w ? os1 : os;
@@ -727,23 +717,17 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
       lds_barrier();
       // Z <- gamma_C Z - Kh^T (W Z)
 #pragma unroll
-      for (int q = 0; q < GDN_LB; ++q) {
-        if (q >= nbat) break;
-        const int o = q * PB * C + R32::at(r, 8 * g);
-        const frag yh = *reinterpret_cast<const frag*>(yth + o);
-        const frag yl = *reinterpret_cast<const frag*>(ytl + o);
-        f32x4 zc[NTW];
+      for (int m2 = 1; m2 < GDN_KMAX; ++m2)
+        if ((bmask >> m2) & 1u) {
+          const int q = __builtin_popcount(bmask & ((1u << m2) - 1u));
+          const int o = q * PB * C + R32::at(r, 8 * g);
+          const frag yh = *reinterpret_cast<const frag*>(yth + o);
+          const frag yl = *reinterpret_cast<const frag*>(ytl + o);
 #pragma unroll
-        for (int u = 0; u < NTW; ++u)
-          zc[u] = NTW * wave + u < NTILE ? mma3(kh_[u], kl_[u], yh, yl, f32x4{0.f, 0.f, 0.f, 0.f})
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m2 = 1; m2 < GDN_KMAX; ++m2)
-          if (m2 == ms[q]) {
-#pragma unroll
-            for (int u = 0; u < NTW; ++u) Z[m2][u] = gC * Z[m2][u] - zc[u];
-          }
-      }
+          for (int u = 0; u < NTW; ++u)
+            if (NTW * wave + u < NTILE)
+              Z[m2][u] = gC * Z[m2][u] - mma3(kh_[u], kl_[u], yh, yl, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
       lds_barrier();  // zt and yt are reused by the next batch
     }
     // ---- the chunk's own tokens (Kh^T U), then the Fenwick merge for j + 1
