@@ -962,10 +962,12 @@ void output_kernel(Params pr) {
   // Heads of one group next to each other (they share B and C), then
   // segments, then groups: the work-groups resident on one XCD at a time
   // cover few heads and many segments, so the level slots they read stay
-  // in that XCD's L2.
+  // in that XCD's L2.  Segments are dealt from the last one down: a segment
+  // whose index has more set bits has more levels above it to apply, so the
+  // longer work-groups start first and the shorter ones fill the tail.
   const int hpg = H / G, npair = hpg / HP;
   const int pi = tile % npair;
-  const int q = (tile / npair) % pr.ns;
+  const int q = pr.ns - 1 - (tile / npair) % pr.ns;
   const int grp = (tile / (npair * pr.ns)) % G;
   const int b = tile / (npair * pr.ns * G);
   const int h0 = grp * hpg + pi * HP;  // first head of the work-group

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
   // then segments, then groups: see output_kernel
   const int hpg = H / G;
   const int pi = tile % hpg;
-  const int q = (tile / hpg) % pr.ns;
+  const int q = pr.ns - 1 - (tile / hpg) % pr.ns;
   const int grp = (tile / (hpg * pr.ns)) % G;
   const int b = tile / (hpg * pr.ns * G);
   const int h = grp * hpg + pi;
