@@ -68,6 +68,27 @@ constexpr int GDN_LB = 4;     // chunk levels the level pass handles per batch
 
 // ------------------------------------------------------------ pass 1
 
+// Eight consecutive io-type elements as fp32 (one 16-byte load for bf16).
+template <class T>
+__device__ inline void load8f(const T* p, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[e + 4] = b[e];
+    }
+  }
+}
+__device__ inline void store8f(float* lo, float* hi, const float (&x)[8]) {
+  *reinterpret_cast<f32x4*>(lo) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(hi) = f32x4{x[4], x[5], x[6], x[7]};
+}
+
 template <class T, int N, int P>
 __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
   using M = Mfma<float>;  // 16x16x4 fp32: A row r / B column r, contraction element g
@@ -102,11 +123,14 @@ __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
   const T* vg = static_cast<const T*>(pr.v);
   const T* lg = static_cast<const T*>(pr.lam);
 
-  for (int i = tid; i < C * N; i += NT) {
-    const int t = i / N, n = i % N;
+  for (int i = tid; i < C * N / 8; i += NT) {  // eight keys / queries per thread and step
+    const int t = (8 * i) / N, n = (8 * i) % N;
     const int64_t row = ((int64_t)b * T_ + t0 + t) * H + h;
-    qf[LN::at(t, n)] = to_f(qg[row * N + n]);
-    kf[LN::at(t, n)] = to_f(kg[row * N + n]);
+    float x[8];
+    load8f(qg + row * N + n, x);
+    store8f(qf + LN::at(t, n), qf + LN::at(t, n + 4), x);
+    load8f(kg + row * N + n, x);
+    store8f(kf + LN::at(t, n), kf + LN::at(t, n + 4), x);
   }
   for (int i = tid; i < C * (c_log + 1); i += NT) {
     const int t = i / (c_log + 1), l = i % (c_log + 1);
@@ -132,11 +156,14 @@ __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < C * P; i += NT) {
-    const int t = i / P, p = i % P;
-    const float x = to_f(vg[(((int64_t)b * T_ + t0 + t) * H + h) * P + p]);
-    vf[LV::at(t, p)] = x;
-    vb[LV::at(t, p)] = bet[t] * x;
+  for (int i = tid; i < C * P / 8; i += NT) {
+    const int t = (8 * i) / P, p = (8 * i) % P;
+    float x[8], y[8];
+    load8f(vg + (((int64_t)b * T_ + t0 + t) * H + h) * P + p, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = bet[t] * x[e];
+    store8f(vf + LV::at(t, p), vf + LV::at(t, p + 4), x);
+    store8f(vb + LV::at(t, p), vb + LV::at(t, p + 4), y);
   }
   // ---- Q K^T and K K^T, masked: wave w owns the 16x16 tile (w >> 1, w & 1)
   {
