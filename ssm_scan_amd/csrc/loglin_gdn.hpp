@@ -188,16 +188,21 @@ __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
   __syncthreads();
   // ---- Th = (I + L)^-1, blocked: 8x8 diagonal blocks by substitution,
   // then [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1, D^-1]] at 16, 32
-  if (tid < C) {
-    const int jc = tid, blk = jc & ~7;
+  if (tid < C) {  // column jc of its 8x8 diagonal block, in registers
+    const int jc = tid, blk = jc & ~7, jj = jc & 7;
+    float x[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      float v = ii == jj ? 1.f : 0.f;
+#pragma unroll
+      for (int mm = 0; mm < ii; ++mm) v -= lm[LC::at(blk + ii, blk + mm)] * x[mm];
+      x[ii] = ii < jj ? 0.f : v;  // above the diagonal: zero
+    }
     for (int i = 0; i < C; ++i) {
-      float x = 0.f;
-      if (i == jc) {
-        x = 1.f;
-      } else if (i > jc && i < blk + 8) {
-        for (int m = jc; m < i; ++m) x -= lm[LC::at(i, m)] * tm[LC::at(m, jc)];
-      }
-      tm[LC::at(i, jc)] = x;
+      float v = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) v = i == blk + ii ? x[ii] : v;
+      tm[LC::at(i, jc)] = v;
     }
   }
   __syncthreads();
