@@ -439,12 +439,12 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
 template <class T, int C, int P, int N>
 constexpr int bwd_dq_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + 3 * C * BWD_LMAX + 5 * 64 + BWD_LMAX);
+         4 * (C * (C + 1) + 2 * C * BWD_LMAX + 4 * 64 + BWD_LMAX + 2 * (2 * C / 16) * 64);
 }
 template <class T, int C, int P, int N>
 constexpr int bwd_dkv_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + C * 8 + (C / 8) * 64 + 2 * 64 + 3 * 64 + BWD_LMAX);
+         4 * (C * (C + 1) + C * 8 + (C / 8) * 64 + (2 * C / 16) * 64 + 3 * 64 + BWD_LMAX);
 }
 
 // S = C B^T and D = dO X^T for the query rows [16 rb, +16) of the chunk,
@@ -574,25 +574,38 @@ struct ChunkTiles {
   }
 };
 
-// Two waves per 16-row block: wave w owns query rows [16 (w mod C/16), +16)
-// and every other 16-column tile of N from w / (C/16) on (two waves per SIMD
-// hide more latency than one).  dC_t = sum_s (M ⊙ D)[t, s] B_s within the
-// chunk plus, for each chunk level k whose bit is set in j,
+// Two waves per 16-row block (C / 8 waves; two waves per SIMD hide more
+// latency than one).  The score tiles go as in bwd_intra_scores.  The
+// products with the state dimension (the intra dC product and every chunk
+// level's) give each wave RPW = 2 adjacent 16-row blocks (1 for a 16-token
+// chunk) and every NCG-th 16-column tile: a state fragment read from LDS
+// then serves two row blocks, which halves the LDS reads of the level
+// states against one row block per wave.  dC_t = sum_s (M ⊙ D)[t, s] B_s
+// within the chunk plus, for each chunk level k whose bit is set in j,
 // lambda[t, c+k] exp(decay) (Z_k dO_t) with Z_k the lower half's state;
 // dlambda[t, l] = the level-l bucket sum of E S D inside the chunk, and
-// exp(decay) C_t . (Z_k dO_t) at level c + k (each wave of a pair sums its
-// own tiles; the two partial sums are added in a fixed order at the end).
+// exp(decay) C_t . (Z_k dO_t) at level c + k: each column group's share of
+// the row sum is staged in LDS and the NCG shares are added in a fixed order.
 // The next level's state is loaded into registers while the current one
 // is used.
 constexpr int bwd_chunk_threads(int C) { return C / 16 * 128; }
+template <int C>
+struct ChunkSplit {
+  static constexpr int NWR = C / 16, NW = 2 * NWR;
+  static constexpr int RPW = NWR >= 2 ? 2 : 1;  // 16-row blocks per wave
+  static constexpr int NRG = NWR / RPW;         // row groups
+  static constexpr int NCG = NW / NRG;          // column groups
+};
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams pr) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  constexpr int NWR = C / 16, NW = 2 * NWR, NT = NW * 64, KB = M::KB, NB = N / 16;
-  constexpr int NBH = (NB + 1) / 2;  // column tiles per wave
+  using CS = ChunkSplit<C>;
+  constexpr int NWR = CS::NWR, NW = CS::NW, NT = NW * 64, KB = M::KB, NB = N / 16;
+  constexpr int RPW = CS::RPW, NRG = CS::NRG, NCG = CS::NCG;
+  constexpr int NBW = (NB + NCG - 1) / NCG;  // column tiles per wave in the state products
   constexpr int c_log = ilog2c(C);
   __shared__ __attribute__((aligned(16))) T csh[C * N];
   __shared__ __attribute__((aligned(16))) T bsh[C * N];
@@ -603,11 +616,12 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   __shared__ __attribute__((aligned(16))) T zlo[sizeof(T) == 2 ? N * P : 1];
   __shared__ float esd[C][C + 1];
   __shared__ float lam_s[C][BWD_LMAX];
-  __shared__ float dlam_s[C][BWD_LMAX];  // intra levels; chunk levels: first wave of a pair
-  __shared__ float dlam_t[C][BWD_LMAX];  // chunk levels: second wave of a pair
-  __shared__ float cum[64], ecum[64], wst[64], term_s[64], term_t[64], gap_s[BWD_LMAX];
+  __shared__ float dlam_s[C][BWD_LMAX];
+  __shared__ float red[2][NCG][64];  // a chunk level's row sums per column group (two levels in flight)
+  __shared__ float cum[64], ecum[64], wst[64], term_s[64], gap_s[BWD_LMAX];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int half = wave >= NWR ? 1 : 0, rb = wave - half * NWR;
+  const int rg = wave % NRG, cg = wave / NRG;  // state products: row group, column group
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int64_t T_ = pr.seqlen;
   const ChunkTiles ct(pr.batch * H * pr.nc);
@@ -662,11 +676,9 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     if (i < C * ll) {
       lam_s[i / ll][i % ll] = to_f(lv_[q]);
       dlam_s[i / ll][i % ll] = 0.f;
-      dlam_t[i / ll][i % ll] = 0.f;
     }
   }
   if (tid < pr.kc) gap_s[tid + 1] = gap;
-  if (tid < C) term_t[tid] = 0.f;
   chunk_decays<T, C>(la, cum, ecum, wst, tid);
   lds_barrier();
   // the states of the first two active levels are requested now, each later
@@ -704,20 +716,25 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     }
   }
 
-  const int tw = 16 * rb;
-  // this wave's share of the chunk-level dlambda and dlog_a sums
-  float(*const dlam_h)[BWD_LMAX] = half ? dlam_t : dlam_s;
-  float* const term_h = half ? term_t : term_s;
-  f32x4 dc[NBH];  // column tile nb = half + 2 q
+  f32x4 dc[RPW][NBW];  // row block RPW rg + rr, column tile cg + NCG q
 #pragma unroll
-  for (int q = 0; q < NBH; ++q) dc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) dc[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < C / KB; ++kt) {  // keys s; entries with s > t are zero
-    const auto a = frag_along<T, LC>(wsh, tw + r, kt * KB, g);
+    typename M::frag a[RPW];
 #pragma unroll
-    for (int q = 0; q < NBH; ++q)
-      if (NB % 2 == 0 || half + 2 * q < NB)
-        dc[q] = M::mma(a, frag_down<T, LN>(bsh, kt * KB, 16 * (half + 2 * q), g, r), dc[q]);
+    for (int rr = 0; rr < RPW; ++rr) a[rr] = frag_along<T, LC>(wsh, 16 * (RPW * rg + rr) + r, kt * KB, g);
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int nb = cg + NCG * q;
+      if (NB % NCG == 0 || nb < NB) {
+        const auto bf = frag_down<T, LN>(bsh, kt * KB, 16 * nb, g, r);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) dc[rr][q] = M::mma(a[rr], bf, dc[rr][q]);
+      }
+    }
   }
   lds_barrier();  // dlam_s of the intra levels is written
   if (tid < C) {
@@ -725,27 +742,44 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     for (int l = 0; l <= c_log; ++l) tsum += lam_s[tid][l] * dlam_s[tid][l];
     term_s[tid] = tsum;
   }
-  lds_barrier();
 
   // operands every chunk level reuses: this wave's dO fragments, and its C
   // values at the positions of u's result tiles (for dlambda)
-  typename M::frag ao[P / KB];
+  typename M::frag ao[RPW][P / KB];
 #pragma unroll
-  for (int kp = 0; kp < P / KB; ++kp) ao[kp] = frag_along<T, LP>(osh, tw + r, kp * KB, g);
-  f32x4 cv[NBH];
+  for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-  for (int q = 0; q < NBH; ++q)
+    for (int kp = 0; kp < P / KB; ++kp) ao[rr][kp] = frag_along<T, LP>(osh, 16 * (RPW * rg + rr) + r, kp * KB, g);
+  f32x4 cv[RPW][NBW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      cv[q][i] = (NB % 2 == 0 || half + 2 * q < NB) ? to_f(csh[LN::at(tw + 4 * g + i, 16 * (half + 2 * q) + r)])
-                                                     : 0.f;
+  for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+    for (int q = 0; q < NBW; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        cv[rr][q][i] = (NB % NCG == 0 || cg + NCG * q < NB)
+                           ? to_f(csh[LN::at(16 * (RPW * rg + rr) + 4 * g + i, 16 * (cg + NCG * q) + r)])
+                           : 0.f;
+  // dlambda and dlog_a terms of a chunk level from its column groups' row sums
+  auto finish_level = [&](int kk, int rbuf) {
+    if (tid < C) {
+      float sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCG; ++c) sum += red[rbuf][c][tid];
+      const int lv = c_log + kk;
+      const float dl = M::ex(cum[tid] + gap_s[kk]) * sum;
+      dlam_s[tid][lv] = dl;
+      term_s[tid] += lam_s[tid][lv] * dl;
+    }
+  };
 
-  int buf = 0;
+  int buf = 0, pk = 0;  // pk: the previous level, whose row sums wait in red[buf ^ 1]
   while (k) {
     if (buf == 0)  // uniform
       st0.store(zsh, zlo, tid);
     else
       st1.store(zsh, zlo, tid);
+    if (pk) finish_level(pk, buf ^ 1);
     lds_barrier();
     act &= act - 1u;
     const int kn = act ? __builtin_ctz(act) + 1 : 0;
@@ -757,77 +791,85 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
       else
         st1.load(state_of(k3), tid);
     }
-    f32x4 u[NBH];  // u[t][n] = sum_p dO[t][p] Z[n][p], this wave's column tiles
+    f32x4 u[RPW][NBW];  // u[t][n] = sum_p dO[t][p] Z[n][p]
 #pragma unroll
-    for (int q = 0; q < NBH; ++q) u[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+      for (int q = 0; q < NBW; ++q) u[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {
-      const auto a = ao[kp];
 #pragma unroll
-      for (int q = 0; q < NBH; ++q) {
-        const int nb = half + 2 * q;
-        if (NB % 2 == 0 || nb < NB) {
-          u[q] = M::mma(a, frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g), u[q]);
-          if constexpr (sizeof(T) == 2)
-            u[q] = M::mma(a, frag_along<T, LP>(zlo, 16 * nb + r, kp * KB, g), u[q]);
+      for (int q = 0; q < NBW; ++q) {
+        const int nb = cg + NCG * q;
+        if (NB % NCG == 0 || nb < NB) {
+          const auto zh = frag_along<T, LP>(zsh, 16 * nb + r, kp * KB, g);
+#pragma unroll
+          for (int rr = 0; rr < RPW; ++rr) u[rr][q] = M::mma(ao[rr][kp], zh, u[rr][q]);
+          if constexpr (sizeof(T) == 2) {
+            const auto zl = frag_along<T, LP>(zlo, 16 * nb + r, kp * KB, g);
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) u[rr][q] = M::mma(ao[rr][kp], zl, u[rr][q]);
+          }
         }
       }
     }
     const int lv = c_log + k;
     const float gk = gap_s[k];
-    f32x4 part;  // this wave's share of C_t . u_t, per row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tw + 4 * g + i;
-      const float wt = M::ex(cum[t] + gk);
-      float pt = 0.f;
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int tw = 16 * (RPW * rg + rr);
+      f32x4 part;  // this wave's share of C_t . u_t, per row
 #pragma unroll
-      for (int q = 0; q < NBH; ++q)
-        if (NB % 2 == 0 || half + 2 * q < NB) pt += u[q][i] * cv[q][i];
-      part[i] = pt;
-      const float lk = lam_s[t][lv];
+      for (int i = 0; i < 4; ++i) {
+        const int t = tw + 4 * g + i;
+        const float wt = M::ex(cum[t] + gk);
+        float pt = 0.f;
 #pragma unroll
-      for (int q = 0; q < NBH; ++q) dc[q][i] += (lk * wt) * u[q][i];
-    }
-    {
-      // lanes r < 4 of lane group g hold the row sums of t = tw + 4 g +
-      // [0, 2, 1, 3][r]: this wave's share of dlambda[t][lv]
-      const float rs = sum16x4(part, r);
-      if (r < 4) {
-        const int t = tw + 4 * g + (((r & 1) << 1) | (r >> 1));
-        const float dl = M::ex(cum[t] + gk) * rs;
-        dlam_h[t][lv] = dl;
-        term_h[t] += lam_s[t][lv] * dl;
+        for (int q = 0; q < NBW; ++q)
+          if (NB % NCG == 0 || cg + NCG * q < NB) pt += u[rr][q][i] * cv[rr][q][i];
+        part[i] = pt;
+        const float lk = lam_s[t][lv];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) dc[rr][q][i] += (lk * wt) * u[rr][q][i];
       }
+      // lanes r < 4 of lane group g hold the row sums of t = tw + 4 g +
+      // [0, 2, 1, 3][r]: this column group's share
+      const float rs = sum16x4(part, r);
+      if (r < 4) red[buf][cg][tw + 4 * g + (((r & 1) << 1) | (r >> 1))] = rs;
     }
-    lds_barrier();  // zsh is restaged by the next level
+    lds_barrier();  // zsh is restaged by the next level; red[buf] is complete
+    pk = k;
     k = kn;
     buf ^= 1;
   }
+  if (pk) finish_level(pk, buf ^ 1);
 
   T* dcg = static_cast<T*>(pr.dch) + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
-  for (int q = 0; q < NBH; ++q)
-    if (NB % 2 == 0 || half + 2 * q < NB) {
+  for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dcg[(int64_t)(tw + 4 * g + i) * H * N + 16 * (half + 2 * q) + r] = from_f<T>(dc[q][i]);
-    }
+    for (int q = 0; q < NBW; ++q)
+      if (NB % NCG == 0 || cg + NCG * q < NB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dcg[(int64_t)(16 * (RPW * rg + rr) + 4 * g + i) * H * N + 16 * (cg + NCG * q) + r] =
+              from_f<T>(dc[rr][q][i]);
+      }
+  lds_barrier();  // dlam_s is complete
   T* dlg = static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L;
   for (int i = tid; i < C * L; i += NT) {
     const int t = i / L, l = i % L;
-    float v = 0.f;
-    if (l < pr.ll) v = l <= c_log ? dlam_s[t][l] : dlam_s[t][l] + dlam_t[t][l];
-    dlg[(int64_t)t * H * L + l] = from_f<T>(v);
+    dlg[(int64_t)t * H * L + l] = from_f<T>(l < pr.ll ? dlam_s[t][l] : 0.f);
   }
-  if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid] + term_t[tid];
+  if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid];
   lds_barrier();  // the next tile restages every LDS array
   }
 }
 
-// The mask epilogue runs per query row block as in bwd_dq_kernel; then the
-// two waves w of a pair own key rows [16 (w mod C/16), +16), each every
-// other 16-column tile of P and of N: dX_s = sum_t (M ⊙ S)[t, s] dO_t and
+// The mask epilogue runs per query row block as in bwd_dq_kernel; then, as
+// there, each wave takes RPW adjacent 16-row blocks of keys and every
+// NCG-th 16-column tile of P and of N (a level-state fragment read from LDS
+// serves both row blocks): dX_s = sum_t (M ⊙ S)[t, s] dO_t and
 // dB_s = sum_t (M ⊙ D)[t, s] C_t within the chunk, plus, for each chunk level
 // k whose bit is clear in i and whose upper half exists,
 // exp(decay s -> end of the lower half) (R_k^T B_s, R_k X_s) with R_k the
@@ -838,8 +880,10 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  constexpr int NWR = C / 16, NW = 2 * NWR, NT = NW * 64, KB = M::KB, NB = N / 16, PB = P / 16;
-  constexpr int NBH = (NB + 1) / 2, PBH = (PB + 1) / 2;  // column tiles per wave
+  using CS = ChunkSplit<C>;
+  constexpr int NWR = CS::NWR, NW = CS::NW, NT = NW * 64, KB = M::KB, NB = N / 16, PB = P / 16;
+  constexpr int RPW = CS::RPW, NRG = CS::NRG, NCG = CS::NCG;
+  constexpr int NBW = (NB + NCG - 1) / NCG, PBW = (PB + NCG - 1) / NCG;  // column tiles per wave
   constexpr int c_log = ilog2c(C);
   __shared__ __attribute__((aligned(16))) T csh[C * N];
   __shared__ __attribute__((aligned(16))) T bsh[C * N];
@@ -852,10 +896,11 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   __shared__ float gsh[C][C + 1];
   __shared__ float lam_s[C][8];
   __shared__ float colpart[NW][64];
-  __shared__ float xpart[2][64];  // X_s . (chunk-level dX_s), per wave of a pair
+  __shared__ float xpart[NCG][64];  // X_s . (chunk-level dX_s), per column group
   __shared__ float cum[64], ecum[64], wst[64], gap_s[BWD_LMAX];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int half = wave >= NWR ? 1 : 0, rb = wave - half * NWR;
+  const int rg = wave % NRG, cg = wave / NRG;  // state products: row group, column group
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int64_t T_ = pr.seqlen;
   const ChunkTiles ct(pr.batch * H * pr.nc);
@@ -941,33 +986,46 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     colpart[wave][lane] = cs;
   }
 
-  const int sw = 16 * rb;
-  // dX: intra-chunk part, chunk-level part (column tile half + 2 q of each)
-  f32x4 dx[PBH], dxe[PBH], db[NBH];
+  // dX: intra-chunk part, chunk-level part; dB (row block RPW rg + rr,
+  // column tile cg + NCG q of P or of N)
+  f32x4 dx[RPW][PBW], dxe[RPW][PBW], db[RPW][NBW];
 #pragma unroll
-  for (int q = 0; q < PBH; ++q) dx[q] = dxe[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rr = 0; rr < RPW; ++rr) {
 #pragma unroll
-  for (int q = 0; q < NBH; ++q) db[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < PBW; ++q) dx[rr][q] = dxe[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) db[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int kt = 0; kt < C / KB; ++kt) {  // queries t; entries with t < s are zero
-    const auto aw = frag_down<T, LC>(wsh, kt * KB, sw, g, r);
-    const auto av = frag_down<T, LC>(vsh, kt * KB, sw, g, r);
+    typename M::frag aw[RPW], av[RPW];
 #pragma unroll
-    for (int q = 0; q < PBH; ++q)
-      if (PB % 2 == 0 || half + 2 * q < PB)
-        dx[q] = M::mma(aw, frag_down<T, LP>(osh, kt * KB, 16 * (half + 2 * q), g, r), dx[q]);
+    for (int rr = 0; rr < RPW; ++rr) {
+      aw[rr] = frag_down<T, LC>(wsh, kt * KB, 16 * (RPW * rg + rr), g, r);
+      av[rr] = frag_down<T, LC>(vsh, kt * KB, 16 * (RPW * rg + rr), g, r);
+    }
 #pragma unroll
-    for (int q = 0; q < NBH; ++q)
-      if (NB % 2 == 0 || half + 2 * q < NB)
-        db[q] = M::mma(av, frag_down<T, LN>(csh, kt * KB, 16 * (half + 2 * q), g, r), db[q]);
+    for (int q = 0; q < PBW; ++q)
+      if (PB % NCG == 0 || cg + NCG * q < PB) {
+        const auto bo = frag_down<T, LP>(osh, kt * KB, 16 * (cg + NCG * q), g, r);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) dx[rr][q] = M::mma(aw[rr], bo, dx[rr][q]);
+      }
+#pragma unroll
+    for (int q = 0; q < NBW; ++q)
+      if (NB % NCG == 0 || cg + NCG * q < NB) {
+        const auto bc = frag_down<T, LN>(csh, kt * KB, 16 * (cg + NCG * q), g, r);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) db[rr][q] = M::mma(av[rr], bc, db[rr][q]);
+      }
   }
 
-  // this wave's B and X row fragments, the A operands of every chunk level
-  typename M::frag abf[N / KB], axf[P / KB];
+  // this wave's X row fragments, an A operand of every chunk level
+  typename M::frag axf[RPW][P / KB];
 #pragma unroll
-  for (int kn2 = 0; kn2 < N / KB; ++kn2) abf[kn2] = frag_along<T, LN>(bsh, sw + r, kn2 * KB, g);
+  for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-  for (int kp = 0; kp < P / KB; ++kp) axf[kp] = frag_along<T, LP>(xsh, sw + r, kp * KB, g);
+    for (int kp = 0; kp < P / KB; ++kp) axf[rr][kp] = frag_along<T, LP>(xsh, 16 * (RPW * rg + rr) + r, kp * KB, g);
 
   int buf = 0;
   while (k) {
@@ -986,47 +1044,63 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
       else
         st1.load(state_of(k3), tid);
     }
-    f32x4 tx[PBH], tb[NBH];
+    f32x4 tx[RPW][PBW], tb[RPW][NBW];
 #pragma unroll
-    for (int q = 0; q < PBH; ++q) tx[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < RPW; ++rr) {
 #pragma unroll
-    for (int q = 0; q < NBH; ++q) tb[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < PBW; ++q) tx[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NBW; ++q) tb[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int kn2 = 0; kn2 < N / KB; ++kn2) {  // tx[s][p] = sum_n B[s][n] R[n][p]
-      const auto a = abf[kn2];
+      typename M::frag ab[RPW];
 #pragma unroll
-      for (int q = 0; q < PBH; ++q) {
-        const int pb = half + 2 * q;
-        if (PB % 2 == 0 || pb < PB) {
-          tx[q] = M::mma(a, frag_down<T, LP>(rsh, kn2 * KB, 16 * pb, g, r), tx[q]);
-          if constexpr (sizeof(T) == 2)
-            tx[q] = M::mma(a, frag_down<T, LP>(rlo, kn2 * KB, 16 * pb, g, r), tx[q]);
+      for (int rr = 0; rr < RPW; ++rr) ab[rr] = frag_along<T, LN>(bsh, 16 * (RPW * rg + rr) + r, kn2 * KB, g);
+#pragma unroll
+      for (int q = 0; q < PBW; ++q) {
+        const int pb = cg + NCG * q;
+        if (PB % NCG == 0 || pb < PB) {
+          const auto rh = frag_down<T, LP>(rsh, kn2 * KB, 16 * pb, g, r);
+#pragma unroll
+          for (int rr = 0; rr < RPW; ++rr) tx[rr][q] = M::mma(ab[rr], rh, tx[rr][q]);
+          if constexpr (sizeof(T) == 2) {
+            const auto rl = frag_down<T, LP>(rlo, kn2 * KB, 16 * pb, g, r);
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) tx[rr][q] = M::mma(ab[rr], rl, tx[rr][q]);
+          }
         }
       }
     }
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) {  // tb[s][n] = sum_p X[s][p] R[n][p]
-      const auto a = axf[kp];
 #pragma unroll
-      for (int q = 0; q < NBH; ++q) {
-        const int nb = half + 2 * q;
-        if (NB % 2 == 0 || nb < NB) {
-          tb[q] = M::mma(a, frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g), tb[q]);
-          if constexpr (sizeof(T) == 2)
-            tb[q] = M::mma(a, frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g), tb[q]);
+      for (int q = 0; q < NBW; ++q) {
+        const int nb = cg + NCG * q;
+        if (NB % NCG == 0 || nb < NB) {
+          const auto rh = frag_along<T, LP>(rsh, 16 * nb + r, kp * KB, g);
+#pragma unroll
+          for (int rr = 0; rr < RPW; ++rr) tb[rr][q] = M::mma(axf[rr][kp], rh, tb[rr][q]);
+          if constexpr (sizeof(T) == 2) {
+            const auto rl = frag_along<T, LP>(rlo, 16 * nb + r, kp * KB, g);
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) tb[rr][q] = M::mma(axf[rr][kp], rl, tb[rr][q]);
+          }
         }
       }
     }
     const float gk = gap_s[k];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = sw + 4 * g + i;
-      const float w = M::ex(cum[C - 1] - cum[s] + gk);
+    for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-      for (int q = 0; q < PBH; ++q) dxe[q][i] += w * tx[q][i];
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * (RPW * rg + rr) + 4 * g + i;
+        const float w = M::ex(cum[C - 1] - cum[s] + gk);
 #pragma unroll
-      for (int q = 0; q < NBH; ++q) db[q][i] += w * tb[q][i];
-    }
+        for (int q = 0; q < PBW; ++q) dxe[rr][q][i] += w * tx[rr][q][i];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) db[rr][q][i] += w * tb[rr][q][i];
+      }
     lds_barrier();  // rsh is restaged by the next level
     k = kn;
     buf ^= 1;
@@ -1034,29 +1108,40 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   T* dxg = static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P;
   T* dbg = static_cast<T*>(pr.dbh) + (((int64_t)b * T_ + t0) * H + h) * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = sw + 4 * g + i;
-    float part = 0.f;  // X_s . (chunk-level part of dX_s), this wave's columns
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int sw = 16 * (RPW * rg + rr);
+    f32x4 part;  // X_s . (chunk-level part of dX_s), this wave's columns
 #pragma unroll
-    for (int q = 0; q < PBH; ++q) {
-      const int pb = half + 2 * q;
-      if (PB % 2 == 0 || pb < PB) {
-        part += dxe[q][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
-        dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[q][i] + dxe[q][i]);
+    for (int i = 0; i < 4; ++i) {
+      const int s = sw + 4 * g + i;
+      float pt = 0.f;
+#pragma unroll
+      for (int q = 0; q < PBW; ++q) {
+        const int pb = cg + NCG * q;
+        if (PB % NCG == 0 || pb < PB) {
+          pt += dxe[rr][q][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
+          dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[rr][q][i] + dxe[rr][q][i]);
+        }
       }
-    }
+      part[i] = pt;
 #pragma unroll
-    for (int q = 0; q < NBH; ++q)
-      if (NB % 2 == 0 || half + 2 * q < NB) dbg[(int64_t)s * H * N + 16 * (half + 2 * q) + r] = from_f<T>(db[q][i]);
-    part = sum16(part);
-    if (r == 0) xpart[half][s] = part;
+      for (int q = 0; q < NBW; ++q)
+        if (NB % NCG == 0 || cg + NCG * q < NB)
+          dbg[(int64_t)s * H * N + 16 * (cg + NCG * q) + r] = from_f<T>(db[rr][q][i]);
+    }
+    // lanes r < 4 of lane group g hold the row sums of s = sw + 4 g + [0, 2, 1, 3][r]
+    const float rs = sum16x4(part, r);
+    if (r < 4) xpart[cg][sw + 4 * g + (((r & 1) << 1) | (r >> 1))] = rs;
   }
   lds_barrier();  // colpart and xpart are complete (also when no level ran)
   if (tid < C) {
     float cs = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) cs += colpart[w][tid];
-    pr.term2[(int64_t)bh * T_ + t0 + tid] = cs + (xpart[0][tid] + xpart[1][tid]);
+    float xs = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) xs += xpart[c][tid];
+    pr.term2[(int64_t)bh * T_ + t0 + tid] = cs + xs;
   }
   lds_barrier();  // the next tile restages every LDS array
   }
