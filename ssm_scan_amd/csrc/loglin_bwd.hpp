@@ -436,15 +436,27 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
 
 // LDS bytes of the two chunk passes (the host only instantiates shapes that
 // fit the 160 KB of a CU).
+// Work split of the chunk passes' products with the state dimension (see
+// bwd_dq_kernel).
+template <class T, int C>
+struct ChunkSplit {
+  static constexpr int NWR = C / 16, NW = 2 * NWR;
+  // 16-row blocks per wave (fp32 keeps one: its operands take four times the
+  // registers per contraction step)
+  static constexpr int RPW = (sizeof(T) == 2 && NWR >= 2) ? 2 : 1;
+  static constexpr int NRG = NWR / RPW;         // row groups
+  static constexpr int NCG = NW / NRG;          // column groups
+};
+
 template <class T, int C, int P, int N>
 constexpr int bwd_dq_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + 2 * C * BWD_LMAX + 4 * 64 + BWD_LMAX + 2 * (2 * C / 16) * 64);
+         4 * (C * (C + 1) + 2 * C * BWD_LMAX + 4 * 64 + BWD_LMAX + 2 * ChunkSplit<T, C>::NCG * 64);
 }
 template <class T, int C, int P, int N>
 constexpr int bwd_dkv_lds() {
   return (int)sizeof(T) * (2 * C * N + 2 * C * P + 2 * C * C + (sizeof(T) == 2 ? 2 : 1) * N * P) +
-         4 * (C * (C + 1) + C * 8 + (C / 8) * 64 + (2 * C / 16) * 64 + 3 * 64 + BWD_LMAX);
+         4 * (C * (C + 1) + C * 8 + (C / 8) * 64 + ChunkSplit<T, C>::NCG * 64 + 3 * 64 + BWD_LMAX);
 }
 
 // S = C B^T and D = dO X^T for the query rows [16 rb, +16) of the chunk,
@@ -589,20 +601,13 @@ struct ChunkTiles {
 // The next level's state is loaded into registers while the current one
 // is used.
 constexpr int bwd_chunk_threads(int C) { return C / 16 * 128; }
-template <int C>
-struct ChunkSplit {
-  static constexpr int NWR = C / 16, NW = 2 * NWR;
-  static constexpr int RPW = NWR >= 2 ? 2 : 1;  // 16-row blocks per wave
-  static constexpr int NRG = NWR / RPW;         // row groups
-  static constexpr int NCG = NW / NRG;          // column groups
-};
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams pr) {
   using M = Mfma<T>;
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  using CS = ChunkSplit<C>;
+  using CS = ChunkSplit<T, C>;
   constexpr int NWR = CS::NWR, NW = CS::NW, NT = NW * 64, KB = M::KB, NB = N / 16;
   constexpr int RPW = CS::RPW, NRG = CS::NRG, NCG = CS::NCG;
   constexpr int NBW = (NB + NCG - 1) / NCG;  // column tiles per wave in the state products
@@ -880,7 +885,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   using LN = Rows<T, N>;
   using LP = Rows<T, P>;
   using LC = Rows<T, C>;
-  using CS = ChunkSplit<C>;
+  using CS = ChunkSplit<T, C>;
   constexpr int NWR = CS::NWR, NW = CS::NW, NT = NW * 64, KB = M::KB, NB = N / 16, PB = P / 16;
   constexpr int RPW = CS::RPW, NRG = CS::NRG, NCG = CS::NCG;
   constexpr int NBW = (NB + NCG - 1) / NCG, PBW = (PB + NCG - 1) / NCG;  // column tiles per wave
@@ -1020,12 +1025,21 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
       }
   }
 
-  // this wave's X row fragments, an A operand of every chunk level
-  typename M::frag axf[RPW][P / KB];
+  // this wave's B and X row fragments, the A operands of every chunk level
+  // (B's for bf16 only: fp32 fragments hold one element each, and N / 4 of
+  // them per row block would not fit in registers)
+  constexpr bool HOLD_B = sizeof(T) == 2;
+  typename M::frag abf[RPW][HOLD_B ? N / KB : 1], axf[RPW][P / KB];
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
+  for (int rr = 0; rr < RPW; ++rr) {
+    if constexpr (HOLD_B) {
+#pragma unroll
+      for (int kn2 = 0; kn2 < N / KB; ++kn2)
+        abf[rr][kn2] = frag_along<T, LN>(bsh, 16 * (RPW * rg + rr) + r, kn2 * KB, g);
+    }
 #pragma unroll
     for (int kp = 0; kp < P / KB; ++kp) axf[rr][kp] = frag_along<T, LP>(xsh, 16 * (RPW * rg + rr) + r, kp * KB, g);
+  }
 
   int buf = 0;
   while (k) {
@@ -1056,7 +1070,8 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     for (int kn2 = 0; kn2 < N / KB; ++kn2) {  // tx[s][p] = sum_n B[s][n] R[n][p]
       typename M::frag ab[RPW];
 #pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) ab[rr] = frag_along<T, LN>(bsh, 16 * (RPW * rg + rr) + r, kn2 * KB, g);
+      for (int rr = 0; rr < RPW; ++rr)
+        ab[rr] = HOLD_B ? abf[rr][HOLD_B ? kn2 : 0] : frag_along<T, LN>(bsh, 16 * (RPW * rg + rr) + r, kn2 * KB, g);
 #pragma unroll
       for (int q = 0; q < PBW; ++q) {
         const int pb = cg + NCG * q;
