@@ -151,7 +151,7 @@ def _oracle_task(args):
 CPU_SHARE = 16
 
 
-def cpu_baseline(cfg, d, budget_s: float) -> dict:
+def cpu_baseline(cfg, d, budget_s: float, use_pool: bool = True) -> dict:
     """Time the fp64 oracle on uniformly random output rows (all heads) of
     the workload: rows cost O(t) each, so random rows give an unbiased
     per-token rate of the full O(T^2) oracle.  Runs in a fork pool before
@@ -180,6 +180,8 @@ def cpu_baseline(cfg, d, budget_s: float) -> dict:
     done, el, how = 0, 0.0, None
     ctx = mp.get_context("fork")
     try:
+        if not use_pool:
+            raise mp.TimeoutError("in-process timing requested")
         with ctx.Pool(workers) as pool:
             # warm the workers (imports), then calibrate on two rows per worker
             pool.map_async(_oracle_task, [(0, [0])] * workers).get(timeout=60)
@@ -214,8 +216,9 @@ def cpu_baseline(cfg, d, budget_s: float) -> dict:
             pool.terminate()
         how = f"{workers} processes x 1 BLAS thread"
     except mp.TimeoutError:
-        print("[bench] cpu oracle: the worker pool stopped answering; timing in this process",
-              file=sys.stderr, flush=True)
+        if use_pool:
+            print("[bench] cpu oracle: the worker pool stopped answering; timing in this process",
+                  file=sys.stderr, flush=True)
     if done == 0:  # the pool leg failed: one core, in this process
         from threadpoolctl import threadpool_limits
 
@@ -248,6 +251,40 @@ def cpu_baseline(cfg, d, budget_s: float) -> dict:
         "seconds": el,
         "check": check,
     }
+
+
+def cpu_baseline_guarded(cfg, d, budget_s: float) -> dict:
+    """cpu_baseline in a forked child process of its own process group, with
+    a deadline: if it has not answered by then, the child and its pool are
+    killed and the rows are timed here on one core instead.  (Runs before
+    the GPU is touched, so forking is safe.)"""
+    import signal
+
+    ctx = mp.get_context("fork")
+    rd, wr = ctx.Pipe(duplex=False)
+
+    def child():
+        os.setpgrp()  # the pool's workers join this group
+        try:
+            wr.send(cpu_baseline(cfg, d, budget_s))
+        except Exception as e:  # noqa: BLE001 - reported to the parent
+            wr.send({"error": repr(e)})
+        os._exit(0)
+
+    p = ctx.Process(target=child)
+    p.start()
+    res = rd.recv() if rd.poll(budget_s + 150.0) else None
+    try:
+        os.killpg(p.pid, signal.SIGKILL)  # leftovers of the pool, if any
+    except (ProcessLookupError, PermissionError):
+        pass
+    p.join(10)
+    if res is None or "error" in res:
+        why = "no answer" if res is None else res["error"]
+        print(f"[bench] cpu oracle: the pool leg failed ({why}); timing in this process",
+              file=sys.stderr, flush=True)
+        res = cpu_baseline(cfg, d, budget_s, use_pool=False)
+    return res
 
 
 def check_against_sample(out, check, max_pairs=4096) -> dict:
@@ -359,7 +396,7 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, d, args.cpu_budget)
+        cpu = cpu_baseline_guarded(cfg, d, args.cpu_budget)
 
     import torch
 
