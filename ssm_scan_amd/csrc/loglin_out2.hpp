@@ -296,8 +296,11 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
   issue_lam(j0);
   load_la(j0);
 
-  auto step = [&](auto cur_c, int jl) __attribute__((always_inline)) {
-    constexpr int CUR = decltype(cur_c)::value;
+  // one chunk; Q = jl mod 4 (jl's low bits fix which local levels it reads
+  // and where it pushes its state), CUR = jl mod 2 (the buffer parity)
+  auto step = [&](auto q_c, int jl) __attribute__((always_inline)) {
+    constexpr int Q = decltype(q_c)::value;
+    constexpr int CUR = Q & 1;
     unsigned char* bs = CUR ? bsh1 : bsh0;
     unsigned char* xs = CUR ? xsh1 : xsh0;
     const int j = j0 + jl;
@@ -441,7 +444,8 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
         if (i < nres && (!MASKED || ((lmask >> lres[i]) & 1))) level(zres[i], lres[i], eres[i], half);
 #pragma unroll
       for (int e = 0; e < MM; ++e)
-        if (e < m && ((jl >> e) & 1) && (!MASKED || ((lmask >> (c_log + e + 1)) & 1)))
+        if (e < m && (e < 2 ? ((Q >> e) & 1) != 0 : ((jl >> e) & 1) != 0) &&
+            (!MASKED || ((lmask >> (c_log + e + 1)) & 1)))
           level(zl[e], c_log + e + 1, eloc[e], half);
     }
     // levels above the segment past the resident ones (a segment index with
@@ -529,7 +533,9 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
           Sn[kk][1][i] = __uint_as_float(s16[1]);
         }
       // merge with the entries of the blocks this chunk completes
-      const int z = __builtin_ctz(~(unsigned)jl);  // trailing ones of jl
+      // trailing ones of jl: fixed by Q while a next chunk exists (a segment
+      // has at most 8 chunks, so jl = 7 has none)
+      constexpr int z = Q == 1 ? 1 : (Q == 3 ? 2 : 0);
       float cur_a = atot;
 #pragma unroll
       for (int e = 0; e < MM; ++e) {
@@ -559,16 +565,18 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
 #pragma unroll
     for (int k = 1; k <= MM; ++k) {
       dloc[k] += atot;
-      if (((jl + 1) & ((1 << (k - 1)) - 1)) == 0) dloc[k] = 0.f;
+      if (((Q + 1) & ((1 << (k - 1)) - 1)) == 0) dloc[k] = 0.f;
     }
     // No barrier here: the next chunk writes only the other parity's decays
     // before its first barrier, and every tile it overwrites after that
     // barrier was last read before this chunk's staging barrier or, for B
     // and X, two chunks back.
   };
-  for (int jl = 0; jl < nch; jl += 2) {
+  for (int jl = 0; jl < nch; jl += 4) {
     step(std::integral_constant<int, 0>{}, jl);
     if (jl + 1 < nch) step(std::integral_constant<int, 1>{}, jl + 1);
+    if (jl + 2 < nch) step(std::integral_constant<int, 2>{}, jl + 2);
+    if (jl + 3 < nch) step(std::integral_constant<int, 3>{}, jl + 3);
   }
 }
 
