@@ -799,12 +799,241 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
   }
 }
 
+// ---- the chunk pass for bf16 inputs
+
+// A operand of a 16x16x32 bf16 product from an fp32 C x C tile (LDS, Rows
+// layout): lane (g, r) takes row `row`, columns 8 g .. 8 g + 7, each scaled
+// by sc[column], split into a bf16 hi / lo pair.
+__device__ inline void split_a32(const float* tile, const float* sc, int row, int g, bf16x8& hi, bf16x8& lo) {
+  using LC = Rows<float, GDN_C>;
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(tile + LC::at(row, 8 * g));
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(tile + LC::at(row, 8 * g + 4));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (e < 4 ? a0[e] : a1[e - 4]) * (sc ? sc[8 * g + e] : 1.f);
+    const bf16 h = (bf16)x;
+    hi[e] = h;
+    lo[e] = (bf16)(x - (float)h);
+  }
+}
+
+// Same work as gdn_chunk_kernel.  Q, K and V are bf16 already, so Q K^T and
+// K K^T run on v_mfma_f32_16x16x32_bf16 exactly (fp32 accumulation), and the
+// products of an fp32 C x C factor with K or V (W, U, Qe, the intra outputs)
+// split the fp32 factor into a bf16 hi / lo pair against the exact bf16
+// operand (two products per tile, one contraction step of 32 tokens).  The
+// triangular inverse and G stay fp32.  Q, K and V are staged in bf16, which
+// halves their LDS.
+template <int N, int P>
+__global__ __launch_bounds__(GDN_NT) void gdn_chunk_bf16_kernel(GdnParams pr) {
+  using T = bf16;
+  using MF = Mfma<float>;
+  using MB = Mfma<bf16>;
+  using frag = bf16x8;
+  constexpr int C = GDN_C, NT = GDN_NT, c_log = 5;
+  static_assert(C == 32 && N % 32 == 0 && P % 16 == 0, "tile shapes");
+  constexpr int NTILE = N / 16, PT = P / 16;
+  using LN = GdnRowsN<N>;
+  using LV = std::conditional_t<P == 32, R32, Rows<bf16, P>>;
+  using LC = Rows<float, C>;
+  __shared__ __attribute__((aligned(16))) bf16 qb[C * N];
+  __shared__ __attribute__((aligned(16))) bf16 kb[C * N];
+  __shared__ __attribute__((aligned(16))) bf16 vbf[C * P];
+  __shared__ __attribute__((aligned(16))) float am[C * C];  // tril(Q K^T ⊙ Gamma)
+  __shared__ __attribute__((aligned(16))) float lm[C * C];  // L
+  __shared__ __attribute__((aligned(16))) float tm[C * C];  // Th = (I + L)^-1
+  __shared__ __attribute__((aligned(16))) float gm[C * C];  // G
+  __shared__ __attribute__((aligned(16))) float gl[C * C];  // G ⊙ lambda by level
+  __shared__ __attribute__((aligned(16))) float pt[C * C];  // block-inverse temporary
+  __shared__ float lam_s[C][8];                              // intra-chunk levels 0..c
+  __shared__ float cum[C], gam[C], bet[C], bg[C];
+
+  const int item = blockIdx.x;  // (batch*head) * nc + chunk
+  const int bh = item / pr.nc, j = item % pr.nc;
+  const int H = pr.nheads, L = pr.nlevels;
+  const int b = bh / H, h = bh % H;
+  const int64_t T_ = pr.seqlen, t0 = (int64_t)j * C;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const T* qg = static_cast<const T*>(pr.q);
+  const T* kg = static_cast<const T*>(pr.k);
+  const T* vg = static_cast<const T*>(pr.v);
+  const T* lg = static_cast<const T*>(pr.lam);
+
+  for (int i = tid; i < C * N / 8; i += NT) {  // eight keys / queries per thread and step
+    const int t = (8 * i) / N, n = (8 * i) % N;
+    const int64_t row = ((int64_t)b * T_ + t0 + t) * H + h;
+    *reinterpret_cast<bf16x8*>(qb + LN::at(t, n)) = *reinterpret_cast<const bf16x8*>(qg + row * N + n);
+    *reinterpret_cast<bf16x8*>(kb + LN::at(t, n)) = *reinterpret_cast<const bf16x8*>(kg + row * N + n);
+  }
+  for (int i = tid; i < C * P / 8; i += NT) {
+    const int t = (8 * i) / P, p = (8 * i) % P;
+    *reinterpret_cast<bf16x8*>(vbf + LV::at(t, p)) =
+        *reinterpret_cast<const bf16x8*>(vg + (((int64_t)b * T_ + t0 + t) * H + h) * P + p);
+  }
+  for (int i = tid; i < C * (c_log + 1); i += NT) {
+    const int t = i / (c_log + 1), l = i % (c_log + 1);
+    lam_s[t][l] = to_f(lg[(((int64_t)b * T_ + t0 + t) * H + h) * L + l]);
+  }
+  if (tid < 64) {  // inclusive cumulative log alpha over the chunk
+    const int64_t gi = ((int64_t)b * T_ + t0 + (tid < C ? tid : 0)) * H + h;
+    float x = tid < C ? pr.log_alpha[gi] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(x, d, 64);
+      if (tid >= d) x += o;
+    }
+    const float tot = __shfl(x, C - 1, 64);
+    if (tid < C) {
+      const float be = pr.beta[gi];
+      cum[tid] = x;
+      gam[tid] = expf(x);
+      bet[tid] = be;
+      bg[tid] = be * expf(x);
+      pr.kh[(int64_t)item * C + tid] = expf(tot - x);  // gamma_C / gamma_t
+      if (tid == 0) pr.gc[item] = expf(tot);
+    }
+  }
+  __syncthreads();
+  // ---- Q K^T and K K^T, masked: wave w owns the 16x16 tile (w >> 1, w & 1)
+  {
+    const int tb = wave >> 1, sb = wave & 1;
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+    if (sb <= tb) {
+#pragma unroll
+      for (int kk = 0; kk < N / 32; ++kk) {
+        const frag bk = *reinterpret_cast<const frag*>(kb + LN::at(16 * sb + r, 32 * kk + 8 * g));
+        sq = MB::mma(*reinterpret_cast<const frag*>(qb + LN::at(16 * tb + r, 32 * kk + 8 * g)), bk, sq);
+        sk = MB::mma(*reinterpret_cast<const frag*>(kb + LN::at(16 * tb + r, 32 * kk + 8 * g)), bk, sk);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+      const float gr = s <= t ? expf(cum[t] - cum[s]) : 0.f;
+      am[LC::at(t, s)] = sq[i] * gr;
+      lm[LC::at(t, s)] = s < t ? bet[t] * sk[i] * gr : 0.f;
+    }
+  }
+  __syncthreads();
+  // ---- Th = (I + L)^-1, blocked: 8x8 diagonal blocks by substitution,
+  // then [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1, D^-1]] at 16, 32
+  if (tid < C) {  // column jc of its 8x8 diagonal block, in registers
+    const int jc = tid, blk = jc & ~7, jj = jc & 7;
+    float x[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      float v = ii == jj ? 1.f : 0.f;
+#pragma unroll
+      for (int mm = 0; mm < ii; ++mm) v -= lm[LC::at(blk + ii, blk + mm)] * x[mm];
+      x[ii] = ii < jj ? 0.f : v;  // above the diagonal: zero
+    }
+    for (int i = 0; i < C; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) v = i == blk + ii ? x[ii] : v;
+      tm[LC::at(i, jc)] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb = 8; hb < C; hb *= 2) {  // half block size: 8, then 16
+    const int cnt = (C / (2 * hb)) * hb * hb;
+    for (int i = tid; i < cnt; i += NT) {  // B A^-1 (rows in the lower half, columns in the upper)
+      const int blk = i / (hb * hb), e = i % (hb * hb);
+      const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
+      float x = 0.f;
+      for (int m = col; m < blk * 2 * hb + hb; ++m) x += lm[LC::at(row, m)] * tm[LC::at(m, col)];
+      pt[LC::at(row, col)] = x;
+    }
+    __syncthreads();
+    for (int i = tid; i < cnt; i += NT) {  // the lower-left block: -D^-1 (B A^-1)
+      const int blk = i / (hb * hb), e = i % (hb * hb);
+      const int row = blk * 2 * hb + hb + e / hb, col = blk * 2 * hb + e % hb;
+      float x = 0.f;
+      for (int m = blk * 2 * hb + hb; m <= row; ++m) x -= tm[LC::at(row, m)] * pt[LC::at(m, col)];
+      tm[LC::at(row, col)] = x;
+    }
+    __syncthreads();
+  }
+  // ---- G = tril(Q K^T ⊙ Gamma) Th diag(beta) and G ⊙ lambda (fp32)
+  {
+    const int tb = wave >> 1, sb = wave & 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m0 = 0; m0 < C; m0 += 4)
+      acc = MF::mma(frag_along<float, LC>(am, 16 * tb + r, m0, g),
+                    frag_down<float, LC>(tm, m0, 16 * sb, g, r), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+      const float gv = s <= t ? acc[i] * bet[s] : 0.f;
+      gm[LC::at(t, s)] = gv;
+      gl[LC::at(t, s)] = s <= t ? gv * lam_s[t][bit_length((unsigned)(t ^ s))] : 0.f;
+    }
+  }
+  // ---- U = Th diag(beta) V and W = Th diag(beta gamma) K, straight to the
+  //      workspace (row tile tile & 1, column tile tile >> 1)
+  float* ug = pr.u + (int64_t)item * C * P;
+  float* wg = pr.w + (int64_t)item * C * N;
+  for (int tile = wave; tile < 2 * PT; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    frag ah, al;
+    split_a32(tm, bet, 16 * tb + r, g, ah, al);
+    const frag bv = frag_down_bf16<LV>(vbf, 0, 16 * cb, g, r);
+    f32x4 acc = MB::mma(ah, bv, f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = MB::mma(al, bv, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ug[(16 * tb + 4 * g + i) * P + 16 * cb + r] = acc[i];
+  }
+  for (int tile = wave; tile < 2 * NTILE; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    frag ah, al;
+    split_a32(tm, bg, 16 * tb + r, g, ah, al);
+    const frag bk = frag_down_bf16<LN>(kb, 0, 16 * cb, g, r);
+    f32x4 acc = MB::mma(ah, bk, f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = MB::mma(al, bk, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wg[(16 * tb + 4 * g + i) * N + 16 * cb + r] = acc[i];
+  }
+  __syncthreads();  // gm and gl are complete
+  // ---- Qe = diag(gamma) Q - G diag(gamma) K and the intra outputs (G ⊙ lambda) V
+  float* qeg = pr.qe + (int64_t)item * C * N;
+  float* oig = pr.oi + (int64_t)item * C * P;
+  for (int tile = wave; tile < 2 * NTILE; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    frag ah, al;
+    split_a32(gm, gam, 16 * tb + r, g, ah, al);
+    const frag bk = frag_down_bf16<LN>(kb, 0, 16 * cb, g, r);
+    f32x4 acc = MB::mma(ah, bk, f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = MB::mma(al, bk, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i, n = 16 * cb + r;
+      qeg[t * N + n] = gam[t] * (float)qb[LN::at(t, n)] - acc[i];
+    }
+  }
+  for (int tile = wave; tile < 2 * PT; tile += 4) {
+    const int tb = tile & 1, cb = tile >> 1;
+    frag ah, al;
+    split_a32(gl, nullptr, 16 * tb + r, g, ah, al);
+    const frag bv = frag_down_bf16<LV>(vbf, 0, 16 * cb, g, r);
+    f32x4 acc = MB::mma(ah, bv, f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = MB::mma(al, bv, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oig[(16 * tb + 4 * g + i) * P + 16 * cb + r] = acc[i];
+  }
+}
+
 using GdnFn = int (*)(const GdnParams&, hipStream_t);
 
 template <class T, int N, int P>
 int launch_gdn(const GdnParams& pr, hipStream_t st) {
   const int items = pr.batch * pr.nheads * pr.nc;
-  hipLaunchKernelGGL((gdn_chunk_kernel<T, N, P>), dim3(items), dim3(GDN_NT), 0, st, pr);
+  if constexpr (sizeof(T) == 2 && N % 32 == 0)
+    hipLaunchKernelGGL((gdn_chunk_bf16_kernel<N, P>), dim3(items), dim3(GDN_NT), 0, st, pr);
+  else
+    hipLaunchKernelGGL((gdn_chunk_kernel<T, N, P>), dim3(items), dim3(GDN_NT), 0, st, pr);
   const int blocks = pr.batch * pr.nheads * (P / GDN_PB);
   if constexpr (sizeof(T) == 2 && N % 32 == 0)
     hipLaunchKernelGGL((gdn_scan_bf16_kernel<N, P>), dim3(blocks), dim3(GDN_SNT), 0, st, pr);
