@@ -300,7 +300,7 @@ __global__ __launch_bounds__(GDN_NT) void gdn_chunk_kernel(GdnParams pr) {
 // One chunk's operands of the level pass, loaded into registers one chunk
 // ahead and then stored to LDS: Qe, W and K (C x N), U and the intra outputs
 // for this work-group's 16 columns, gamma_C / gamma_t, and lambda rows.
-template <class T, int N, int P, int NT_, bool KS = false>
+template <class T, int N, int P, int NT_>
 struct GdnStage {
   static constexpr int C = GDN_C, PB = GDN_PB, NT = NT_;
   static constexpr int NV = (C * PB + NT - 1) / NT;  // U / intra-output values per thread
@@ -308,8 +308,8 @@ struct GdnStage {
   static constexpr int NQ = (NQ4 + NT - 1) / NT;  // per thread
   static constexpr int NL = (C * GDN_LMAX + NT - 1) / NT;
   f32x4 qe[NQ], w[NQ], k[NQ];
-  float ks[KS ? NQ : 1];  // gamma_C / gamma_t of each K row group (KS)
-  float u2[NV], o2[NV], lam[NL], khv, gcv;
+  float u2[NV], o2[NV], khv, gcv;
+  T lam[NL];  // raw: converted (and zeroed past the level count) when staged
   __device__ inline void load(const GdnParams& pr, int item, int b, int h, int64_t t0, int p0, int tid) {
     const float* qeg = pr.qe + (int64_t)item * C * N;
     const float* wg = pr.w + (int64_t)item * C * N;
@@ -327,7 +327,6 @@ struct GdnStage {
       } else {
         k[q] = *reinterpret_cast<const f32x4*>(kr);
       }
-      if constexpr (KS) ks[q] = pr.kh[(int64_t)item * C + t];
     }
 #pragma unroll
     for (int q = 0; q < NV; ++q) {  // C x 16 = 512 values
@@ -337,11 +336,9 @@ struct GdnStage {
     }
     const T* lg = static_cast<const T*>(pr.lam);
 #pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int e = q * NT + tid, t = e / GDN_LMAX, l = e % GDN_LMAX;
-      lam[q] = (t < C && l < pr.ll)
-                   ? to_f(lg[(((int64_t)b * pr.seqlen + t0 + t) * pr.nheads + h) * pr.nlevels + l])
-                   : 0.f;
+    for (int q = 0; q < NL; ++q) {  // unconditional loads: nothing waits for them here
+      const int e = q * NT + tid, t = min(e / GDN_LMAX, C - 1), l = min(e % GDN_LMAX, pr.ll - 1);
+      lam[q] = lg[(((int64_t)b * pr.seqlen + t0 + t) * pr.nheads + h) * pr.nlevels + l];
     }
     khv = tid < C ? pr.kh[(int64_t)item * C + tid] : 0.f;
     gcv = pr.gc[item];
@@ -426,7 +423,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_kernel(GdnParams pr) {
 #pragma unroll
     for (int q = 0; q < St::NL; ++q) {
       const int e = q * NT + tid;
-      if (e < C * GDN_LMAX) lam_s[e / GDN_LMAX][e % GDN_LMAX] = st.lam[q];
+      if (e < C * GDN_LMAX) lam_s[e / GDN_LMAX][e % GDN_LMAX] = e % GDN_LMAX < pr.ll ? to_f(st.lam[q]) : 0.f;
     }
     if (tid < C) khs[tid] = st.khv;
     const float gC = st.gcv;
@@ -591,14 +588,25 @@ __device__ inline f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c
 
 // Same walk as gdn_scan_kernel.  Every product runs on
 // v_mfma_f32_16x16x32_bf16 with each fp32 operand split into a bf16 hi / lo
-// pair (three products per step, about 16 significant bits per operand
-// instead of fp32's 24, at a twelfth of the fp32 MFMA cost per step).  The
-// operands are staged in the layouts the products read: Qe and W as token
-// rows, Kh transposed (rows of the key dimension, Kh = diag(gamma_C / gamma)
-// K folded in at staging), and the level states, W Z and U transposed (rows
-// of the 16 value columns).  The level states stay fp32 in registers; only
-// their copies for the products are split.  Each wave keeps its Qe or W
-// row fragments and its Kh^T fragments in registers for the whole chunk.
+// pair (about 16 significant bits per operand instead of fp32's 24): three
+// products per step for two split operands, two where K, exact in bf16,
+// meets a split one.  Kh = diag(gamma_C / gamma) K never forms: the state
+// update subtracts K^T (diag(gamma_C / gamma) W Z) and the chunk's own
+// tokens add K^T (diag(gamma_C / gamma) U), the scale applied to the fp32
+// W Z and U before they are split.
+//
+// A chunk's operands (Qe and W rows in fp32, K rows in bf16, this
+// work-group's 16 columns of U and of the intra outputs) are copied into
+// LDS by global_load_lds_dwordx4, one chunk ahead into the other of two
+// buffers, in XOR-swizzled row layouts: no registers hold them in flight
+// and no staging pass rewrites them.  Each wave reads its Qe or W row
+// fragments (fp32, split in registers) and its K^T fragments (transposing
+// reads) once per chunk and keeps them for every level.  The level states,
+// W Z and U are staged transposed (rows of the 16 value columns); the level
+// states stay fp32 in registers and only their copies for the products are
+// split.  Lambda rows, gamma_C / gamma_t and the odd batch slots' output
+// sums are double-buffered by chunk parity too, so a chunk ends without a
+// barrier.
 template <int N, int P>
 __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
   using T = bf16;
@@ -609,18 +617,21 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
   constexpr int NTILE = N / 16;                 // 16-row blocks of a state
   constexpr int NTW = (NTILE + NWV - 1) / NWV;  // of them per wave
   constexpr int NKK = N / 32;                   // contraction steps over the key dimension
-  using LN = GdnRowsN<N>;
-  using LP = Rows<float, PB>;
-  using St = GdnStage<T, N, P, NT, true>;
-  __shared__ __attribute__((aligned(16))) bf16 qh[C * N], ql[C * N];   // Qe
-  __shared__ __attribute__((aligned(16))) bf16 wh[C * N], wl[C * N];   // W
-  __shared__ __attribute__((aligned(16))) bf16 kth[C * N], ktl[C * N];  // Kh (token rows)
-  __shared__ __attribute__((aligned(16))) bf16 uth[PB * C], utl[PB * C];  // U^T
+  constexpr int NL = (C * GDN_LMAX + NT - 1) / NT;
+  using LN = GdnRowsN<N>;     // level states (transposed)
+  using LF = Rows<float, N>;  // Qe and W rows
+  using LK = Rows<bf16, N>;   // K rows
+  using LP = Rows<float, PB>;  // U, the intra outputs and the output sums: 16 columns
+  __shared__ __attribute__((aligned(16))) float qf[2][C * N];    // Qe
+  __shared__ __attribute__((aligned(16))) float wf[2][C * N];    // W
+  __shared__ __attribute__((aligned(16))) bf16 kb[2][C * N];     // K
+  __shared__ __attribute__((aligned(16))) float uf[2][C * PB];   // U
+  __shared__ __attribute__((aligned(16))) float of[2][C * PB];   // intra outputs + even batch slots
+  __shared__ __attribute__((aligned(16))) float os1[2][C * PB];  // odd batch slots
+  __shared__ __attribute__((aligned(16))) float khs[2][C];       // gamma_C / gamma_t
+  __shared__ float lam_s[2][C][GDN_LMAX];
   __shared__ __attribute__((aligned(16))) bf16 zth[GDN_LB * PB * N], ztl[GDN_LB * PB * N];  // Z^T
   __shared__ __attribute__((aligned(16))) bf16 yth[GDN_LB * PB * C], ytl[GDN_LB * PB * C];  // (W Z)^T
-  __shared__ __attribute__((aligned(16))) float os[C * PB];
-  __shared__ __attribute__((aligned(16))) float os1[C * PB];
-  __shared__ float lam_s[C][GDN_LMAX];
 
   const int nblk = P / PB;
   const int pblk = blockIdx.x % nblk, bh = blockIdx.x / nblk;
@@ -630,10 +641,35 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   T* og = static_cast<T*>(pr.out);
+  const T* kg = static_cast<const T*>(pr.k);
+  const T* lg = static_cast<const T*>(pr.lam);
   // products: wave w forms Qe Z (outputs) for w mod 4 < 2, else W Z, for
   // token rows [16 (w mod 2), +16) and batch slots w / 4, w / 4 + 2
   const bool qe_wave = (wave & 2) == 0;
   const int rbw = wave & 1, q0w = wave >> 2;
+
+  // chunk j's copies into buffer j mod 2 (U by waves 6 and 7, the intra
+  // outputs by waves 4 and 5: the first waves copy a Qe and W piece more),
+  // its lambda rows and gamma_C / gamma_t into registers
+  T lam[NL];  // raw: converted (and zeroed past the level count) when staged
+  float khv = 0.f;
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int item = bh * pr.nc + j, buf = j & 1;
+    const int64_t t0 = (int64_t)j * C;
+    rows_to_lds<float, C, N, NWV>(pr.qe + (int64_t)item * C * N, N, qf[buf], wave, lane);
+    rows_to_lds<float, C, N, NWV>(pr.w + (int64_t)item * C * N, N, wf[buf], wave, lane);
+    rows_to_lds<T, C, N, NWV>(kg + (((int64_t)b * T_ + t0) * H + h) * N, (int64_t)H * N, kb[buf], wave, lane);
+    rows_to_lds<float, C, PB, NWV>(pr.u + (int64_t)item * C * P + p0, P, uf[buf], (wave + 2) & (NWV - 1), lane);
+    rows_to_lds<float, C, PB, NWV>(pr.oi + (int64_t)item * C * P + p0, P, of[buf], (wave + 4) & (NWV - 1), lane);
+    // unconditional loads at clamped indices: a load under a branch whose
+    // value is converted there makes the wave wait for every copy in flight
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int e = q * NT + tid, t = min(e / GDN_LMAX, C - 1), l = min(e % GDN_LMAX, pr.ll - 1);
+      lam[q] = lg[(((int64_t)b * T_ + t0 + t) * H + h) * pr.nlevels + l];
+    }
+    khv = pr.kh[(int64_t)item * C + (tid & (C - 1))];
+  };
 
   f32x4 Z[GDN_KMAX][NTW];
 #pragma unroll
@@ -641,61 +677,47 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
 #pragma unroll
     for (int u = 0; u < NTW; ++u) Z[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  St st;
-  st.load(pr, bh * pr.nc, b, h, 0, p0, tid);
+  issue(0);
   for (int j = 0; j < pr.nc; ++j) {
     const int64_t t0 = (int64_t)j * C;
-    // ---- this chunk's operands into LDS, split; then the next chunk's loads
+    const int buf = j & 1;
+    const float gC = pr.gc[bh * pr.nc + j];
+    float* const ofb = of[buf];
+    float* const os1b = os1[buf];
+    const float* const khb = khs[buf];
+    // ---- this chunk's lambda rows and scales into LDS, then the next chunk's copies
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and loads of the chunk have landed
 #pragma unroll
-    for (int q = 0; q < St::NQ; ++q) {
-      if (q * NT + tid >= St::NQ4) break;
-      const int e = (q * NT + tid) * 4, t = e / N, n = e % N;
-      split_store4(qh, ql, LN::at(t, n), st.qe[q]);
-      split_store4(wh, wl, LN::at(t, n), st.w[q]);
-      split_store4(kth, ktl, LN::at(t, n), st.k[q] * st.ks[q]);  // Kh rows
-    }
-#pragma unroll
-    for (int q = 0; q < St::NV; ++q) {
-      const int e = q * NT + tid, t = e / PB, p = e % PB;
-      if (e < C * PB) {
-        bf16 hi, lo;
-        split_bf16(st.u2[q], hi, lo);
-        uth[R32::at(p, t)] = hi;
-        utl[R32::at(p, t)] = lo;
-        os[LP::at(t, p)] = st.o2[q];
-        os1[LP::at(t, p)] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < St::NL; ++q) {
+    for (int q = 0; q < NL; ++q) {
       const int e = q * NT + tid;
-      if (e < C * GDN_LMAX) lam_s[e / GDN_LMAX][e % GDN_LMAX] = st.lam[q];
+      if (e < C * GDN_LMAX) lam_s[buf][e / GDN_LMAX][e % GDN_LMAX] = e % GDN_LMAX < pr.ll ? to_f(lam[q]) : 0.f;
     }
-    const float gC = st.gcv;
-    lds_barrier();
-    if (j + 1 < pr.nc) st.load(pr, bh * pr.nc + j + 1, b, h, t0 + C, p0, tid);
-    // this chunk's operand fragments of the wave
+    if (tid < C) khs[buf][tid] = khv;
+    for (int i = tid; i < C * PB; i += NT) os1b[i] = 0.f;
+    lds_barrier();  // every wave's copies have landed; the other buffer is free
+    if (j + 1 < pr.nc) issue(j + 1);
+    // this chunk's operand fragments of the wave: Qe or W rows, split
     frag ah[NKK], al[NKK];
     {
-      const bf16* ah_s = qe_wave ? qh : wh;
-      const bf16* al_s = qe_wave ? ql : wl;
+      const float* a_s = qe_wave ? qf[buf] : wf[buf];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int o = LN::at(16 * rbw + r, 32 * kk + 8 * g);
-        ah[kk] = *reinterpret_cast<const frag*>(ah_s + o);
-        al[kk] = *reinterpret_cast<const frag*>(al_s + o);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(a_s + LF::at(16 * rbw + r, 32 * kk + 8 * g));
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(a_s + LF::at(16 * rbw + r, 32 * kk + 8 * g + 4));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 hi, lo;
+          split_bf16(e < 4 ? x0[e] : x1[e - 4], hi, lo);
+          ah[kk][e] = hi;
+          al[kk][e] = lo;
+        }
       }
     }
-    frag kh_[NTW], kl_[NTW];  // Kh^T fragments: rows 16 nb + r of Kh^T, tokens 8 g ..
+    frag kt[NTW];  // K^T fragments: rows 16 nb + r of K^T, tokens 8 g ..
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
       const int nb = NTW * wave + u;
-      if (nb < NTILE) {
-        kh_[u] = frag_down_bf16<LN>(kth, 0, 16 * nb, g, r);
-        kl_[u] = frag_down_bf16<LN>(ktl, 0, 16 * nb, g, r);
-      } else {
-        kh_[u] = kl_[u] = frag{};
-      }
+      kt[u] = nb < NTILE ? frag_down_bf16<LK>(kb[buf], 0, 16 * nb, g, r) : frag{};
     }
 
     // ---- chunk levels whose bit is set in j, up to GDN_LB at a time
@@ -724,7 +746,7 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
         }
       lds_barrier();
       {
-        float* od = q0w ? os1 : os;
+        float* od = q0w ? os1b : ofb;
 #pragma unroll
         for (int q = q0w; q < GDN_LB; q += 2) {
           if (q >= nbat) break;
@@ -739,15 +761,16 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int t = 16 * rbw + 4 * g + i;
-              od[LP::at(t, r)] += lam_s[t][c_log + ms[q]] * acc[i];
+              od[LP::at(t, r)] += lam_s[buf][t][c_log + ms[q]] * acc[i];
             }
-          } else {
-            split_store4(yth, ytl, q * PB * C + R32::at(r, 16 * rbw + 4 * g), acc);
+          } else {  // diag(gamma_C / gamma) W Z
+            const f32x4 ks = *reinterpret_cast<const f32x4*>(khb + 16 * rbw + 4 * g);
+            split_store4(yth, ytl, q * PB * C + R32::at(r, 16 * rbw + 4 * g), acc * ks);
           }
         }
       }
       lds_barrier();
-      // Z <- gamma_C Z - Kh^T (W Z)
+      // Z <- gamma_C Z - K^T (diag(gamma_C / gamma) W Z)
 #pragma unroll
       for (int m2 = 1; m2 < GDN_KMAX; ++m2)
         if ((bmask >> m2) & 1u) {
@@ -758,19 +781,28 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
 #pragma unroll
           for (int u = 0; u < NTW; ++u)
             if (NTW * wave + u < NTILE)
-              Z[m2][u] = gC * Z[m2][u] - mma3(kh_[u], kl_[u], yh, yl, f32x4{0.f, 0.f, 0.f, 0.f});
+              Z[m2][u] = gC * Z[m2][u] - M::mma(kt[u], yl, M::mma(kt[u], yh, f32x4{0.f, 0.f, 0.f, 0.f}));
         }
       lds_barrier();  // zt and yt are reused by the next batch
     }
-    // ---- the chunk's own tokens (Kh^T U), then the Fenwick merge for j + 1
+    // ---- the chunk's own tokens, K^T (diag(gamma_C / gamma) U), then the
+    // Fenwick merge for j + 1
     f32x4 own[NTW];
     {
-      const int o = R32::at(r, 8 * g);
-      const frag uh = *reinterpret_cast<const frag*>(uth + o);
-      const frag ul = *reinterpret_cast<const frag*>(utl + o);
+      // U^T fragment: column p0 + r, tokens 8 g .. 8 g + 7
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(khb + 8 * g);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(khb + 8 * g + 4);
+      frag uh, ul;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hi, lo;
+        split_bf16(uf[buf][LP::at(8 * g + e, r)] * (e < 4 ? k0[e] : k1[e - 4]), hi, lo);
+        uh[e] = hi;
+        ul[e] = lo;
+      }
 #pragma unroll
       for (int u = 0; u < NTW; ++u)
-        own[u] = NTW * wave + u < NTILE ? mma3(kh_[u], kl_[u], uh, ul, f32x4{0.f, 0.f, 0.f, 0.f})
+        own[u] = NTW * wave + u < NTILE ? M::mma(kt[u], ul, M::mma(kt[u], uh, f32x4{0.f, 0.f, 0.f, 0.f}))
                                         : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (j + 1 < pr.nc) {
@@ -793,9 +825,12 @@ __global__ __launch_bounds__(GDN_SNT) void gdn_scan_bf16_kernel(GdnParams pr) {
     }
     for (int i = tid; i < C * PB; i += NT) {
       const int t = i / PB, p = i % PB;
-      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(os[LP::at(t, p)] + os1[LP::at(t, p)]);
+      og[(((int64_t)b * T_ + t0 + t) * H + h) * P + p0 + p] = from_f<T>(ofb[LP::at(t, p)] + os1b[LP::at(t, p)]);
     }
-    lds_barrier();  // the next chunk restages every tile
+    // No barrier: the next chunk stages lambda, the scales and the odd
+    // slots' sums in the other parity's buffers, its first batch writes Z^T
+    // only after its first barrier, and the copies into this chunk's
+    // buffers start after that barrier too.
   }
 }
 
