@@ -284,7 +284,10 @@ __global__ __launch_bounds__(BWD_SCAN_NT) void bwd_cuma_kernel(BwdParams pr) {
 
 // Token tiles of one chunk staged through registers: every global load of
 // the four tiles is issued before the first LDS store, so the work-group
-// waits for one memory latency instead of one per load.
+// waits for one memory latency instead of one per load.  The loads are
+// unconditional (a short tile's spare lanes load its last piece again and
+// store nothing): a load under a branch into a register that lives across
+// the branch makes the next one wait for it.
 template <class T, int R, int W, int NT>
 struct RowsStage {
   using L = Rows<T, W>;
@@ -294,8 +297,8 @@ struct RowsStage {
   __device__ inline void load(const T* g, int64_t grs, int tid) {
 #pragma unroll
     for (int q = 0; q < IT; ++q) {
-      const int i = q * NT + tid;
-      if (i < PIECES) v[q] = load16(g + (int64_t)(i / L::NBLK) * grs + (i % L::NBLK) * L::VEC);
+      const int i = PIECES % NT == 0 ? q * NT + tid : min(q * NT + tid, PIECES - 1);
+      v[q] = load16(g + (int64_t)(i / L::NBLK) * grs + (i % L::NBLK) * L::VEC);
     }
   }
   __device__ inline void store(T* lds, int tid) const {
@@ -346,9 +349,15 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
   for (int nb = 0; nb < Tl::NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   RowsStage<T, C, N, NT> sk;
   RowsStage<T, C, P, NT> sv;
-  // issue the loads of chunk j's rows; returns its log a and lambda values
+  // issue the loads of chunk j's rows; returns its log a and lambda value
   // for this thread's token (by value: see the scan pass on loop-carried
-  // values held through references)
+  // values held through references).  Both loads are unconditional and
+  // lambda stays in the io type until it is used: converting it here would
+  // make the wave wait for the rows in flight.
+  struct Next {
+    float la;
+    T lam;
+  };
   auto issue = [&](int j) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)j * C;
     const T* kg = static_cast<const T*>(REV ? pr.Cm : pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N;
@@ -356,19 +365,19 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
     sk.load(kg, (int64_t)G * N, tid);
     sv.load(vg, (int64_t)H * P, tid);
     const int tt = tid < C ? tid : 0;
-    f32x2 v;
-    v[0] = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tt) * H + h] : 0.f;
-    v[1] = REV ? to_f(static_cast<const T*>(pr.lam)[(((int64_t)b * T_ + t0 + tt) * H + h) * L + c_log + k])
-               : 0.f;
+    Next v;
+    v.la = pr.log_a[((int64_t)b * T_ + t0 + tt) * H + h];
+    v.lam = REV ? static_cast<const T*>(pr.lam)[(((int64_t)b * T_ + t0 + tt) * H + h) * L + c_log + k]
+                : from_f<T>(0.f);
     return v;
   };
   const int n = hi - lo;
-  f32x2 nxt = {0.f, 0.f};
+  Next nxt = {0.f, from_f<T>(0.f)};
   if (n > 0) nxt = issue(REV ? hi - 1 : lo);
   for (int step = 0; step < n; ++step) {
     sk.store(ksh, tid);
     sv.store(vsh, tid);
-    const float la = nxt[0], lamv = nxt[1];
+    const float la = tid < C ? nxt.la : 0.f, lamv = to_f(nxt.lam);
     if (step + 1 < n) nxt = issue(REV ? hi - 2 - step : lo + step + 1);
     chunk_decays<T, C>(la, cum, ecum, wst, tid);
     lds_barrier();
@@ -637,6 +646,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   RowsStage<T, C, P, NT> sx, so;
   T lv_[LIT];
   float la = 0.f;
+  double ca_hi = 0.0, ca_lo = 0.0;
   auto load_rows = [&](int tile) {  // token rows of a tile into registers
     const int tid = opaque_tid();
     const int bh = tile / pr.nc, j = tile % pr.nc;
@@ -650,9 +660,17 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
 #pragma unroll
     for (int q = 0; q < LIT; ++q) {
       const int i = q * NT + tid;
-      lv_[q] = i < C * ll ? lg[(int64_t)(i / ll) * H * L + i % ll] : from_f<T>(0.f);
+      const int ic = min(i, C * ll - 1);  // unconditional (see RowsStage)
+      lv_[q] = lg[(int64_t)(ic / ll) * H * L + ic % ll];
     }
-    la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+    la = pr.log_a[((int64_t)b * T_ + t0 + min(tid, C - 1)) * H + h];
+    // level k's gap (lane k - 1): log-decay from the end of the lower half
+    // to chunk j, from the prefix sums at j and at the first chunk of j's
+    // upper half at level k
+    const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
+    const int kl = tid < pr.kc ? tid : 0;
+    ca_hi = ca[j];
+    ca_lo = ca[(j >> kl) << kl];
   };
   if (ct.tile(0) >= 0) load_rows(ct.tile(0));
   for (int m = 0; ct.more(m); ++m) {
@@ -663,13 +681,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   const int b = bh / H, h = bh % H;
   const int64_t t0 = (int64_t)j * C;
   const unsigned act0 = (unsigned)j & ((1u << pr.kc) - 1u);  // active chunk levels (bit k-1)
-  // level k's gap: log-decay from the end of the lower half to chunk j
-  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
-  float gap = 0.f;
-  if (tid < pr.kc && ((act0 >> tid) & 1u)) {
-    const int h0 = (j >> tid) << tid;  // first chunk of j's upper half at level tid + 1
-    gap = (float)(ca[j] - ca[h0]);
-  }
+  const float gap = tid < pr.kc && ((act0 >> tid) & 1u) ? (float)(ca_hi - ca_lo) : 0.f;
 
   sc.store(csh, tid);
   sb.store(bsh, tid);
@@ -684,7 +696,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     }
   }
   if (tid < pr.kc) gap_s[tid + 1] = gap;
-  chunk_decays<T, C>(la, cum, ecum, wst, tid);
+  chunk_decays<T, C>(tid < C ? la : 0.f, cum, ecum, wst, tid);
   lds_barrier();
   // the states of the first two active levels are requested now, each later
   // one two levels ahead of its use; then the next tile's rows
@@ -914,6 +926,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   RowsStage<T, C, P, NT> sx, so;
   T lv_[LIT];
   float la = 0.f;
+  double ca_hi = 0.0, ca_lo = 0.0;
   auto load_rows = [&](int tile) {  // token rows of a tile into registers
     const int tid = opaque_tid();
     const int bh = tile / pr.nc, ich = tile % pr.nc;
@@ -927,9 +940,18 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 #pragma unroll
     for (int q = 0; q < LIT; ++q) {
       const int i = q * NT + tid;
-      lv_[q] = i < C * (c_log + 1) ? lg[(int64_t)(i / (c_log + 1)) * H * L + i % (c_log + 1)] : from_f<T>(0.f);
+      const int ic = min(i, C * (c_log + 1) - 1);  // unconditional (see RowsStage)
+      lv_[q] = lg[(int64_t)(ic / (c_log + 1)) * H * L + ic % (c_log + 1)];
     }
-    la = tid < C ? pr.log_a[((int64_t)b * T_ + t0 + tid) * H + h] : 0.f;
+    la = pr.log_a[((int64_t)b * T_ + t0 + min(tid, C - 1)) * H + h];
+    // level k's gap (lane k - 1): log-decay from the end of chunk i to the
+    // end of its lower half, from the prefix sums at the first chunk of the
+    // upper half at level k (clamped for lanes whose level is inactive) and
+    // after chunk i
+    const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
+    const int kl = tid < pr.kc ? tid : 0;
+    ca_hi = ca[min(((ich >> kl) + 1) << kl, pr.nc)];
+    ca_lo = ca[ich + 1];
   };
   if (ct.tile(0) >= 0) load_rows(ct.tile(0));
   for (int m = 0; ct.more(m); ++m) {
@@ -943,13 +965,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   unsigned act0 = 0;
   for (int k = 1; k <= pr.kc; ++k)
     if (!((i_ch >> (k - 1)) & 1) && ((((i_ch >> (k - 1)) + 1) << (k - 1)) < pr.nc)) act0 |= 1u << (k - 1);
-  // level k's gap: log-decay from the end of chunk i to the end of its lower half
-  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
-  float gap = 0.f;
-  if (tid < pr.kc && ((act0 >> tid) & 1u)) {
-    const int h0 = ((i_ch >> tid) + 1) << tid;  // first chunk of the upper half at level tid + 1
-    gap = (float)(ca[h0] - ca[i_ch + 1]);
-  }
+  const float gap = tid < pr.kc && ((act0 >> tid) & 1u) ? (float)(ca_hi - ca_lo) : 0.f;
 
   sc.store(csh, tid);
   sb.store(bsh, tid);
@@ -961,7 +977,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     if (i < C * (c_log + 1)) lam_s[i / (c_log + 1)][i % (c_log + 1)] = to_f(lv_[q]);
   }
   if (tid < pr.kc) gap_s[tid + 1] = gap;
-  chunk_decays<T, C>(la, cum, ecum, wst, tid);
+  chunk_decays<T, C>(tid < C ? la : 0.f, cum, ecum, wst, tid);
   lds_barrier();
   // the states of the first two active levels are requested now, each later
   // one two levels ahead of its use; then the next tile's rows

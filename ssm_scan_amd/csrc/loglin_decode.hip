@@ -47,42 +47,77 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams dp) {
   float* S = dp.S + (int64_t)bh * LL * N * P;
   const int c0 = 4 * pq;  // first of the work-group's 4 columns
 
-  float x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = to_f(Xv[c0 + i]);
+  // The loads that depend on nothing are issued together, unconditionally
+  // (idle rows read row N - 1) and kept in the io type until all are out: a
+  // load under a branch, or one converted as soon as it is issued, makes
+  // the thread wait for it before the next goes out.
   const int64_t gb = ((int64_t)b * G + grp) * N;
-  const float cn = row ? to_f(static_cast<const T*>(dp.Cm)[gb + n]) : 0.f;
-  const float bn = row ? to_f(static_cast<const T*>(dp.Bm)[gb + n]) : 0.f;
-  const float lam_merge = z >= 0 ? to_f(lam[z + 1]) : 0.f;
+  const int nr = row ? n : N - 1;
+  T xr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr[i] = Xv[c0 + i];
+  const T cr = static_cast<const T*>(dp.Cm)[gb + nr];
+  const T br = static_cast<const T*>(dp.Bm)[gb + nr];
+  const T lr0 = lam[0], lrm = lam[z >= 0 ? z + 1 : 0];
+  constexpr int U = 16;  // levels whose loads are in flight together
+  float gr[U];
+  T lr[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int l = min(i, LL - 1);
+    gr[i] = gold[l];
+    lr[i] = lam[l];
+  }
 
-  // new level 0, the token itself (S_0 = B_t X_t^T), then every occupied
-  // older level; the levels 0..z also merge into level z+1
-  f32x4 acc = (to_f(lam[0]) * bn * cn) * f32x4{x[0], x[1], x[2], x[3]};
+  // every occupied older level (S_l^T, C applied at the end), then the new
+  // level 0, the token itself (S_0 = B_t X_t^T); the levels 0..z also merge
+  // into level z+1
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   f32x4 merged = {0.f, 0.f, 0.f, 0.f};
   if (t > 0 && row) {
-    constexpr int U = 8;  // levels whose loads are in flight together
+    // Before step t the buckets are those of the prefix 0 .. t-1: level 0
+    // and, for l >= 1, level l where bit l-1 of t-1 is set (level z+1 is
+    // empty).  Known from t alone, so the state loads need not wait for the
+    // decay factors; a bucket whose factor has underflowed to 0 adds 0.
+    const unsigned long long occ = ((unsigned long long)(t - 1) << 1) | 1ull;
     for (int l0 = 0; l0 < LL; l0 += U) {  // uniform; empty levels load nothing
       f32x4 sv[U];
-      float gv[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
         const int l = l0 + i;
-        gv[i] = (l < LL && l != z + 1) ? gold[l] : 0.f;
-        sv[i] = gv[i] != 0.f ? *reinterpret_cast<const f32x4*>(S + (((int64_t)l * PQ + pq) * N + n) * 4)
-                             : f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[i] = (l < LL && ((occ >> l) & 1ull))
+                    ? *reinterpret_cast<const f32x4*>(S + (((int64_t)l * PQ + pq) * N + n) * 4)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      float gv[U], lv[U];  // decay factor and lambda of each level
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        gv[i] = l0 == 0 ? gr[i] : gold[min(l0 + i, LL - 1)];
+        // the factors are uniform (scalar loads): taking them here, after
+        // the state loads have gone out, keeps the compiler from loading
+        // and waiting for each one next to its use
+        asm volatile("" : "+v"(gv[i]));
+        lv[i] = l0 == 0 ? to_f(lr[i]) : to_f(lam[min(l0 + i, LL - 1)]);
+      }
+      const float lam_merge = z >= 0 ? to_f(lrm) : 0.f;
 #pragma unroll
       for (int i = 0; i < U; ++i) {
         const int l = l0 + i;
-        if (gv[i] != 0.f) {
+        if (l < LL && ((occ >> l) & 1ull)) {
           const bool merge = l <= z;
-          const float w = (merge ? lam_merge : to_f(lam[l])) * a * gv[i];
-          acc += (w * cn) * sv[i];
+          const float w = (merge ? lam_merge : lv[i]) * a * gv[i];
+          acc += w * sv[i];
           if (merge) merged += gv[i] * sv[i];
         }
       }
     }
   }
+  const float cn = row ? to_f(cr) : 0.f;
+  const float bn = row ? to_f(br) : 0.f;
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = to_f(xr[i]);
+  acc = cn * (acc + (to_f(lr0) * bn) * f32x4{x[0], x[1], x[2], x[3]});
   if (row) {  // the merged level and level 0, stored without decay factor
     if (z >= 0) *reinterpret_cast<f32x4*>(S + (((int64_t)(z + 1) * PQ + pq) * N + n) * 4) = merged;
     *reinterpret_cast<f32x4*>(S + ((int64_t)pq * N + n) * 4) =
