@@ -560,12 +560,15 @@ void state_kernel(Params pr) {
     }
     for (int i = tid; i < HS * (KC - C); i += NT) wst[(i / (KC - C)) * KC + C + i % (KC - C)] = 0.f;
   }
-  // heads of one group next to each other: they read the same B rows
+  // heads of one group next to each other (they read the same B rows), then
+  // groups, then segments: the work-groups running together on an XCD (a
+  // contiguous range of tiles) cover every head of a few segments and share
+  // each token's log-decay line (32 heads' log-decays per 128 bytes)
   const int hpg = H / G, npair = hpg / HS;
   const int pi = tile % npair;
-  const int q = (tile / npair) % pr.ns;
-  const int grp = (tile / (npair * pr.ns)) % G;
-  const int b = tile / (npair * pr.ns * G);
+  const int grp = (tile / npair) % G;
+  const int q = (tile / (npair * G)) % pr.ns;
+  const int b = tile / (npair * G * pr.ns);
   const int h0 = grp * hpg + pi * HS;
   const int h = h0 + hh;
   const int bh = b * H + h;

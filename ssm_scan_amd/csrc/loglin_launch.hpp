@@ -69,12 +69,13 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   constexpr bool PAIRS = sizeof(T) == 2 && P == 64;
   if (use2) {
     constexpr int NN = OUT2 ? N : 128;
-    pr.total = pr.batch * pr.ns * pr.nheads;
+    // batch x groups of 8 segments x 8 XCDs x heads (see output2_kernel)
+    const int grid = pr.batch * ((pr.ns + 7) / 8) * 8 * pr.nheads;
     const size_t shm = (size_t)C * lam_words(pr.ll, 2) * 4;
     if (pr.lmask == ~0ull)
-      hipLaunchKernelGGL((output2_kernel<NN, false>), dim3(pad8(pr.total)), dim3(256), shm, st, pr);
+      hipLaunchKernelGGL((output2_kernel<NN, false>), dim3(grid), dim3(256), shm, st, pr);
     else
-      hipLaunchKernelGGL((output2_kernel<NN, true>), dim3(pad8(pr.total)), dim3(256), shm, st, pr);
+      hipLaunchKernelGGL((output2_kernel<NN, true>), dim3(grid), dim3(256), shm, st, pr);
   } else if (PAIRS && pr.hp == 2)
     launch_output<T, C, P, N, PAIRS ? 2 : 1>(pr, st);
   else

@@ -123,21 +123,32 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
   __shared__ float gap_s[GS];
   extern __shared__ unsigned lam_w[];  // [C][LW] level weights, 32-bit words
 
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  if (tile >= pr.total) return;
+  // Work-group -> (segment, head).  The hardware deals work-groups to the 8
+  // XCDs round-robin by id.  XCD x takes its u-th group of 8 segments
+  // (counted from the last) at offset (u + x) mod 8, so over u every XCD
+  // meets every offset and every group: the same mix of segment indices,
+  // whose set bits decide a segment's level count, the longest first.  It
+  // runs all heads of a segment in turn, heads of one group next to each
+  // other (they read the same B and C rows), so the work-groups running
+  // together on an XCD cover every head of one or two segments and share
+  // each token's log-decay and level-weight lines (a 128-byte line holds
+  // 32 heads' log-decays).
+  const int H = pr.nheads;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int ng8 = (pr.ns + 7) >> 3;  // groups of 8 segments per batch entry
+  const int slot = kx / H;
+  const int b = slot / ng8, u = slot % ng8;
+  const int qd = 8 * u + ((u + xcd) & 7);  // segment, counted from the last
+  if (b >= pr.batch || qd >= pr.ns) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels, LL = pr.ll;
+  const int G = pr.ngroups, L = pr.nlevels, LL = pr.ll;
   const int LW = lam_words(LL, 2);
-  // heads of a group next to each other (they read the same B and C rows),
-  // then segments, then groups: see output_kernel
   const int hpg = H / G;
-  const int pi = tile % hpg;
-  const int q = pr.ns - 1 - (tile / hpg) % pr.ns;
-  const int grp = (tile / (hpg * pr.ns)) % G;
-  const int b = tile / (hpg * pr.ns * G);
-  const int h = grp * hpg + pi;
+  const int h = kx % H;
+  const int grp = h / hpg;
+  const int q = pr.ns - 1 - qd;
   const int bh = b * H + h;
   const int c_log = 6;
   const int m = pr.m;
