@@ -78,7 +78,7 @@ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 // Pairs at chunk level k whose upper half holds at least one chunk.
 __host__ __device__ inline int bwd_pairs(int nc, int k) {
   const int half = 1 << (k - 1);
-  return nc > half ? (nc - half + 2 * half - 1) / (2 * half) : 0;
+  return nc > half ? (nc + half - 1) >> k : 0;  // ceil((nc - half) / 2^k), a shift: no division
 }
 // Pieces per half at chunk level k.
 __host__ __device__ inline int bwd_pieces(int k) {
@@ -309,6 +309,45 @@ struct RowsStage {
     }
   }
 };
+
+// A tile of R token rows staged in LDS in the Rows layout, written to global
+// rows (row stride grs elements) 16 bytes a lane: one store instruction per
+// lane and 16-byte piece instead of one per element.
+template <class T, int R, int W, int NT>
+__device__ inline void rows_from_lds(const T* lds, T* g, int64_t grs, int tid) {
+  using L = Rows<T, W>;
+  constexpr int PIECES = R * L::NBLK;
+#pragma unroll
+  for (int q = 0; q < (PIECES + NT - 1) / NT; ++q) {
+    const int i = q * NT + tid;
+    if (PIECES % NT == 0 || i < PIECES) {
+      const int row = i / L::NBLK, blk = i % L::NBLK;
+      store16(g + (int64_t)row * grs + blk * L::VEC, load16(lds + L::at(row, blk * L::VEC)));
+    }
+  }
+}
+
+// Level weights' gradients of C token rows (L per row, row stride H L), the
+// first ll of each row from LDS and zeros past them; 16 bytes a lane when
+// the rows are whole 16-byte pieces.
+template <class T, int C, int LMAX, int NT>
+__device__ inline void dlam_rows_out(const float (*dl)[LMAX], T* g, int H, int L, int ll, int tid) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  if (L % VEC == 0) {  // uniform
+    for (int i = tid; i < C * (L / VEC); i += NT) {
+      const int t = i / (L / VEC), l0 = (i % (L / VEC)) * VEC;
+      vec16_t<T> v;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = from_f<T>(l0 + e < ll ? dl[t][l0 + e] : 0.f);
+      store16(g + (int64_t)t * H * L + l0, v);
+    }
+  } else {
+    for (int i = tid; i < C * L; i += NT) {
+      const int t = i / L, l = i % L;
+      g[(int64_t)t * H * L + l] = from_f<T>(l < ll ? dl[t][l] : 0.f);
+    }
+  }
+}
 
 // ------------------------------------------------------------ launch 2
 
@@ -861,7 +900,9 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   }
   if (pk) finish_level(pk, buf ^ 1);
 
-  T* dcg = static_cast<T*>(pr.dch) + (((int64_t)b * T_ + t0) * H + h) * N;
+  // the dC tile through LDS (csh: every wave is done with the C rows), then
+  // out by rows
+  lds_barrier();
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
@@ -869,15 +910,13 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
       if (NB % NCG == 0 || cg + NCG * q < NB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dcg[(int64_t)(16 * (RPW * rg + rr) + 4 * g + i) * H * N + 16 * (cg + NCG * q) + r] =
-              from_f<T>(dc[rr][q][i]);
+          csh[LN::at(16 * (RPW * rg + rr) + 4 * g + i, 16 * (cg + NCG * q) + r)] = from_f<T>(dc[rr][q][i]);
       }
-  lds_barrier();  // dlam_s is complete
-  T* dlg = static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L;
-  for (int i = tid; i < C * L; i += NT) {
-    const int t = i / L, l = i % L;
-    dlg[(int64_t)t * H * L + l] = from_f<T>(l < pr.ll ? dlam_s[t][l] : 0.f);
-  }
+  lds_barrier();  // dlam_s and the dC tile are complete
+  rows_from_lds<T, C, N, NT>(csh, static_cast<T*>(pr.dch) + (((int64_t)b * T_ + t0) * H + h) * N,
+                             (int64_t)H * N, tid);
+  dlam_rows_out<T, C, BWD_LMAX, NT>(dlam_s, static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L, H,
+                                    L, pr.ll, tid);
   if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid];
   lds_barrier();  // the next tile restages every LDS array
   }
@@ -1136,8 +1175,9 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     k = kn;
     buf ^= 1;
   }
-  T* dxg = static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P;
-  T* dbg = static_cast<T*>(pr.dbh) + (((int64_t)b * T_ + t0) * H + h) * N;
+  // the dX and dB tiles through LDS (osh and csh: every wave is done with the
+  // dO and C rows), then out by rows
+  lds_barrier();
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     const int sw = 16 * (RPW * rg + rr);
@@ -1151,20 +1191,23 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
         const int pb = cg + NCG * q;
         if (PB % NCG == 0 || pb < PB) {
           pt += dxe[rr][q][i] * to_f(xsh[LP::at(s, 16 * pb + r)]);
-          dxg[(int64_t)s * H * P + 16 * pb + r] = from_f<T>(dx[rr][q][i] + dxe[rr][q][i]);
+          osh[LP::at(s, 16 * pb + r)] = from_f<T>(dx[rr][q][i] + dxe[rr][q][i]);
         }
       }
       part[i] = pt;
 #pragma unroll
       for (int q = 0; q < NBW; ++q)
-        if (NB % NCG == 0 || cg + NCG * q < NB)
-          dbg[(int64_t)s * H * N + 16 * (cg + NCG * q) + r] = from_f<T>(db[rr][q][i]);
+        if (NB % NCG == 0 || cg + NCG * q < NB) csh[LN::at(s, 16 * (cg + NCG * q) + r)] = from_f<T>(db[rr][q][i]);
     }
     // lanes r < 4 of lane group g hold the row sums of s = sw + 4 g + [0, 2, 1, 3][r]
     const float rs = sum16x4(part, r);
     if (r < 4) xpart[cg][sw + 4 * g + (((r & 1) << 1) | (r >> 1))] = rs;
   }
-  lds_barrier();  // colpart and xpart are complete (also when no level ran)
+  lds_barrier();  // colpart, xpart and the dX and dB tiles are complete
+  rows_from_lds<T, C, P, NT>(osh, static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P,
+                             tid);
+  rows_from_lds<T, C, N, NT>(csh, static_cast<T*>(pr.dbh) + (((int64_t)b * T_ + t0) * H + h) * N,
+                             (int64_t)H * N, tid);
   if (tid < C) {
     float cs = 0.f;
 #pragma unroll
