@@ -32,7 +32,7 @@
 //   5. bwd_dkv_kernel           per chunk: dX and dB (this head), from the
 //                               intra block and the upper-half states;
 //   6. bwd_group_sum_kernel     dB, dC = sums over each group's heads;
-//   7. bwd_dloga_kernel         suffix sums of dO.O - X.dX.
+//   7. bwd_dloga_part_kernel, bwd_dloga_kernel   suffix sums of dO.O - X.dX.
 #pragma once
 
 #include "loglin_device.hpp"
@@ -1252,32 +1252,82 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams pr) {
 
 // ------------------------------------------------------------ launch 7
 
-// grid (batch*nheads), 1024 threads: dlog_a[t] = sum_{t' >= t} (term1 - term2),
-// each thread a contiguous run of tokens, runs combined by a suffix scan.
+// dlog_a[t] = sum_{t' >= t} (term1 - term2), in fp64, over segments of
+// whole 1024-token blocks (at most DLOGA_SEGS per (batch, head)): first each
+// segment's total, then per segment the sum of the later segments' totals
+// and a suffix scan of the segment, block by block from its end.  Token
+// reads are coalesced; the totals reuse the chunk passes' prefix-sum region
+// (nc + 1 doubles per head, at least the segment count: free by now).
+constexpr int DLOGA_SEGS = 64;
+__host__ __device__ inline int dloga_nseg(int64_t T) {
+  const int64_t n = (T + 4095) / 4096;
+  return (int)(n < DLOGA_SEGS ? n : DLOGA_SEGS);
+}
+__device__ inline int64_t dloga_segt(int64_t T, int nseg) {
+  return ((T + nseg - 1) / nseg + BWD_SCAN_NT - 1) / BWD_SCAN_NT * BWD_SCAN_NT;
+}
+
+// grid (nseg, batch*nheads), 256 threads: segment totals.
 template <class T>  // (a template so that every unit's copy is a weak symbol)
-__global__ __launch_bounds__(BWD_SCAN_NT) void bwd_dloga_kernel(BwdParams pr) {
-  __shared__ float sh[BWD_SCAN_NT];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int H = pr.nheads, b = bh / H, h = bh % H;
+__global__ __launch_bounds__(256) void bwd_dloga_part_kernel(BwdParams pr) {
+  __shared__ double wsum[4];
+  const int s = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int64_t T_ = pr.seqlen;
-  const int64_t per = (T_ + BWD_SCAN_NT - 1) / BWD_SCAN_NT;
-  const int64_t lo = min((int64_t)tid * per, T_), hi = min(lo + per, T_);
+  const int nseg = gridDim.x;
+  const int64_t segt = dloga_segt(T_, nseg);
+  const int64_t lo = (int64_t)s * segt, hi = min(lo + segt, T_);
   const float* t1 = pr.term1 + (int64_t)bh * T_;
   const float* t2 = pr.term2 + (int64_t)bh * T_;
-  float tot = 0.f;
-  for (int64_t t = hi - 1; t >= lo; --t) tot += t1[t] - t2[t];
-  sh[tid] = tot;
+  double acc = 0.0;
+  for (int64_t t = lo + tid; t < hi; t += 256) acc += (double)t1[t] - (double)t2[t];
+  for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+  if ((tid & 63) == 0) wsum[tid >> 6] = acc;
   __syncthreads();
-  for (int d = 1; d < BWD_SCAN_NT; d <<= 1) {  // inclusive suffix sums over threads
-    const float v = tid + d < BWD_SCAN_NT ? sh[tid + d] : 0.f;
+  if (tid == 0) pr.cuma[(int64_t)bh * nseg + s] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// grid (nseg, batch*nheads), 1024 threads: one segment's suffix sums.
+template <class T>
+__global__ __launch_bounds__(BWD_SCAN_NT) void bwd_dloga_kernel(BwdParams pr) {
+  constexpr int NT = BWD_SCAN_NT, NWV = NT / 64;
+  __shared__ double wsum[2][NWV];  // wave totals of a block, by block parity
+  const int s = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int H = pr.nheads, b = bh / H, h = bh % H;
+  const int64_t T_ = pr.seqlen;
+  const int nseg = gridDim.x;
+  const int64_t segt = dloga_segt(T_, nseg);
+  const int64_t lo = (int64_t)s * segt, hi = min(lo + segt, T_);
+  const float* t1 = pr.term1 + (int64_t)bh * T_;
+  const float* t2 = pr.term2 + (int64_t)bh * T_;
+  double carry = 0.0;  // the later segments, then the later blocks
+  for (int s2 = nseg - 1; s2 > s; --s2) carry += pr.cuma[(int64_t)bh * nseg + s2];
+  const int64_t nblk = hi > lo ? (hi - lo + NT - 1) / NT : 0;
+  float a1 = 0.f, a2 = 0.f;  // this thread's token of the next block (clamped: no branch)
+  auto ld = [&](int64_t blk) __attribute__((always_inline)) {
+    const int64_t t = min(lo + blk * NT + tid, hi - 1);
+    a1 = t1[t];
+    a2 = t2[t];
+  };
+  if (nblk > 0) ld(nblk - 1);
+  for (int64_t blk = nblk - 1, it = 0; blk >= 0; --blk, ++it) {
+    const int64_t t = lo + blk * NT + tid;
+    double v = t < hi ? (double)a1 - (double)a2 : 0.0;
+    if (blk > 0) ld(blk - 1);
+    for (int d = 1; d < 64; d <<= 1) {  // inclusive suffix sums within the wave
+      const double o = __shfl_down(v, d, 64);
+      if (lane + d < 64) v += o;
+    }
+    if (lane == 0) wsum[it & 1][w] = v;
     __syncthreads();
-    sh[tid] += v;
-    __syncthreads();
-  }
-  float run = tid + 1 < BWD_SCAN_NT ? sh[tid + 1] : 0.f;
-  for (int64_t t = hi - 1; t >= lo; --t) {
-    run += t1[t] - t2[t];
-    pr.dloga[((int64_t)b * T_ + t) * H + h] = run;
+    double after = carry, total = carry;
+#pragma unroll
+    for (int w2 = 0; w2 < NWV; ++w2) {
+      const double x = wsum[it & 1][w2];
+      total += x;
+      if (w2 > w) after += x;
+    }
+    if (t < hi) pr.dloga[((int64_t)b * T_ + t) * H + h] = (float)(v + after);
+    carry = total;
   }
 }
 
@@ -1331,7 +1381,9 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
   const int64_t groups4 = (int64_t)pr.batch * pr.seqlen * pr.ngroups * (N / 4);
   hipLaunchKernelGGL((bwd_group_sum_kernel<T, N>), dim3((unsigned)((groups4 + 255) / 256)),
                      dim3(256), 0, st, pr);
-  hipLaunchKernelGGL((bwd_dloga_kernel<T>), dim3(bh), dim3(BWD_SCAN_NT), 0, st, pr);
+  const int nseg = dloga_nseg(pr.seqlen);
+  hipLaunchKernelGGL((bwd_dloga_part_kernel<T>), dim3(nseg, bh), dim3(256), 0, st, pr);
+  hipLaunchKernelGGL((bwd_dloga_kernel<T>), dim3(nseg, bh), dim3(BWD_SCAN_NT), 0, st, pr);
   return (int)hipGetLastError();
 }
 
