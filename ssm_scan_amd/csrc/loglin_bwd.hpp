@@ -437,6 +437,134 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
     for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wave + r] = S[nb][i];
 }
 
+// Forward-direction level states (key B, value X) without re-reading the
+// token rows per level.  The lower half of chunk level k at pair p is the
+// aligned block of 2^(k-1) chunks starting at chunk p 2^k, summed decayed to
+// its end; such blocks nest, so one walk over the chunks builds all of them:
+// after chunk c the aligned blocks of 2^e chunks ending at c are complete
+// for e up to the trailing ones of c (the Fenwick rule), a completed block
+// whose bit e is 0 is the lower half of level e + 1 (stored when its upper
+// half exists) and waits for its right sibling, and the sibling folds it in
+// decayed by its own total log-decay.
+//
+// grid (ceil(nc / 8), batch*nheads): the blocks inside one aligned group of
+// 8 chunks (levels 1 to 4), from the group's chunk states; the totals of
+// the full groups go to part_f (free in this direction) for
+// bwd_zst_up_kernel when there are levels above 4.
+template <class T, int C, int P, int N>
+__global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(BwdParams pr) {
+  using Tl = Tiles<T, C, P, N>;
+  constexpr int NT = Tl::NT, NB = Tl::NB;
+  static_assert(Tl::KC == C, "token tiles are not padded here");
+  __shared__ __attribute__((aligned(16))) T ksh[C * N];
+  __shared__ __attribute__((aligned(16))) T vsh[C * P];
+  __shared__ __attribute__((aligned(16))) float cum[64], ecum[64], wst[64];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.y, H = pr.nheads, G = pr.ngroups;
+  const int b = bh / H, h = bh % H, grp = h / (H / G);
+  const int64_t T_ = pr.seqlen;
+  const int g8 = blockIdx.x, c0 = 8 * g8, c1 = min(c0 + 8, pr.nc);
+  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
+  float* zst = pr.zst + (int64_t)bh * pr.nstate * (N * P);
+  auto put = [&](float* dst, const f32x4* S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wave + r] = S[nb][i];
+  };
+  RowsStage<T, C, N, NT> sk;
+  RowsStage<T, C, P, NT> sv;
+  float la_n = 0.f;  // next chunk's log a for this thread's token
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int64_t t0 = (int64_t)j * C;
+    sk.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
+    sv.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
+    la_n = pr.log_a[((int64_t)b * T_ + t0 + (tid < C ? tid : 0)) * H + h];
+  };
+  f32x4 stk[3][NB];  // left blocks of 1, 2 and 4 chunks waiting for their siblings
+  issue(c0);
+  for (int c = c0; c < c1; ++c) {
+    sk.store(ksh, tid);
+    sv.store(vsh, tid);
+    const float la = tid < C ? la_n : 0.f;
+    if (c + 1 < c1) issue(c + 1);
+    chunk_decays<T, C>(la, cum, ecum, wst, tid);
+    lds_barrier();
+    f32x4 cur[NB];  // this chunk's state, decayed to its end
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) cur[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    chunk_state_mma_split<T, C, P, N>(ksh, vsh, wst, cur, wave, g, r);
+    lds_barrier();  // the next chunk restages the tiles
+    const int i = c - c0;
+    bool open = true;  // uniform
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!open) continue;
+      if (e == 3) {  // the whole group (i = 7): lower half of level 4 when even
+        if (pr.kc >= 5) put(pr.part_f + ((int64_t)bh * ((pr.nc + 7) >> 3) + g8) * (N * P), cur);
+        if (!(g8 & 1) && (g8 >> 1) < bwd_pairs(pr.nc, 4))
+          put(zst + (int64_t)bwd_state_index(pr.nc, 4, g8 >> 1) * (N * P), cur);
+        open = false;
+      } else if (!((i >> e) & 1)) {  // a left block: lower half of level e + 1
+        const int k = e + 1, pair = c >> k;
+        if (pair < bwd_pairs(pr.nc, k)) put(zst + (int64_t)bwd_state_index(pr.nc, k, pair) * (N * P), cur);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) stk[e][nb] = cur[nb];
+        open = false;
+      } else {  // a right block: its left sibling, decayed across it, folds in
+        const float dec = __expf((float)(ca[c + 1] - ca[c + 1 - (1 << e)]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) cur[nb] = dec * stk[e][nb] + cur[nb];
+      }
+    }
+  }
+}
+
+// grid (N P / 1024, batch*nheads), 256 threads: the lower halves of chunk
+// levels 5 and up, by the same walk over the full groups' totals (a block
+// of 2^z groups completed at group q is the lower half of level z + 4).
+// Each thread owns four consecutive state elements of every block; the
+// totals of 16 groups are loaded at a time.
+constexpr int BWD_UP_DEPTH = 24;  // group levels: chunk levels up to 27
+template <int P, int N>
+__global__ __launch_bounds__(256) void bwd_zst_up_kernel(BwdParams pr) {
+  constexpr int D = BWD_UP_DEPTH, U = 16;
+  const int bh = blockIdx.y;
+  const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e4 >= N * P) return;
+  const int ng = pr.nc >> 3;  // full groups
+  const float* gt = pr.part_f + (int64_t)bh * ((pr.nc + 7) >> 3) * (N * P) + e4;
+  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
+  float* zst = pr.zst + (int64_t)bh * pr.nstate * (N * P) + e4;
+  f32x4 stk[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) stk[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < ng; q0 += U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const f32x4*>(gt + (int64_t)min(q0 + u, ng - 1) * (N * P));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u;
+      if (q >= ng) break;  // uniform
+      const int z = __builtin_ctz(~(unsigned)q);  // trailing ones of q
+      f32x4 cur = v[u];
+      // Unrolled into uniform branches, one per entry, so that every stack
+      // index is a constant and the stack stays in registers.
+#pragma unroll
+      for (int e = 0; e < D; ++e)
+        if (e < z) cur = __expf((float)(ca[8 * (q + 1)] - ca[8 * (q + 1 - (1 << e))])) * stk[e] + cur;
+      const int k = z + 4, pair = (8 * (q + 1 - (1 << z))) >> k;
+      if (z >= 1 && k <= pr.kc && pair < bwd_pairs(pr.nc, k))
+        *reinterpret_cast<f32x4*>(zst + (int64_t)bwd_state_index(pr.nc, k, pair) * (N * P)) = cur;
+#pragma unroll
+      for (int e = 0; e < D; ++e)
+        if (e == z) stk[e] = cur;
+    }
+  }
+}
+
 // ------------------------------------------------------------ launch 3
 
 // grid (nstate, batch*nheads), 256 threads.  Combines the pieces of one
@@ -1362,16 +1490,17 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
   hipLaunchKernelGGL((bwd_atot_kernel<T, C>), dim3(pr.nc, bh), dim3(64), 0, st, pr);
   hipLaunchKernelGGL((bwd_cuma_kernel<T>), dim3(bh), dim3(BWD_SCAN_NT), 0, st, pr);
   if (pr.npart > 0) {
-    hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, false>), dim3(pr.npart, bh),
-                       dim3(Tl::NT), 0, st, pr);
+    // forward direction: blocks of the chunk states, levels 1-4 per group of
+    // 8 chunks, then the levels above from the groups' totals
+    hipLaunchKernelGGL((bwd_zst_group_kernel<T, C, P, N>), dim3((pr.nc + 7) / 8, bh), dim3(Tl::NT), 0, st, pr);
+    if (pr.kc >= 5)
+      hipLaunchKernelGGL((bwd_zst_up_kernel<P, N>), dim3((N * P + 1023) / 1024, bh), dim3(256), 0, st, pr);
+    // reverse direction: per (level, pair, piece), the pieces then reduced
     hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh),
                        dim3(Tl::NT), 0, st, pr);
-    if (pr.nstate > pr.nstate_direct) {
-      hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, false>),
-                         dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
+    if (pr.nstate > pr.nstate_direct)
       hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>),
                          dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
-    }
   }
   const int tiles = pr.nc * bh;
   hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(bwd_chunk_grid(bwd_dq_kernel<T, C, P, N>, C, tiles)),

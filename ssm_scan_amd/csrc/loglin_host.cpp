@@ -163,6 +163,9 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   int rc = check_dims(d, chunk, nullptr, &fp);
   if (rc) return rc;
   if (fp.ll > loglin::BWD_LMAX) return LOGLIN_ERR_DIM;
+  // chunk levels above 4 are walked over groups of 8 chunks with a stack of
+  // BWD_UP_DEPTH block sums
+  if (fp.kc > loglin::BWD_UP_DEPTH + 2) return LOGLIN_ERR_DIM;
   if (!pick_bwd(d->io_dtype, chunk, (int)d->headdim, (int)d->dstate)) return LOGLIN_ERR_SHAPE;
   pl->nc = fp.nc;
   pl->kc = fp.kc;
