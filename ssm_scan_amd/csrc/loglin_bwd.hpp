@@ -23,10 +23,17 @@
 // tokens, which is why those states are per level).  Launches:
 //   1. bwd_atot_kernel          per-chunk total log-decay, bwd_cuma_kernel
 //                               their fp64 prefix sums;
-//   2. bwd_level_state_kernel   per (level, pair, piece of <= 8 chunks): the
+//   2. forward direction: bwd_zst_group_kernel, per aligned group of 8
+//                               chunks, the lower halves of levels 1-4 as
+//                               nested blocks of the chunk states, and
+//                               bwd_zst_up_kernel the levels above from the
+//                               groups' totals;
+//                               reverse direction: bwd_level_state_kernel,
+//                               per (level, pair, piece of <= 8 chunks), the
 //                               decayed sum over the piece's chunks of the
-//                               lower half (forward) or upper half (reverse);
-//   3. bwd_level_reduce_kernel  pieces -> one state per (level, pair), fp32;
+//                               upper half;
+//   3. bwd_level_reduce_kernel  reverse pieces -> one state per (level,
+//                               pair), fp32;
 //   4. bwd_dq_kernel            per chunk: dC (this head) and dlambda, from the
 //                               intra block and the lower-half states;
 //   5. bwd_dkv_kernel           per chunk: dX and dB (this head), from the
