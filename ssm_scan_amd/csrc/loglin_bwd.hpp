@@ -60,7 +60,7 @@ struct BwdParams {
   void* dlam;
   float* atot;    // [batch*nheads, nc]
   double* cuma;   // [batch*nheads, nc + 1] exclusive prefix sums of atot
-  float* part_f;  // [batch*nheads, npart, N, P] fp32, lower-half pieces
+  float* part_f;  // [batch*nheads, ceil(nc / 8), N, P] fp32, totals of the groups of 8 chunks
   float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
   float* zst;     // [batch*nheads, nstate, N, P] fp32, lower-half sums
   float* rst;     // [batch*nheads, nstate, N, P] fp32, upper-half sums
@@ -374,6 +374,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
   using M = Mfma<T>;
   constexpr int NT = Tl::NT;
   static_assert(Tl::KC == C, "token tiles are not padded here");
+  static_assert(REV, "forward-direction states come from bwd_zst_group_kernel (part_f holds group totals)");
   __shared__ __attribute__((aligned(16))) T ksh[C * N];
   __shared__ __attribute__((aligned(16))) T vsh[C * P];
   __shared__ __attribute__((aligned(16))) float cum[64], ecum[64], wst[64], wsh[64];
@@ -456,8 +457,8 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
 //
 // grid (ceil(nc / 8), batch*nheads): the blocks inside one aligned group of
 // 8 chunks (levels 1 to 4), from the group's chunk states; the totals of
-// the full groups go to part_f (free in this direction) for
-// bwd_zst_up_kernel when there are levels above 4.
+// the full groups go to part_f for bwd_zst_up_kernel when there are levels
+// above 4.
 template <class T, int C, int P, int N>
 __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(BwdParams pr) {
   using Tl = Tiles<T, C, P, N>;
@@ -580,6 +581,7 @@ __global__ __launch_bounds__(256) void bwd_zst_up_kernel(BwdParams pr) {
 // piece's start (pieces in order).  Writes the fp32 state, row-major [N][P].
 template <class T, int P, int N, bool REV>
 __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
+  static_assert(REV, "forward-direction states come from the block walk, not from pieces");
   constexpr int Q4 = N * P / 4;              // float4 groups of a state
   constexpr int EPT = (Q4 + 255) / 256;      // per thread
   const int bh = blockIdx.y, tid = threadIdx.x;

@@ -187,8 +187,8 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   off = round_up(off + bh * fp.nc * sizeof(float));
   pl->off_cuma = off;
   off = round_up(off + bh * (fp.nc + 1) * sizeof(double));
-  pl->off_pf = off;
-  off = round_up(off + bh * npart * pn * sizeof(float));
+  pl->off_pf = off;  // totals of the groups of 8 chunks (levels above 4)
+  off = round_up(off + bh * (fp.kc >= 5 ? (size_t)(fp.nc + 7) / 8 : 0) * pn * sizeof(float));
   pl->off_pr = off;
   off = round_up(off + bh * npart * pn * sizeof(float));
   pl->off_z = off;
