@@ -388,6 +388,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
   const int half = 1 << (k - 1);
   const int base = pair * 2 * half + (REV ? half : 0);  // first chunk of the half
   const int lo = base + pc * BWD_PIECE;
+  if (lo >= pr.nc) return;  // uniform: a piece past the sequence (the reduce skips it)
   const int hi = min(min(lo + BWD_PIECE, base + half), pr.nc);
   constexpr int c_log = ilog2c(C);
 
@@ -601,6 +602,7 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
   for (int s = 0; s < np; ++s) {
     const int pcs = REV ? s : np - 1 - s;
     const int clo = base + pcs * BWD_PIECE;
+    if (clo >= pr.nc) break;  // uniform: pieces past the sequence hold nothing and are not written
     const int chi = min(min(clo + BWD_PIECE, base + half), pr.nc);
     const float w = Mfma<T>::ex(run);
 #pragma unroll
@@ -1505,8 +1507,7 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
     if (pr.kc >= 5)
       hipLaunchKernelGGL((bwd_zst_up_kernel<P, N>), dim3((N * P + 1023) / 1024, bh), dim3(256), 0, st, pr);
     // reverse direction: per (level, pair, piece), the pieces then reduced
-    hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh),
-                       dim3(Tl::NT), 0, st, pr);
+    hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh), dim3(Tl::NT), 0, st, pr);
     if (pr.nstate > pr.nstate_direct)
       hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>),
                          dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
