@@ -82,6 +82,15 @@ constexpr int BWD_LMAX = 32;
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Pairs at chunk level k whose upper half holds at least one chunk.
 __host__ __device__ inline int bwd_pairs(int nc, int k) {
   const int half = 1 << (k - 1);
@@ -896,20 +905,24 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
 
   // intra-chunk levels: the level-l bucket of t (l >= 1) is the 2^(l-1) keys
   // below t's aligned 2^l block boundary, present when bit l-1 of t is set;
-  // wave w sums the levels l = w mod NW
-  if (lane < C) {
-    const int t = lane;
-    for (int l = wave; l <= c_log; l += NW) {
+  // wave w sums the levels l = w mod NW.  Each level's loop has its length
+  // fixed at compile time, so its LDS reads go out together (a loop of
+  // runtime length waits for one read per key: 32 for the top level)
+  static_for<0, c_log + 1>([&](auto lc) __attribute__((always_inline)) {
+    constexpr int l = decltype(lc)::value;
+    if (l % NW == wave && lane < C) {
+      const int t = lane;
       float v = 0.f;
-      if (l == 0) {
+      if constexpr (l == 0) {
         v = esd[t][t];
       } else if ((t >> (l - 1)) & 1) {
         const int lo = t & ~((1 << l) - 1);
-        for (int s = lo; s < lo + (1 << (l - 1)); ++s) v += esd[t][s];
+#pragma unroll
+        for (int s = 0; s < (1 << (l - 1)); ++s) v += esd[t][lo + s];
       }
       dlam_s[t][l] = v;
     }
-  }
+  });
 
   f32x4 dc[RPW][NBW];  // row block RPW rg + rr, column tile cg + NCG q
 #pragma unroll
@@ -1179,9 +1192,13 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   // dlog_a agree where they overlap (the rounding of M ⊙ S to the io type for
   // the dX product would otherwise enter one term and not the other).  Wave w
   // sums the rows t = w mod NW.
-  if (lane < C) {
+  if (lane < C) {  // rows in a loop of fixed length: the reads go out together
     float cs = 0.f;
-    for (int t = lane + ((wave - lane) % NW + NW) % NW; t < C; t += NW) cs += gsh[t][lane];
+#pragma unroll
+    for (int i = 0; i < (C + NW - 1) / NW; ++i) {
+      const int t = wave + i * NW;
+      if (t >= lane && t < C) cs += gsh[t][lane];
+    }
     colpart[wave][lane] = cs;
   }
 
