@@ -34,12 +34,14 @@
 //                               upper half;
 //   3. bwd_level_reduce_kernel  reverse pieces -> one state per (level,
 //                               pair), fp32;
-//   4. bwd_dq_kernel            per chunk: dC (this head) and dlambda, from the
-//                               intra block and the lower-half states;
-//   5. bwd_dkv_kernel           per chunk: dX and dB (this head), from the
-//                               intra block and the upper-half states;
-//   6. bwd_group_sum_kernel     dB, dC = sums over each group's heads;
-//   7. bwd_dloga_part_kernel, bwd_dloga_kernel   suffix sums of dO.O - X.dX.
+//   4. bwd_dq_kernel            per (group, chunk): dC and each head's
+//                               dlambda, from the intra block and the
+//                               lower-half states;
+//   5. bwd_dkv_kernel           per (group, chunk): each head's dX, and dB,
+//                               from the intra block and the upper-half states
+//                               (a work-group takes the group's heads in turn
+//                               and sums their dB or dC in registers);
+//   6. bwd_dloga_part_kernel, bwd_dloga_kernel   suffix sums of dO.O - X.dX.
 #pragma once
 
 #include "loglin_device.hpp"
@@ -64,8 +66,6 @@ struct BwdParams {
   float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
   float* zst;     // [batch*nheads, nstate, N, P] fp32, lower-half sums
   float* rst;     // [batch*nheads, nstate, N, P] fp32, upper-half sums
-  void* dch;      // [batch, seqlen, nheads, N] io type: this head's share of dC
-  void* dbh;      // [batch, seqlen, nheads, N] io type: this head's share of dB
   float* term1;   // [batch*nheads, seqlen] dO_t . O_t
   float* term2;   // [batch*nheads, seqlen] X_t . dX_t
   int batch, seqlen, nheads, ngroups, nlevels;
@@ -765,6 +765,37 @@ __device__ inline int opaque_tid() {
 // level count depends on its index bits, so a fixed residue would load some
 // work-groups far more than others).  Each work-group prefetches the next
 // tile's token rows into registers while it computes the current one.
+// Work items of the chunk passes: tiles (batch * group, chunk), each taken
+// by one work-group for every head of the group in turn, so that the heads'
+// dB and dC contributions add up in registers (no per-head shares and no
+// group-sum pass; the order of the sum is fixed: head order).
+struct BwdItem {
+  int bh, j, b, h, grp, hi;
+};
+struct BwdItems {
+  int hpg, nc, H, G;
+  __device__ explicit BwdItems(const BwdParams& pr)
+      : hpg(pr.nheads / pr.ngroups), nc(pr.nc), H(pr.nheads), G(pr.ngroups) {}
+  __device__ BwdItem at(int item) const {
+    BwdItem x;
+    const int tile = item / hpg;
+    x.hi = item - tile * hpg;
+    const int bg = tile / nc;
+    x.j = tile - bg * nc;
+    x.b = bg / G;
+    x.grp = bg - x.b * G;
+    x.h = x.grp * hpg + x.hi;
+    x.bh = x.b * H + x.h;
+    return x;
+  }
+  // the work-group's item at step mi (its tile at step mi / hpg), or -1
+  template <class CT>
+  __device__ int item(const CT& ct, int mi) const {
+    const int t = ct.tile(mi / hpg);
+    return t < 0 ? -1 : t * hpg + mi % hpg;
+  }
+};
+
 struct ChunkTiles {
   int base, end, L, l;
   __device__ explicit ChunkTiles(int total) {
@@ -825,7 +856,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   const int rg = wave % NRG, cg = wave / NRG;  // state products: row group, column group
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int64_t T_ = pr.seqlen;
-  const ChunkTiles ct(pr.batch * H * pr.nc);
+  const ChunkTiles ct(pr.batch * G * pr.nc);
   // lambda rows: every level the sequence reaches (ll <= BWD_LMAX)
   constexpr int LIT = (C * BWD_LMAX + NT - 1) / NT;
   const int ll = pr.ll;
@@ -834,10 +865,11 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   T lv_[LIT];
   float la = 0.f;
   double ca_hi = 0.0, ca_lo = 0.0;
-  auto load_rows = [&](int tile) {  // token rows of a tile into registers
+  const BwdItems it(pr);
+  auto load_rows = [&](int item) {  // token rows of an item into registers
     const int tid = opaque_tid();
-    const int bh = tile / pr.nc, j = tile % pr.nc;
-    const int b = bh / H, h = bh % H, grp = h / (H / G);
+    const BwdItem x = it.at(item);
+    const int bh = x.bh, j = x.j, b = x.b, h = x.h, grp = x.grp;
     const int64_t t0 = (int64_t)j * C;
     sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
     sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
@@ -859,13 +891,14 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     ca_hi = ca[j];
     ca_lo = ca[(j >> kl) << kl];
   };
-  if (ct.tile(0) >= 0) load_rows(ct.tile(0));
-  for (int m = 0; ct.more(m); ++m) {
-  const int tile = ct.tile(m), next = ct.tile(m + 1);
-  if (tile < 0) continue;  // uniform: the last step has fewer tiles than work-groups
+  f32x4 dc[RPW][NBW];  // row block RPW rg + rr, column tile cg + NCG q: summed over the group's heads
+  if (it.item(ct, 0) >= 0) load_rows(it.item(ct, 0));
+  for (int mi = 0; ct.more(mi / it.hpg); ++mi) {
+  const int item = it.item(ct, mi), next = it.item(ct, mi + 1);
+  if (item < 0) continue;  // uniform: the last step has fewer tiles than work-groups
   const int tid = opaque_tid(), lane = tid & 63, g = lane >> 4, r = lane & 15;
-  const int bh = tile / pr.nc, j = tile % pr.nc;
-  const int b = bh / H, h = bh % H;
+  const BwdItem x = it.at(item);
+  const int bh = x.bh, j = x.j, b = x.b, h = x.h;
   const int64_t t0 = (int64_t)j * C;
   const unsigned act0 = (unsigned)j & ((1u << pr.kc) - 1u);  // active chunk levels (bit k-1)
   const float gap = tid < pr.kc && ((act0 >> tid) & 1u) ? (float)(ca_hi - ca_lo) : 0.f;
@@ -924,11 +957,12 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     }
   });
 
-  f32x4 dc[RPW][NBW];  // row block RPW rg + rr, column tile cg + NCG q
+  if (x.hi == 0) {  // the group's first head: its dC sum starts
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
+    for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-    for (int q = 0; q < NBW; ++q) dc[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < NBW; ++q) dc[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int kt = 0; kt < C / KB; ++kt) {  // keys s; entries with s > t are zero
     typename M::frag a[RPW];
@@ -1052,21 +1086,25 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   }
   if (pk) finish_level(pk, buf ^ 1);
 
-  // the dC tile through LDS (csh: every wave is done with the C rows), then
-  // out by rows
+  // after the group's last head: the dC tile through LDS (csh: every wave
+  // is done with the C rows), then out by rows
+  const bool last = x.hi == it.hpg - 1;  // uniform
   lds_barrier();
+  if (last) {
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
+    for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-    for (int q = 0; q < NBW; ++q)
-      if (NB % NCG == 0 || cg + NCG * q < NB) {
+      for (int q = 0; q < NBW; ++q)
+        if (NB % NCG == 0 || cg + NCG * q < NB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          csh[LN::at(16 * (RPW * rg + rr) + 4 * g + i, 16 * (cg + NCG * q) + r)] = from_f<T>(dc[rr][q][i]);
-      }
+          for (int i = 0; i < 4; ++i)
+            csh[LN::at(16 * (RPW * rg + rr) + 4 * g + i, 16 * (cg + NCG * q) + r)] = from_f<T>(dc[rr][q][i]);
+        }
+  }
   lds_barrier();  // dlam_s and the dC tile are complete
-  rows_from_lds<T, C, N, NT>(csh, static_cast<T*>(pr.dch) + (((int64_t)b * T_ + t0) * H + h) * N,
-                             (int64_t)H * N, tid);
+  if (last)
+    rows_from_lds<T, C, N, NT>(csh, static_cast<T*>(pr.dC) + (((int64_t)b * T_ + t0) * G + x.grp) * N,
+                               (int64_t)G * N, tid);
   dlam_rows_out<T, C, BWD_LMAX, NT>(dlam_s, static_cast<T*>(pr.dlam) + (((int64_t)b * T_ + t0) * H + h) * L, H,
                                     L, pr.ll, tid);
   if (tid < C) pr.term1[(int64_t)bh * T_ + t0 + tid] = term_s[tid];
@@ -1111,17 +1149,18 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   const int rg = wave % NRG, cg = wave / NRG;  // state products: row group, column group
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int64_t T_ = pr.seqlen;
-  const ChunkTiles ct(pr.batch * H * pr.nc);
+  const ChunkTiles ct(pr.batch * G * pr.nc);
   constexpr int LIT = (C * (c_log + 1) + NT - 1) / NT;
   RowsStage<T, C, N, NT> sc, sb;
   RowsStage<T, C, P, NT> sx, so;
   T lv_[LIT];
   float la = 0.f;
   double ca_hi = 0.0, ca_lo = 0.0;
-  auto load_rows = [&](int tile) {  // token rows of a tile into registers
+  const BwdItems it(pr);
+  auto load_rows = [&](int item) {  // token rows of an item into registers
     const int tid = opaque_tid();
-    const int bh = tile / pr.nc, ich = tile % pr.nc;
-    const int b = bh / H, h = bh % H, grp = h / (H / G);
+    const BwdItem x = it.at(item);
+    const int bh = x.bh, ich = x.j, b = x.b, h = x.h, grp = x.grp;
     const int64_t t0 = (int64_t)ich * C;
     sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
     sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
@@ -1144,13 +1183,14 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     ca_hi = ca[min(((ich >> kl) + 1) << kl, pr.nc)];
     ca_lo = ca[ich + 1];
   };
-  if (ct.tile(0) >= 0) load_rows(ct.tile(0));
-  for (int m = 0; ct.more(m); ++m) {
-  const int tile = ct.tile(m), next = ct.tile(m + 1);
-  if (tile < 0) continue;  // uniform: the last step has fewer tiles than work-groups
+  f32x4 db[RPW][NBW];  // dB of the chunk, summed over the group's heads
+  if (it.item(ct, 0) >= 0) load_rows(it.item(ct, 0));
+  for (int mi = 0; ct.more(mi / it.hpg); ++mi) {
+  const int item = it.item(ct, mi), next = it.item(ct, mi + 1);
+  if (item < 0) continue;  // uniform: the last step has fewer tiles than work-groups
   const int tid = opaque_tid(), lane = tid & 63, g = lane >> 4, r = lane & 15;
-  const int bh = tile / pr.nc, i_ch = tile % pr.nc;
-  const int b = bh / H, h = bh % H;
+  const BwdItem x = it.at(item);
+  const int bh = x.bh, i_ch = x.j, b = x.b, h = x.h;
   const int64_t t0 = (int64_t)i_ch * C;
   // active chunk levels (bit k-1): i in a lower half whose upper half exists
   unsigned act0 = 0;
@@ -1204,13 +1244,15 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 
   // dX: intra-chunk part, chunk-level part; dB (row block RPW rg + rr,
   // column tile cg + NCG q of P or of N)
-  f32x4 dx[RPW][PBW], dxe[RPW][PBW], db[RPW][NBW];
+  f32x4 dx[RPW][PBW], dxe[RPW][PBW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
 #pragma unroll
     for (int q = 0; q < PBW; ++q) dx[rr][q] = dxe[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (x.hi == 0) {  // the group's first head: its dB sum starts
 #pragma unroll
-    for (int q = 0; q < NBW; ++q) db[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < NBW; ++q) db[rr][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 #pragma unroll
   for (int kt = 0; kt < C / KB; ++kt) {  // queries t; entries with t < s are zero
@@ -1331,8 +1373,9 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     k = kn;
     buf ^= 1;
   }
-  // the dX and dB tiles through LDS (osh and csh: every wave is done with the
-  // dO and C rows), then out by rows
+  // the dX tile and, after the group's last head, the dB tile through LDS
+  // (osh and csh: every wave is done with the dO and C rows), then out by rows
+  const bool last = x.hi == it.hpg - 1;  // uniform
   lds_barrier();
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
@@ -1351,9 +1394,11 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
         }
       }
       part[i] = pt;
+      if (last) {
 #pragma unroll
-      for (int q = 0; q < NBW; ++q)
-        if (NB % NCG == 0 || cg + NCG * q < NB) csh[LN::at(s, 16 * (cg + NCG * q) + r)] = from_f<T>(db[rr][q][i]);
+        for (int q = 0; q < NBW; ++q)
+          if (NB % NCG == 0 || cg + NCG * q < NB) csh[LN::at(s, 16 * (cg + NCG * q) + r)] = from_f<T>(db[rr][q][i]);
+      }
     }
     // lanes r < 4 of lane group g hold the row sums of s = sw + 4 g + [0, 2, 1, 3][r]
     const float rs = sum16x4(part, r);
@@ -1362,8 +1407,9 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
   lds_barrier();  // colpart, xpart and the dX and dB tiles are complete
   rows_from_lds<T, C, P, NT>(osh, static_cast<T*>(pr.dX) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P,
                              tid);
-  rows_from_lds<T, C, N, NT>(csh, static_cast<T*>(pr.dbh) + (((int64_t)b * T_ + t0) * H + h) * N,
-                             (int64_t)H * N, tid);
+  if (last)
+    rows_from_lds<T, C, N, NT>(csh, static_cast<T*>(pr.dB) + (((int64_t)b * T_ + t0) * G + x.grp) * N,
+                               (int64_t)G * N, tid);
   if (tid < C) {
     float cs = 0.f;
 #pragma unroll
@@ -1378,35 +1424,6 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
 }
 
 // ------------------------------------------------------------ launch 6
-
-// dB and dC: the heads of each group summed in head order (the per-head
-// shares are stored in the io type, summed in fp32); 4 elements per thread.
-template <class T, int N>
-__global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdParams pr) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int H = pr.nheads, G = pr.ngroups, hpg = H / G;
-  const int64_t total = (int64_t)pr.batch * pr.seqlen * G * (N / 4);
-  if (q >= total) return;
-  const int n = (int)(q % (N / 4)) * 4;
-  const int64_t rest = q / (N / 4);
-  const int grp = (int)(rest % G);
-  const int64_t bt = rest / G;
-  f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < hpg; ++k) {
-    const int64_t idx = (bt * H + grp * hpg + k) * N + n;
-    const T* pb = static_cast<const T*>(pr.dbh) + idx;
-    const T* pc = static_cast<const T*>(pr.dch) + idx;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sb[e] += to_f(pb[e]);
-      sc[e] += to_f(pc[e]);
-    }
-  }
-  store4(static_cast<T*>(pr.dB) + (bt * G + grp) * N + n, sb);
-  store4(static_cast<T*>(pr.dC) + (bt * G + grp) * N + n, sc);
-}
-
-// ------------------------------------------------------------ launch 7
 
 // dlog_a[t] = sum_{t' >= t} (term1 - term2), in fp64, over segments of
 // whole 1024-token blocks (at most DLOGA_SEGS per (batch, head)): first each
@@ -1529,14 +1546,11 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
       hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>),
                          dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
   }
-  const int tiles = pr.nc * bh;
+  const int tiles = pr.nc * pr.batch * pr.ngroups;  // (batch * group, chunk), every head of the group in turn
   hipLaunchKernelGGL((bwd_dq_kernel<T, C, P, N>), dim3(bwd_chunk_grid(bwd_dq_kernel<T, C, P, N>, C, tiles)),
                      dim3(bwd_chunk_threads(C)), 0, st, pr);
   hipLaunchKernelGGL((bwd_dkv_kernel<T, C, P, N>), dim3(bwd_chunk_grid(bwd_dkv_kernel<T, C, P, N>, C, tiles)),
                      dim3(bwd_chunk_threads(C)), 0, st, pr);
-  const int64_t groups4 = (int64_t)pr.batch * pr.seqlen * pr.ngroups * (N / 4);
-  hipLaunchKernelGGL((bwd_group_sum_kernel<T, N>), dim3((unsigned)((groups4 + 255) / 256)),
-                     dim3(256), 0, st, pr);
   const int nseg = dloga_nseg(pr.seqlen);
   hipLaunchKernelGGL((bwd_dloga_part_kernel<T>), dim3(nseg, bh), dim3(256), 0, st, pr);
   hipLaunchKernelGGL((bwd_dloga_kernel<T>), dim3(nseg, bh), dim3(BWD_SCAN_NT), 0, st, pr);

@@ -155,7 +155,7 @@ loglin::BwdFn pick_bwd(int dtype, int chunk, int P, int N) {
 // two per-token terms of dlog_a; each region 256-byte aligned.
 struct BwdPlan {
   int nc, kc, ll, npart, nstate, nstate_direct;
-  size_t off_atot, off_cuma, off_pf, off_pr, off_z, off_r, off_dch, off_dbh, off_t1, off_t2, bytes;
+  size_t off_atot, off_cuma, off_pf, off_pr, off_z, off_r, off_t1, off_t2, bytes;
 };
 
 int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
@@ -181,7 +181,6 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   pl->nstate = (int)nstate;
   const size_t bh = (size_t)(d->batch * d->nheads);
   const size_t pn = (size_t)(d->headdim * d->dstate);
-  const size_t tok = (size_t)(d->batch * d->seqlen);
   size_t off = 0;
   pl->off_atot = off;
   off = round_up(off + bh * fp.nc * sizeof(float));
@@ -195,11 +194,6 @@ int check_bwd_dims(const loglin_dims* d, int chunk, BwdPlan* pl) {
   off = round_up(off + bh * nstate * pn * sizeof(float));
   pl->off_r = off;
   off = round_up(off + bh * nstate * pn * sizeof(float));
-  const size_t esz = d->io_dtype == LOGLIN_BF16 ? 2 : 4;  // per-head shares in the io type
-  pl->off_dch = off;
-  off = round_up(off + tok * d->nheads * d->dstate * esz);
-  pl->off_dbh = off;
-  off = round_up(off + tok * d->nheads * d->dstate * esz);
   pl->off_t1 = off;
   off = round_up(off + bh * d->seqlen * sizeof(float));
   pl->off_t2 = off;
@@ -449,8 +443,6 @@ int loglin_bwd(const void* X, const void* B, const void* C, const float* log_a,
   pr.part_r = reinterpret_cast<float*>(ws + pl.off_pr);
   pr.zst = reinterpret_cast<float*>(ws + pl.off_z);
   pr.rst = reinterpret_cast<float*>(ws + pl.off_r);
-  pr.dch = ws + pl.off_dch;
-  pr.dbh = ws + pl.off_dbh;
   pr.term1 = reinterpret_cast<float*>(ws + pl.off_t1);
   pr.term2 = reinterpret_cast<float*>(ws + pl.off_t2);
   pr.batch = (int)dims->batch;
