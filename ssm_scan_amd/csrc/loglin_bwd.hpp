@@ -711,15 +711,13 @@ struct StateStage {
   static constexpr int IT = (PIECES + NT - 1) / NT;
   static constexpr int F4 = L::VEC / 4;  // float4 per piece
   f32x4 v[IT][F4];
-  __device__ inline void load(const float* g, int tid) {
+  __device__ inline void load(const float* g, int tid) {  // unconditional: see RowsStage
 #pragma unroll
     for (int q = 0; q < IT; ++q) {
-      const int i = q * NT + tid;
-      if (i < PIECES) {
-        const float* src = g + (int64_t)(i / L::NBLK) * P + (i % L::NBLK) * L::VEC;
+      const int i = PIECES % NT == 0 ? q * NT + tid : min(q * NT + tid, PIECES - 1);
+      const float* src = g + (int64_t)(i / L::NBLK) * P + (i % L::NBLK) * L::VEC;
 #pragma unroll
-        for (int f = 0; f < F4; ++f) v[q][f] = *reinterpret_cast<const f32x4*>(src + 4 * f);
-      }
+      for (int f = 0; f < F4; ++f) v[q][f] = *reinterpret_cast<const f32x4*>(src + 4 * f);
     }
   }
   __device__ inline void store(T* hi, T* lo, int tid) const {
@@ -871,6 +869,8 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     const BwdItem x = it.at(item);
     const int bh = x.bh, j = x.j, b = x.b, h = x.h, grp = x.grp;
     const int64_t t0 = (int64_t)j * C;
+    // the group's C and B rows (loaded for every head, a branch here would
+    // make the compiler wait for them; staged only for the first)
     sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
     sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
     sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
@@ -903,8 +903,10 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   const unsigned act0 = (unsigned)j & ((1u << pr.kc) - 1u);  // active chunk levels (bit k-1)
   const float gap = tid < pr.kc && ((act0 >> tid) & 1u) ? (float)(ca_hi - ca_lo) : 0.f;
 
-  sc.store(csh, tid);
-  sb.store(bsh, tid);
+  if (x.hi == 0) {  // later heads of the group find the C and B rows in place
+    sc.store(csh, tid);
+    sb.store(bsh, tid);
+  }
   sx.store(xsh, tid);
   so.store(osh, tid);
 #pragma unroll
@@ -1162,6 +1164,8 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     const BwdItem x = it.at(item);
     const int bh = x.bh, ich = x.j, b = x.b, h = x.h, grp = x.grp;
     const int64_t t0 = (int64_t)ich * C;
+    // the group's C and B rows (loaded for every head, a branch here would
+    // make the compiler wait for them; staged only for the first)
     sc.load(static_cast<const T*>(pr.Cm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
     sb.load(static_cast<const T*>(pr.Bm) + (((int64_t)b * T_ + t0) * G + grp) * N, (int64_t)G * N, tid);
     sx.load(static_cast<const T*>(pr.X) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
@@ -1198,8 +1202,10 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
     if (!((i_ch >> (k - 1)) & 1) && ((((i_ch >> (k - 1)) + 1) << (k - 1)) < pr.nc)) act0 |= 1u << (k - 1);
   const float gap = tid < pr.kc && ((act0 >> tid) & 1u) ? (float)(ca_hi - ca_lo) : 0.f;
 
-  sc.store(csh, tid);
-  sb.store(bsh, tid);
+  if (x.hi == 0) {  // later heads of the group find the C and B rows in place
+    sc.store(csh, tid);
+    sb.store(bsh, tid);
+  }
   sx.store(xsh, tid);
   so.store(osh, tid);
 #pragma unroll
