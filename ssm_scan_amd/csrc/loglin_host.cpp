@@ -149,9 +149,9 @@ loglin::BwdFn pick_bwd(int dtype, int chunk, int P, int N) {
   return nullptr;
 }
 
-// Backward workspace: chunk log-decays and their fp64 prefix sums, the two
-// directions' piece partials
-// and level states (fp32), the per-head dC and dB shares and the
+// Backward workspace: chunk log-decays and their fp64 prefix sums, the
+// totals of the groups of 8 chunks (forward direction), the reverse
+// direction's piece partials, both directions' level states (fp32) and the
 // two per-token terms of dlog_a; each region 256-byte aligned.
 struct BwdPlan {
   int nc, kc, ll, npart, nstate, nstate_direct;
