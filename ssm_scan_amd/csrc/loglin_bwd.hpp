@@ -80,17 +80,6 @@ constexpr int BWD_PIECE = 8;
 // Levels held per token row in LDS (sequences up to 2^31 tokens).
 constexpr int BWD_LMAX = 32;
 
-constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
-
-// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
-template <int B, int E, class F>
-__device__ inline void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 // Pairs at chunk level k whose upper half holds at least one chunk.
 __host__ __device__ inline int bwd_pairs(int nc, int k) {
   const int half = 1 << (k - 1);

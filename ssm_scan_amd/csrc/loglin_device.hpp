@@ -205,6 +205,17 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ inline int bit_length(unsigned x) {
   return x ? 32 - __builtin_clz(x) : 0;
 }
@@ -811,6 +822,142 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
   wait_vm<0>();
   if (nfull < ns && nfull % SCAN_DEC == 0) refill(nfull);
   for (int q = nfull; q < ns; ++q) step(widen(ring[wv][q - nfull][lane]), q);
+}
+
+// The same level scan for up to SCAN_RMAX L segments, split into ranges of
+// L segments that run side by side, one wave per range (work-group = the
+// ranges of one run of 64 E state elements).  A slot is the sum over an
+// aligned block of segments, and every block of at most L segments lies in
+// one range, so each wave sweeps its range with a stack of depth log2 L,
+// starting empty.  The blocks that span ranges are the slots of a range's
+// last segment when the range index is odd (2^t ranges for t trailing ones
+// of the index): they are formed after the sweeps from the ranges' totals,
+// exchanged through LDS.  The gaps of levels above log2 L + 1 likewise add
+// the log-decays of whole ranges to the range-local prefix.  All of a
+// wave's copies are issued before its first step (L is a compile-time
+// count, and the sweep is unrolled, so every stack index is a constant).
+constexpr int SCAN_RMAX = 8;
+constexpr int SCAN_L = 16;
+
+template <class T, int N, int L>
+__global__ __launch_bounds__(64 * SCAN_RMAX) void scan_range_kernel(Params pr, int pn) {
+  using M = Mfma<T>;
+  constexpr int E = 16 / (int)sizeof(T);  // state elements per lane
+  constexpr int J = ilog2c(L);
+  static_assert(L == (1 << J) && E % 4 == 0, "ranges of 2^J segments");
+  __shared__ f32x4 tot_s[SCAN_RMAX][E / 4][64];  // range totals, fp32
+  __shared__ float tdec_s[SCAN_RMAX];              // range log-decays
+  const int bh = blockIdx.y, ns = pr.ns, ks = pr.ks;
+  const int lane = threadIdx.x & 63;
+  const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's range
+  const int q0 = r * L;
+  const int e = (blockIdx.x * 64 + lane) * E;  // the grid covers pn exactly
+  const T* src = static_cast<const T*>(pr.seg_state) + (int64_t)bh * ns * pn + e;
+  T* dst = static_cast<T*>(pr.slots) + (int64_t)bh * ns * pn + slot_index<T, N>(e / N, e % N);
+  const float* dec = pr.seg_decay + (int64_t)bh * ns;
+  float* gd = pr.gap_decay + (int64_t)bh * ns * (ks + 1);
+  const bool gap_lane = blockIdx.x == 0 && lane <= ks;  // lane k writes level k's gap
+
+  struct Run {
+    float v[E];
+  };
+  auto widen = [](const f32x4& raw) __attribute__((always_inline)) {
+    Run x;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int c = 0; c < E; ++c) x.v[c] = (float)h[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < E; ++c) x.v[c] = raw[c];
+    }
+    return x;
+  };
+  auto put = [&](int q, const Run& v) __attribute__((always_inline)) {
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 o;
+#pragma unroll
+      for (int c = 0; c < E; ++c) o[c] = (bf16)v.v[c];
+      store16(dst + (int64_t)q * pn, o);
+    } else {
+      store4(dst + (int64_t)q * pn, f32x4{v.v[0], v.v[1], v.v[2], v.v[3]});
+    }
+  };
+
+  // the range's copies and log-decays (segments past the end repeat the
+  // last one; nothing they give is stored)
+  f32x4 raw[L];
+  float dq[L];
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int qc = min(q0 + u, ns - 1);
+    raw[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)qc * pn);
+    dq[u] = dec[qc];
+  }
+  Run stk[J + 1];
+  float stka[J + 1];
+  float pre[L];  // log-decay from the range's start to segment q0 + u
+#pragma unroll
+  for (int i = 0; i <= J; ++i) stka[i] = 0.f;
+  static_for<0, L>([&](auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int z = __builtin_ctz(~(unsigned)u);  // trailing ones of u
+    const int q = q0 + u;
+    // live entries before segment q: the set bits of u
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < J; ++i)
+      if ((u >> i) & 1) run += (i + 1 < lane || lane > J + 1) ? stka[i] : 0.f;
+    pre[u] = run;
+    if (gap_lane && lane <= J + 1 && q < ns) gd[q * (ks + 1) + lane] = run;
+    Run v = widen(raw[u]);
+    float acur = dq[u];
+#pragma unroll
+    for (int i = 0; i < z; ++i) {
+      const float w = M::ex(acur);
+#pragma unroll
+      for (int c = 0; c < E; ++c) v.v[c] = w * stk[i].v[c] + v.v[c];
+      acur += stka[i];
+    }
+    stk[z] = v;
+    stka[z] = acur;
+    // the last segment's block spans ranges when r is odd (formed below)
+    if (q < ns - 1 && (u < L - 1 || (r & 1) == 0)) put(q, v);
+  });
+
+  // range totals to LDS
+#pragma unroll
+  for (int c4 = 0; c4 < E / 4; ++c4)
+    tot_s[r][c4][lane] = f32x4{stk[J].v[4 * c4], stk[J].v[4 * c4 + 1], stk[J].v[4 * c4 + 2], stk[J].v[4 * c4 + 3]};
+  if (lane == 0) tdec_s[r] = stka[J];
+  __syncthreads();
+
+  const int qe = q0 + L - 1;
+  if ((r & 1) && qe < ns - 1) {  // block of 2^t ranges ending with this one
+    const int t = __builtin_ctz(~(unsigned)r);
+    Run acc = stk[J];
+    float a = stka[J];
+    for (int rr = r - 1; rr > r - (1 << t); --rr) {
+      const float w = M::ex(a);
+#pragma unroll
+      for (int c4 = 0; c4 < E / 4; ++c4) {
+        const f32x4 x = tot_s[rr][c4][lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc.v[4 * c4 + c] = w * x[c] + acc.v[4 * c4 + c];
+      }
+      a += tdec_s[rr];
+    }
+    put(qe, acc);
+  }
+  if (gap_lane && lane > J + 1) {
+    // level k = lane: its aligned block starts at range (r >> (k-1-J)) << (k-1-J)
+    const int sh = lane - 1 - J;
+    float rp = 0.f;
+    for (int rr = (r >> sh) << sh; rr < r; ++rr) rp += tdec_s[rr];
+#pragma unroll
+    for (int u = 0; u < L; ++u)
+      if (q0 + u < ns) gd[(q0 + u) * (ks + 1) + lane] = pre[u] + rp;
+  }
 }
 
 // ------------------------------------------------------------- pass 3

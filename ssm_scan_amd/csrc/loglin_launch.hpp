@@ -56,7 +56,11 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
     constexpr int E = 16 / (int)sizeof(T);  // state elements per scan thread
     static_assert((P * N) % (64 * E) == 0, "a scan wave covers 64 E state elements");
     dim3 g2((P * N + E * SCAN_NT - 1) / (E * SCAN_NT), pr.batch * pr.nheads);
-    if (pr.ns < (1 << 10))  // a stack of 10 block sums covers fewer than 2^10 segments
+    dim3 g3(P * N / (64 * E), pr.batch * pr.nheads);  // one wave's elements per work-group
+    if (pr.ns <= SCAN_RMAX * SCAN_L)  // ranges of SCAN_L segments side by side
+      hipLaunchKernelGGL((scan_range_kernel<T, N, SCAN_L>), g3, dim3(64 * ((pr.ns + SCAN_L - 1) / SCAN_L)), 0, st,
+                         pr, P * N);
+    else if (pr.ns < (1 << 10))  // a stack of 10 block sums covers fewer than 2^10 segments
       hipLaunchKernelGGL((scan_kernel<T, N, 10>), g2, dim3(SCAN_NT), 0, st, pr, P * N);
     else
       hipLaunchKernelGGL((scan_kernel<T, N, MAX_DEPTH>), g2, dim3(SCAN_NT), 0, st, pr, P * N);

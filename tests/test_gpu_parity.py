@@ -94,6 +94,14 @@ def test_segment_depths(seg, T):
     check(small_cfg(T=T, H=2, G=1), seg_log2=seg, variant="slow_decay")
 
 
+@pytest.mark.parametrize("nseg", [100, 128, 130])
+def test_segment_ranges(nseg):
+    """One-chunk segments, 100 and 128 of them (the level scan in ranges of
+    16 segments: blocks of 2 and 4 ranges, a short last range, gaps of levels
+    above a range) and 130 (the single sweep)."""
+    check(small_cfg(T=64 * nseg, H=2, G=1), seg_log2=0, variant="slow_decay")
+
+
 @pytest.mark.parametrize("seg", [0, 1, 2, 3])
 def test_segment_depths_fp32(seg):
     cfg = small_cfg(dtype="fp32", T=16 * 37, H=2, G=1, P=16, N=32, C=16, decay="softplus")
