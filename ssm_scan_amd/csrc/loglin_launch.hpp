@@ -44,7 +44,12 @@ int launch_forward(const Params& base, hipStream_t st, void* const* ev) {
   if (pr.ns > 1 && above) {
     // bf16 heads of one group share their B rows in one work-group
     constexpr bool SPAIRS = sizeof(T) == 2;
-    if (SPAIRS && (pr.nheads / pr.ngroups) % 2 == 0) {
+    if (OUT2 && use2 && (pr.nheads / pr.ngroups) % 2 == 0) {
+      // the output pass's shape: the same LDS layouts as there
+      constexpr int NN = OUT2 ? N : 128;
+      pr.total = pr.batch * pr.ns * (pr.nheads / 2);
+      hipLaunchKernelGGL((state2_kernel<NN>), dim3(pad8(pr.total)), dim3(512), 0, st, pr);
+    } else if (SPAIRS && (pr.nheads / pr.ngroups) % 2 == 0) {
       pr.total = pr.batch * pr.ns * (pr.nheads / 2);
       hipLaunchKernelGGL((state_kernel<T, C, P, N, SPAIRS ? 2 : 1>), dim3(pad8(pr.total)),
                          dim3(2 * Tl::NT), 0, st, pr);

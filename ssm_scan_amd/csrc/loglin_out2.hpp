@@ -591,4 +591,171 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
   }
 }
 
+// State pass for the same shape, in the output pass's LDS layouts: the
+// transposing reads of B (272-byte rows) and X (128-byte rows, lane-keyed
+// swizzle) are a lane base plus an immediate, so the only per-chunk address
+// work is the copies'.  One work-group per (batch, segment, two heads of a
+// group), eight waves: wave w serves head w / 4 and its state columns
+// [16 (w mod 4), +16), all N rows.  The heads share one copy of the B rows.
+// The segment's log-decays are copied once, up front, and each chunk's
+// decays are formed while the chunk before it is being reduced; the states
+// go out through LDS, whole 128-byte lines at a time.
+// What it computes is state_kernel's (loglin_device.hpp): each segment's
+// state, decayed to the segment's end, in natural row order, and the
+// segment's log-decay.
+template <int N>
+__global__ __launch_bounds__(512, 2) void state2_kernel(Params pr) {
+  using O = Out2<N>;
+  using M = Mfma<bf16>;
+  constexpr int C = O::C, P = O::P, NB = O::NB, BROW = O::BROW, BBLK = O::BBLK, BINST = O::BINST;
+  constexpr int NWT = 8;
+  constexpr int SEG = 1 << MAX_SEG_LOG2;
+  constexpr int SROW = 2 * N + 16;  // bytes per staged state row (one pad block)
+  static_assert(P * SROW <= C * BROW, "a head's state fits one B buffer");
+  __shared__ __attribute__((aligned(16))) unsigned char bsh0[C * BROW];
+  __shared__ __attribute__((aligned(16))) unsigned char bsh1[C * BROW];
+  __shared__ __attribute__((aligned(16))) unsigned char xsh0[2][C * P * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char xsh1[2][C * P * 2];
+  // per head: the segment's log-decays, and the chunk decays by chunk parity
+  __shared__ __attribute__((aligned(16))) float las[2][SEG * C];
+  __shared__ __attribute__((aligned(16))) float cum[2][2][C], ecum[2][2][C], wst[2][2][C];
+
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  if (tile >= pr.total) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NWT);
+  const int hh = wave >> 2, wv = wave & 3;
+  const int g = lane >> 4, r = lane & 15;
+  const int H = pr.nheads, G = pr.ngroups;
+  // heads of one group next to each other, then groups, then segments (as
+  // state_kernel)
+  const int hpg = H / G, npair = hpg / 2;
+  const int pi = tile % npair;
+  const int grp = (tile / npair) % G;
+  const int q = (tile / (npair * G)) % pr.ns;
+  const int b = tile / (npair * G * pr.ns);
+  const int h0 = grp * hpg + pi * 2;
+  const int h = h0 + hh;
+  const int bh = b * H + h;
+  const int seg = 1 << pr.m;
+  const int j0 = q * seg;
+  const int nch = min(seg, pr.nc - j0);
+  const bf16* Xg = static_cast<const bf16*>(pr.X);
+  const bf16* Bg = static_cast<const bf16*>(pr.Bm);
+
+  // B^T transposing reads: + (32 kt + 4 hh) BROW + 32 nb
+  const unsigned o_bt = (8 * g + (r >> 2)) * BROW + 8 * (r & 3);
+  // X^T transposing reads: + (32 kt + 4 hh) 128
+  const int keyx = ((r >> 3) & 1) | ((g & 1) << 1);
+  const unsigned o_xt = (8 * g + (r >> 2)) * 128 + 16 * ((2 * wv + ((r & 3) >> 1)) ^ (2 * keyx)) +
+                        8 * (r & 1);
+  // copy pieces (byte offsets from the chunk's first row; a B pad block
+  // repeats the row's last block)
+  const unsigned rs_bc = (unsigned)G * N * 2, rs_x = (unsigned)H * P * 2;
+  auto cbc_off = [&](int inst) __attribute__((always_inline)) {
+    const unsigned pos = (unsigned)(inst * 64 + lane);
+    const unsigned rho = pos / BBLK;
+    const unsigned blk = min(pos - rho * BBLK, (unsigned)(BBLK - 2));
+    return __umul24(rho, rs_bc) + 16u * blk;
+  };
+  auto cx_off = [&](int k) __attribute__((always_inline)) {
+    const int pos = (wv + 4 * k) * 64 + lane;
+    const int rho = pos >> 3, phys = pos & 7;
+    const int key = ((rho >> 1) & 1) | (((rho >> 3) & 1) << 1);
+    return __umul24((unsigned)rho, rs_x) + 16u * (phys ^ (2 * key));
+  };
+  auto issue = [&](int j, unsigned char* bs, unsigned char (*xs)[C * P * 2]) __attribute__((always_inline)) {
+    const int64_t r0 = (int64_t)b * pr.seqlen + (int64_t)j * C;
+    const bf16* bsrc = Bg + (r0 * G + grp) * N;
+    const bf16* xsrc = Xg + (r0 * H + h) * P;
+#pragma unroll
+    for (int k = 0; k < (BINST + NWT - 1) / NWT; ++k)
+      if (BINST % NWT == 0 || wave + NWT * k < BINST)
+        dma_16x64_at(bsrc, cbc_off(wave + NWT * k), lds_addr(bs) + (wave + NWT * k) * 1024u);
+#pragma unroll
+    for (int k = 0; k < O::XINST_W; ++k) dma_16x64_at(xsrc, cx_off(k), lds_addr(xs[hh]) + (wv + 4 * k) * 1024u);
+  };
+
+  // the segment's log-decays of this head: wave 0 copies chunk k's, lane t
+  // token t (one 4-byte element per lane)
+  if (wv == 0) {
+    const float* lsrc = pr.log_a + ((int64_t)b * pr.seqlen + (int64_t)j0 * C) * H + h;
+#pragma unroll
+    for (int k = 0; k < SEG; ++k)
+      if (k < nch) dma_4x64_at(lsrc, (unsigned)((k * C + lane) * H) * 4u, lds_addr(&las[hh][k * C]));
+  }
+  f32x4 S[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float seg_sum = 0.f;
+  issue(j0, bsh0, xsh0);
+  auto step = [&](auto cur_c, int jl) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const unsigned char* bs = CUR ? bsh1 : bsh0;
+    const unsigned char* xs = CUR ? xsh1[hh] : xsh0[hh];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the chunk have landed
+    if (jl == 0 && wv == 0)  // (later chunks' decays are formed a step ahead)
+      chunk_decays<bf16, C>(las[hh][lane], cum[hh][0], ecum[hh][0], wst[hh][0], lane);
+    lds_barrier();
+    if (jl + 1 < nch)  // the other buffers were released by the previous barrier
+      issue(j0 + jl + 1, CUR ? bsh0 : bsh1, CUR ? xsh0 : xsh1);
+    const float atot = cum[hh][CUR][C - 1];
+    if (jl > 0) {
+      const float dec = M::ex(atot);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) S[nb] *= dec;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // X rows scaled by the decay to the chunk end: token 32 kt + 8 g + jj
+      const unsigned char* px = xs + o_xt + 32 * kt * 128;
+      const bf16x8 xt = cat8(lds_read8_tr(px), lds_read8_tr(px + 4 * 128));
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wst[hh][CUR][32 * kt + 8 * g]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wst[hh][CUR][32 * kt + 8 * g + 4]);
+      bf16x8 xw;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        xw[jj] = (bf16)((float)xt[jj] * w0[jj]);
+        xw[jj + 4] = (bf16)((float)xt[jj + 4] * w1[jj]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const unsigned char* pb = bs + o_bt + 32 * kt * BROW + 32 * nb;
+        S[nb] = M::mma(cat8(lds_read8_tr(pb), lds_read8_tr(pb + 4 * BROW)), xw, S[nb]);
+      }
+    }
+    if (jl + 1 < nch && wv == 0)
+      chunk_decays<bf16, C>(las[hh][(jl + 1) * C + lane], cum[hh][CUR ^ 1], ecum[hh][CUR ^ 1],
+                            wst[hh][CUR ^ 1], lane);
+    seg_sum += atot;
+    lds_barrier();
+  };
+  for (int jl = 0; jl < nch; jl += 2) {
+    step(std::integral_constant<int, 0>{}, jl);
+    if (jl + 1 < nch) step(std::integral_constant<int, 1>{}, jl + 1);
+  }
+
+  // The state in natural row order (row n of column p at p N + n), staged
+  // in the B buffers (one per head; the last barrier released them) and
+  // written out in whole rows.
+  unsigned char* stg = hh ? bsh1 : bsh0;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const bf16x4 o4 = {(bf16)S[nb][0], (bf16)S[nb][1], (bf16)S[nb][2], (bf16)S[nb][3]};
+    *reinterpret_cast<bf16x4*>(stg + (16 * wv + r) * SROW + 2 * (16 * nb + 4 * g)) = o4;
+  }
+  lds_barrier();
+  constexpr int RB = 2 * N / 16;  // 16-byte blocks per state row
+  unsigned char* dst = reinterpret_cast<unsigned char*>(static_cast<bf16*>(pr.seg_state) +
+                                                        ((int64_t)bh * pr.ns + q) * (P * N));
+#pragma unroll
+  for (int k = 0; k < P * RB / 256; ++k) {
+    const int piece = (wv + 4 * k) * 64 + lane;  // this head's 16-byte pieces
+    const int p = piece / RB, blk = piece % RB;
+    *reinterpret_cast<bf16x8*>(dst + piece * 16) = *reinterpret_cast<const bf16x8*>(stg + p * SROW + 16 * blk);
+  }
+  if (wv == 0 && lane == 0) pr.seg_decay[(int64_t)bh * pr.ns + q] = seg_sum;
+}
+
 }  // namespace loglin
