@@ -836,7 +836,7 @@ __global__ __launch_bounds__(SCAN_NT) void scan_kernel(Params pr, int pn) {
 // the log-decays of whole ranges to the range-local prefix.  All of a
 // wave's copies are issued before its first step (L is a compile-time
 // count, and the sweep is unrolled, so every stack index is a constant).
-constexpr int SCAN_RMAX = 8;
+constexpr int SCAN_RMAX = 16;
 constexpr int SCAN_L = 16;
 
 template <class T, int N, int L>

@@ -94,12 +94,13 @@ def test_segment_depths(seg, T):
     check(small_cfg(T=T, H=2, G=1), seg_log2=seg, variant="slow_decay")
 
 
-@pytest.mark.parametrize("nseg", [100, 128, 130])
-def test_segment_ranges(nseg):
-    """One-chunk segments, 100 and 128 of them (the level scan in ranges of
-    16 segments: blocks of 2 and 4 ranges, a short last range, gaps of levels
-    above a range) and 130 (the single sweep)."""
-    check(small_cfg(T=64 * nseg, H=2, G=1), seg_log2=0, variant="slow_decay")
+@pytest.mark.parametrize("nseg,C", [(100, 64), (128, 64), (130, 64), (256, 32), (257, 32)])
+def test_segment_ranges(nseg, C):
+    """One-chunk segments, 100 to 256 of them (the level scan in ranges of
+    16 segments: blocks of 2 to 8 ranges, a short last range, gaps of levels
+    above a range; 32-token chunks keep the oracle's sequence short) and 257
+    (the single sweep)."""
+    check(small_cfg(T=C * nseg, H=2, G=1, C=C), seg_log2=0, variant="slow_decay")
 
 
 @pytest.mark.parametrize("seg", [0, 1, 2, 3])
