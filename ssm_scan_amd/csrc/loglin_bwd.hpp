@@ -45,6 +45,7 @@
 #pragma once
 
 #include "loglin_device.hpp"
+#include "loglin_out2.hpp"
 
 namespace loglin {
 
@@ -442,6 +443,170 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
   for (int nb = 0; nb < Tl::NB; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wave + r] = S[nb][i];
+}
+
+// The reverse-direction pieces for the output pass's shape (bf16, 64-token
+// chunks, P = 64, N = 64 or 128), in that pass's LDS layouts: C rows in
+// 272-byte rows, dO rows with the lane-keyed swizzle, so every transposing
+// operand read is a lane base plus an immediate.  One work-group per (piece,
+// batch, two heads of a group), eight waves: wave w serves head w / 4 and
+// its state columns [16 (w mod 4), +16); the heads share one copy of the C
+// rows.  The piece's log-decays and level weights are copied once, up front,
+// and each chunk's weights are formed while the chunk after it (the walk
+// runs backwards) is being reduced.  What it computes is
+// bwd_level_state_kernel's reverse direction.
+template <int N>
+__global__ __launch_bounds__(512, 2) void bwd_level_state2_kernel(BwdParams pr) {
+  using O = Out2<N>;
+  using M = Mfma<bf16>;
+  constexpr int C = O::C, P = O::P, NB = O::NB, BROW = O::BROW, BBLK = O::BBLK, BINST = O::BINST;
+  constexpr int NWT = 8;
+  constexpr int c_log = 6;
+  __shared__ __attribute__((aligned(16))) unsigned char csh0[C * BROW];
+  __shared__ __attribute__((aligned(16))) unsigned char csh1[C * BROW];
+  __shared__ __attribute__((aligned(16))) unsigned char dsh0[2][C * P * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char dsh1[2][C * P * 2];
+  // per head: the piece's log-decays and level-weight words (by position in
+  // the piece), and per chunk parity the decays and the weights
+  __shared__ __attribute__((aligned(16))) float las[2][BWD_PIECE * C];
+  __shared__ __attribute__((aligned(16))) unsigned lws[2][BWD_PIECE * C];
+  __shared__ __attribute__((aligned(16))) float cum[2][2][C], ecum[2][2][C], wst[2][2][C], wsh[2][2][C];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NWT);
+  const int hh = wave >> 2, wv = wave & 3;
+  const int g = lane >> 4, r = lane & 15;
+  const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
+  const int b = blockIdx.y / (H / 2), h0 = 2 * (blockIdx.y % (H / 2));
+  const int h = h0 + hh, grp = h0 / (H / G);
+  const int bh = b * H + h;
+  const int64_t T_ = pr.seqlen;
+  int k, pair, pc;
+  bwd_piece_of(blockIdx.x, pr.nc, pr.kc, k, pair, pc);
+  const int half = 1 << (k - 1);
+  const int base = pair * 2 * half + half;  // first chunk of the upper half
+  const int lo = base + pc * BWD_PIECE;
+  if (lo >= pr.nc) return;  // uniform: a piece past the sequence (the reduce skips it)
+  const int hi = min(min(lo + BWD_PIECE, base + half), pr.nc);
+  const int n = hi - lo;
+  const int lev = c_log + k;
+  const bf16* Cg = static_cast<const bf16*>(pr.Cm);
+  const bf16* Dg = static_cast<const bf16*>(pr.dO);
+
+  // C^T transposing reads: + (32 kt + 4 hh) BROW + 32 nb
+  const unsigned o_bt = (8 * g + (r >> 2)) * BROW + 8 * (r & 3);
+  // dO^T transposing reads: + (32 kt + 4 hh) 128
+  const int keyx = ((r >> 3) & 1) | ((g & 1) << 1);
+  const unsigned o_xt = (8 * g + (r >> 2)) * 128 + 16 * ((2 * wv + ((r & 3) >> 1)) ^ (2 * keyx)) +
+                        8 * (r & 1);
+  const unsigned rs_c = (unsigned)G * N * 2, rs_d = (unsigned)H * P * 2;
+  auto cc_off = [&](int inst) __attribute__((always_inline)) {
+    const unsigned pos = (unsigned)(inst * 64 + lane);
+    const unsigned rho = pos / BBLK;
+    const unsigned blk = min(pos - rho * BBLK, (unsigned)(BBLK - 2));
+    return __umul24(rho, rs_c) + 16u * blk;
+  };
+  auto cd_off = [&](int kx) __attribute__((always_inline)) {
+    const int pos = (wv + 4 * kx) * 64 + lane;
+    const int rho = pos >> 3, phys = pos & 7;
+    const int key = ((rho >> 1) & 1) | (((rho >> 3) & 1) << 1);
+    return __umul24((unsigned)rho, rs_d) + 16u * (phys ^ (2 * key));
+  };
+  auto issue = [&](int j, unsigned char* cs, unsigned char (*ds)[C * P * 2]) __attribute__((always_inline)) {
+    const int64_t r0 = (int64_t)b * T_ + (int64_t)j * C;
+    const bf16* csrc = Cg + (r0 * G + grp) * N;
+    const bf16* dsrc = Dg + (r0 * H + h) * P;
+#pragma unroll
+    for (int kx = 0; kx < (BINST + NWT - 1) / NWT; ++kx)
+      if (BINST % NWT == 0 || wave + NWT * kx < BINST)
+        dma_16x64_at(csrc, cc_off(wave + NWT * kx), lds_addr(cs) + (wave + NWT * kx) * 1024u);
+#pragma unroll
+    for (int kx = 0; kx < O::XINST_W; ++kx) dma_16x64_at(dsrc, cd_off(kx), lds_addr(ds[hh]) + (wv + 4 * kx) * 1024u);
+  };
+
+  // The piece's log-decays and the words holding its level weights
+  // lambda[t, c + k] (lane t, one 4-byte word each; the element's parity
+  // picks the half): wave 0 of each head.
+  const int64_t t_lo = (int64_t)b * T_ + (int64_t)lo * C;
+  const int64_t e0 = (t_lo * H + h) * L + lev;  // element of the piece's first token
+  if (wv == 0) {
+    const float* lsrc = pr.log_a + t_lo * H + h;
+    const unsigned* wsrc = static_cast<const unsigned*>(pr.lam) + (e0 >> 1);
+#pragma unroll
+    for (int kx = 0; kx < BWD_PIECE; ++kx)
+      if (kx < n) {
+        dma_4x64_at(lsrc, (unsigned)((kx * C + lane) * H) * 4u, lds_addr(&las[hh][kx * C]));
+        const unsigned wo = (unsigned)(((e0 & 1) + (int64_t)(kx * C + lane) * H * L) >> 1);
+        dma_4x64_at(wsrc, wo * 4u, lds_addr(&lws[hh][kx * C]));
+      }
+  }
+  // decays and weights of the chunk at position jp of the piece (wave 0)
+  auto weights = [&](int jp, int par) __attribute__((always_inline)) {
+    chunk_decays<bf16, C>(las[hh][jp * C + lane], cum[hh][par], ecum[hh][par], wst[hh][par], lane);
+    const unsigned wd = lws[hh][jp * C + lane];
+    const bool upper = ((e0 + (int64_t)(jp * C + lane) * H * L) & 1) != 0;
+    const float lam = __uint_as_float(upper ? (wd & 0xffff0000u) : (wd << 16));
+    wsh[hh][par][lane] = lam * ecum[hh][par][lane];
+  };
+
+  f32x4 S[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) S[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  issue(hi - 1, csh0, dsh0);
+  auto step = [&](auto cur_c, int s) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const int jp = n - 1 - s;  // position of this step's chunk in the piece
+    const unsigned char* cs = CUR ? csh1 : csh0;
+    const unsigned char* ds = CUR ? dsh1[hh] : dsh0[hh];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the chunk have landed
+    if (s == 0 && wv == 0) weights(jp, 0);  // (later chunks' are formed a step ahead)
+    lds_barrier();
+    if (s + 1 < n)  // the other buffers were released by the previous barrier
+      issue(lo + jp - 1, CUR ? csh0 : csh1, CUR ? dsh0 : dsh1);
+    if (s > 0) {
+      const float dec = M::ex(cum[hh][CUR][C - 1]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) S[nb] *= dec;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // dO rows scaled by the weights, split into hi and lo bf16 parts
+      const unsigned char* px = ds + o_xt + 32 * kt * 128;
+      const bf16x8 xt = cat8(lds_read8_tr(px), lds_read8_tr(px + 4 * 128));
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wsh[hh][CUR][32 * kt + 8 * g]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wsh[hh][CUR][32 * kt + 8 * g + 4]);
+      bf16x8 vh, vl;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float v0 = (float)xt[jj] * w0[jj], v1 = (float)xt[jj + 4] * w1[jj];
+        vh[jj] = (bf16)v0;
+        vh[jj + 4] = (bf16)v1;
+        vl[jj] = (bf16)(v0 - (float)vh[jj]);
+        vl[jj + 4] = (bf16)(v1 - (float)vh[jj + 4]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const unsigned char* pb = cs + o_bt + 32 * kt * BROW + 32 * nb;
+        const bf16x8 af = cat8(lds_read8_tr(pb), lds_read8_tr(pb + 4 * BROW));
+        S[nb] = M::mma(af, vh, S[nb]);
+        S[nb] = M::mma(af, vl, S[nb]);
+      }
+    }
+    if (s + 1 < n && wv == 0) weights(jp - 1, CUR ^ 1);
+    lds_barrier();
+  };
+  for (int s = 0; s < n; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < n) step(std::integral_constant<int, 1>{}, s + 1);
+  }
+  float* dst = bwd_pieces(k) == 1
+                   ? pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P)
+                   : pr.part_r + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wv + r] = S[nb][i];
 }
 
 // Forward-direction level states (key B, value X) without re-reading the
@@ -1536,7 +1701,11 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
     if (pr.kc >= 5)
       hipLaunchKernelGGL((bwd_zst_up_kernel<P, N>), dim3((N * P + 1023) / 1024, bh), dim3(256), 0, st, pr);
     // reverse direction: per (level, pair, piece), the pieces then reduced
-    hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh), dim3(Tl::NT), 0, st, pr);
+    constexpr bool LS2 = sizeof(T) == 2 && C == 64 && P == 64 && (N == 64 || N == 128);
+    if (LS2 && (pr.nheads / pr.ngroups) % 2 == 0)  // the output pass's shape: its layouts, heads in pairs
+      hipLaunchKernelGGL((bwd_level_state2_kernel<LS2 ? N : 128>), dim3(pr.npart, bh / 2), dim3(512), 0, st, pr);
+    else
+      hipLaunchKernelGGL((bwd_level_state_kernel<T, C, P, N, true>), dim3(pr.npart, bh), dim3(Tl::NT), 0, st, pr);
     if (pr.nstate > pr.nstate_direct)
       hipLaunchKernelGGL((bwd_level_reduce_kernel<T, P, N, true>),
                          dim3(pr.nstate - pr.nstate_direct, bh), dim3(256), 0, st, pr);
