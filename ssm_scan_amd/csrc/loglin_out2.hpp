@@ -380,7 +380,6 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
           }
           bf16x4 o4 = {(bf16)wv4[0], (bf16)wv4[1], (bf16)wv4[2], (bf16)wv4[3]};
           *reinterpret_cast<bf16x4*>(wrow + 16 * wblk) = o4;
-          __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
         }
       };
       switch (wv) {
