@@ -93,7 +93,7 @@ def test_headline_shape_lengths(T):
     check(small_cfg(T=T))
 
 
-@pytest.mark.parametrize("P,N,C", [(32, 64, 32), (64, 32, 64), (32, 128, 64), (64, 64, 32)])
+@pytest.mark.parametrize("P,N,C", [(32, 64, 32), (64, 32, 64), (32, 128, 64), (64, 64, 32), (64, 64, 64)])
 def test_bf16_shapes(P, N, C):
     check(small_cfg(T=704, H=4, G=1, P=P, N=N, C=C))
 

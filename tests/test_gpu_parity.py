@@ -60,7 +60,7 @@ def test_headline_shape_lengths(T):
 
 @pytest.mark.parametrize("dtype,P,N,C", [
     ("bf16", 16, 32, 16), ("bf16", 32, 64, 32), ("bf16", 64, 32, 64),
-    ("bf16", 16, 128, 32), ("fp32", 16, 16, 16), ("fp32", 64, 128, 64),
+    ("bf16", 16, 128, 32), ("bf16", 64, 64, 64), ("fp32", 16, 16, 16), ("fp32", 64, 128, 64),
     ("fp32", 32, 64, 32), ("fp32", 64, 16, 16),
 ])
 def test_shapes_and_chunks(dtype, P, N, C):
