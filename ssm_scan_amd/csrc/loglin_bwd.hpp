@@ -65,8 +65,8 @@ struct BwdParams {
   double* cuma;   // [batch*nheads, nc + 1] exclusive prefix sums of atot
   float* part_f;  // [batch*nheads, ceil(nc / 8), N, P] fp32, totals of the groups of 8 chunks
   float* part_r;  // [batch*nheads, npart, N, P] fp32, upper-half pieces
-  float* zst;     // [batch*nheads, nstate, N, P] fp32, lower-half sums
-  float* rst;     // [batch*nheads, nstate, N, P] fp32, upper-half sums
+  float* zst;     // [batch*nheads, nstate, N, P] lower-half sums (level-state form, below)
+  float* rst;     // [batch*nheads, nstate, N, P] upper-half sums (level-state form)
   float* term1;   // [batch*nheads, seqlen] dO_t . O_t
   float* term2;   // [batch*nheads, seqlen] X_t . dX_t
   int batch, seqlen, nheads, ngroups, nlevels;
@@ -141,46 +141,10 @@ __device__ inline void rows_load(const T* g, int64_t grs, T* lds, int tid) {
   }
 }
 
-// Level states enter the MFMAs as a pair of io-type tiles, hi = rnd(v) and
-// lo = rnd(v - hi), so that a bf16 product with them keeps about 16 bits of
-// the fp32 state.  dlog_a is a suffix sum over the whole sequence of
-// dO_t . O_t - X_t . dX_t, two terms formed through different states (the
-// lower-half state against dO, the upper-half state against B and X); with
-// the states rounded to bf16 their mismatch near every chunk boundary would
-// accumulate along the sequence.  For fp32 io the lo tile is not used.
-template <class T, int R, int W, int NT>
-__device__ inline void rows_load_split(const float* g, T* hi, T* lo, int tid) {
-  using L = Rows<T, W>;
-  constexpr int PIECES = R * L::NBLK;
-#pragma unroll
-  for (int i0 = 0; i0 < PIECES; i0 += NT) {
-    const int i = i0 + tid;
-    if (i < PIECES) {
-      const int row = i / L::NBLK, pb = i % L::NBLK;
-      const float* src = g + (int64_t)row * W + pb * L::VEC;
-      vec16_t<T> vh, vl;
-      if constexpr (sizeof(T) == 2) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          vh[q] = (bf16)a[q];
-          vh[q + 4] = (bf16)b[q];
-          vl[q] = (bf16)(a[q] - (float)vh[q]);
-          vl[q + 4] = (bf16)(b[q] - (float)vh[q + 4]);
-        }
-        store16(lo + L::at(row, pb * L::VEC), vl);
-      } else {
-        vh = *reinterpret_cast<const f32x4*>(src);
-      }
-      store16(hi + L::at(row, pb * L::VEC), vh);
-    }
-  }
-}
-
 // One chunk's state S[n][p] += sum_t key[t][n] w[t] val[t][p] for this wave's
 // 16 columns (the forward's chunk_state_mma), with w[t] val[t][p] split into
-// hi and lo bf16 fragments for bf16 io (see rows_load_split).
+// hi and lo bf16 fragments for bf16 io (the split of the level states, see
+// state_put4).
 template <class T, int C, int P, int N>
 __device__ inline void chunk_state_mma_split(const T* ks, const T* vs, const float* w, f32x4* S,
                                              int wave, int g, int r) {
@@ -355,6 +319,106 @@ __device__ inline void dlam_rows_out(const float (*dl)[LMAX], T* g, int H, int L
   }
 }
 
+// Level states (zst, rst) as the chunk passes take them: for bf16 io a pair
+// of bf16 planes, hi = rnd(v) and lo = rnd(v - hi), each [N][P], which the
+// products use as two bf16 operands, so that they keep about 16 bits of the
+// fp32 state; for fp32 io the fp32 values [N][P].  Same bytes either way;
+// element (n, p) is at n P + p.  The 16 bits matter for dlog_a: it is a
+// suffix sum over the whole sequence of dO_t . O_t - X_t . dX_t, two terms
+// formed through different states (the lower-half state against dO, the
+// upper-half state against B and X); with the states rounded to bf16 their
+// mismatch near every chunk boundary would accumulate along the sequence.
+//
+// Four consecutive elements idx .. idx + 3 of a state in that form.
+template <class T, int N, int P>
+__device__ inline void state_put4(float* st, int idx, f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16* hp = reinterpret_cast<bf16*>(st);
+    bf16x4 hv, lv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hv[e] = (bf16)v[e];
+      lv[e] = (bf16)(v[e] - (float)hv[e]);
+    }
+    *reinterpret_cast<bf16x4*>(hp + idx) = hv;
+    *reinterpret_cast<bf16x4*>(hp + N * P + idx) = lv;
+  } else {
+    *reinterpret_cast<f32x4*>(st + idx) = v;
+  }
+}
+
+// A wave's NB 16x16 tiles of a state (MFMA layout: lane (g, r) holds rows
+// 16 nb + 4 g + i, i < 4, of column col0 + r) in the level-state form.  For
+// bf16 the two lanes of a pair (r, r + 1) swap one value of each tile, so
+// that each writes two adjacent columns of two rows, four bytes a store:
+// the even lane rows 4 g and 4 g + 2, the odd lane rows 4 g + 1 and 4 g + 3.
+template <class T, int N, int P, int NB>
+__device__ inline void state_put_tiles(float* st, const f32x4* S, int col0, int g, int r) {
+  if constexpr (sizeof(T) == 2) {
+    bf16* hp = reinterpret_cast<bf16*>(st);
+    const bool odd = (r & 1) != 0;
+    const int pc = col0 + (r & ~1);  // the pair's first column
+    auto put2 = [&](int idx, float x, float y) __attribute__((always_inline)) {
+      const bf16 hx = (bf16)x, hy = (bf16)y;
+      const bf16 lx = (bf16)(x - (float)hx), ly = (bf16)(y - (float)hy);
+      *reinterpret_cast<bf16x2*>(hp + idx) = bf16x2{hx, hy};
+      *reinterpret_cast<bf16x2*>(hp + N * P + idx) = bf16x2{lx, ly};
+    };
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      // the even lane receives the odd lane's rows 0 and 2, the odd lane the
+      // even lane's rows 1 and 3
+      const float a = dpp_mov<0xb1>(odd ? S[nb][0] : S[nb][1]);
+      const float c = dpp_mov<0xb1>(odd ? S[nb][2] : S[nb][3]);
+      const int n0 = 16 * nb + 4 * g + (odd ? 1 : 0);
+      put2(n0 * P + pc, odd ? a : S[nb][0], odd ? S[nb][1] : a);
+      put2((n0 + 2) * P + pc, odd ? c : S[nb][2], odd ? S[nb][3] : c);
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[(16 * nb + 4 * g + i) * P + col0 + r] = S[nb][i];
+  }
+}
+
+// The same tiles (bf16) staged in LDS planes hl, ll ([N][P] each, the level
+// state's two planes), so that the state can go out in whole lines
+// (state_lds_out, after a barrier).
+template <int N, int P, int NB>
+__device__ inline void state_tiles_to_lds(bf16* hl, bf16* ll, const f32x4* S, int col0, int g, int r) {
+  const bool odd = (r & 1) != 0;
+  const int pc = col0 + (r & ~1);
+  auto put2 = [&](int idx, float x, float y) __attribute__((always_inline)) {
+    const bf16 hx = (bf16)x, hy = (bf16)y;
+    *reinterpret_cast<bf16x2*>(hl + idx) = bf16x2{hx, hy};
+    *reinterpret_cast<bf16x2*>(ll + idx) = bf16x2{(bf16)(x - (float)hx), (bf16)(y - (float)hy)};
+  };
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float a = dpp_mov<0xb1>(odd ? S[nb][0] : S[nb][1]);
+    const float c = dpp_mov<0xb1>(odd ? S[nb][2] : S[nb][3]);
+    const int n0 = 16 * nb + 4 * g + (odd ? 1 : 0);
+    put2(n0 * P + pc, odd ? a : S[nb][0], odd ? S[nb][1] : a);
+    put2((n0 + 2) * P + pc, odd ? c : S[nb][2], odd ? S[nb][3] : c);
+  }
+}
+// The staged planes out as one level state, 16 bytes a thread (NTH threads,
+// thread index t).
+template <int N, int P, int NTH>
+__device__ inline void state_lds_out(float* st, const bf16* hl, const bf16* ll, int t) {
+  constexpr int PP = N * P / 8;  // 16-byte pieces per plane
+  bf16* hp = reinterpret_cast<bf16*>(st);
+#pragma unroll
+  for (int i0 = 0; i0 < 2 * PP; i0 += NTH) {
+    const int i = i0 + t;
+    if ((2 * PP) % NTH == 0 || i < 2 * PP) {
+      const int plane = i / PP, off = (i % PP) * 8;
+      store16(hp + plane * (N * P) + off, load16((plane ? ll : hl) + off));
+    }
+  }
+}
+
 // ------------------------------------------------------------ launch 2
 
 // grid (npart, batch*nheads).  Wave w owns state columns [16 w, 16 w + 16)
@@ -436,13 +500,16 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_level_state_kerne
     chunk_state_mma_split<T, C, P, N>(ksh, vsh, wsh, S, wave, g, r);
     lds_barrier();  // the next chunk restages the tiles
   }
-  float* dst = bwd_pieces(k) == 1
-                   ? (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P)
-                   : (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
+  if (bwd_pieces(k) == 1) {  // the level's state itself
+    float* dst = (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P);
+    state_put_tiles<T, N, P, Tl::NB>(dst, S, 16 * wave, g, r);
+  } else {  // an fp32 partial for the reduce
+    float* dst = (REV ? pr.part_r : pr.part_f) + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
 #pragma unroll
-  for (int nb = 0; nb < Tl::NB; ++nb)
+    for (int nb = 0; nb < Tl::NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wave + r] = S[nb][i];
+      for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wave + r] = S[nb][i];
+  }
 }
 
 // The reverse-direction pieces for the output pass's shape (bf16, 64-token
@@ -600,13 +667,20 @@ __global__ __launch_bounds__(512, 2) void bwd_level_state2_kernel(BwdParams pr) 
     step(std::integral_constant<int, 0>{}, s);
     if (s + 1 < n) step(std::integral_constant<int, 1>{}, s + 1);
   }
-  float* dst = bwd_pieces(k) == 1
-                   ? pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P)
-                   : pr.part_r + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
+  if (bwd_pieces(k) == 1) {  // the level's state itself, through LDS (the last barrier freed it)
+    float* dst = pr.rst + ((int64_t)bh * pr.nstate + bwd_state_index(pr.nc, k, pair)) * (N * P);
+    bf16* hl = reinterpret_cast<bf16*>(hh ? &dsh0[0][0] : csh0);
+    bf16* ll = reinterpret_cast<bf16*>(hh ? &dsh1[0][0] : csh1);
+    state_tiles_to_lds<N, P, NB>(hl, ll, S, 16 * wv, g, r);
+    lds_barrier();
+    state_lds_out<N, P, 256>(dst, hl, ll, 64 * wv + lane);
+  } else {  // an fp32 partial for the reduce
+    float* dst = pr.part_r + ((int64_t)bh * pr.npart + blockIdx.x) * (N * P);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wv + r] = S[nb][i];
+      for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wv + r] = S[nb][i];
+  }
 }
 
 // Forward-direction level states (key B, value X) without re-reading the
@@ -631,6 +705,8 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(
   __shared__ __attribute__((aligned(16))) T ksh[C * N];
   __shared__ __attribute__((aligned(16))) T vsh[C * P];
   __shared__ __attribute__((aligned(16))) float cum[64], ecum[64], wst[64];
+  // a level state on its way out (bf16 io: its two planes)
+  __shared__ __attribute__((aligned(16))) bf16 zs_hi[sizeof(T) == 2 ? N * P : 8], zs_lo[sizeof(T) == 2 ? N * P : 8];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y, H = pr.nheads, G = pr.ngroups;
@@ -639,7 +715,18 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(
   const int g8 = blockIdx.x, c0 = 8 * g8, c1 = min(c0 + 8, pr.nc);
   const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
   float* zst = pr.zst + (int64_t)bh * pr.nstate * (N * P);
+  // a level state (uniform call: a barrier inside; at most one per chunk, and
+  // the loop's barriers separate one from the next)
   auto put = [&](float* dst, const f32x4* S) __attribute__((always_inline)) {
+    if constexpr (sizeof(T) == 2) {
+      state_tiles_to_lds<N, P, NB>(zs_hi, zs_lo, S, 16 * wave, g, r);
+      lds_barrier();
+      state_lds_out<N, P, NT>(dst, zs_hi, zs_lo, tid);
+    } else {
+      state_put_tiles<T, N, P, NB>(dst, S, 16 * wave, g, r);
+    }
+  };
+  auto put_f32 = [&](float* dst, const f32x4* S) __attribute__((always_inline)) {  // a group total
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -674,7 +761,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(
     for (int e = 0; e < 4; ++e) {
       if (!open) continue;
       if (e == 3) {  // the whole group (i = 7): lower half of level 4 when even
-        if (pr.kc >= 5) put(pr.part_f + ((int64_t)bh * ((pr.nc + 7) >> 3) + g8) * (N * P), cur);
+        if (pr.kc >= 5) put_f32(pr.part_f + ((int64_t)bh * ((pr.nc + 7) >> 3) + g8) * (N * P), cur);
         if (!(g8 & 1) && (g8 >> 1) < bwd_pairs(pr.nc, 4))
           put(zst + (int64_t)bwd_state_index(pr.nc, 4, g8 >> 1) * (N * P), cur);
         open = false;
@@ -699,7 +786,7 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(
 // Each thread owns four consecutive state elements of every block; the
 // totals of 16 groups are loaded at a time.
 constexpr int BWD_UP_DEPTH = 24;  // group levels: chunk levels up to 27
-template <int P, int N>
+template <class T, int P, int N>
 __global__ __launch_bounds__(256) void bwd_zst_up_kernel(BwdParams pr) {
   constexpr int D = BWD_UP_DEPTH, U = 16;
   const int bh = blockIdx.y;
@@ -708,7 +795,7 @@ __global__ __launch_bounds__(256) void bwd_zst_up_kernel(BwdParams pr) {
   const int ng = pr.nc >> 3;  // full groups
   const float* gt = pr.part_f + (int64_t)bh * ((pr.nc + 7) >> 3) * (N * P) + e4;
   const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
-  float* zst = pr.zst + (int64_t)bh * pr.nstate * (N * P) + e4;
+  float* zst = pr.zst + (int64_t)bh * pr.nstate * (N * P);
   f32x4 stk[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) stk[e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -729,7 +816,7 @@ __global__ __launch_bounds__(256) void bwd_zst_up_kernel(BwdParams pr) {
         if (e < z) cur = __expf((float)(ca[8 * (q + 1)] - ca[8 * (q + 1 - (1 << e))])) * stk[e] + cur;
       const int k = z + 4, pair = (8 * (q + 1 - (1 << z))) >> k;
       if (z >= 1 && k <= pr.kc && pair < bwd_pairs(pr.nc, k))
-        *reinterpret_cast<f32x4*>(zst + (int64_t)bwd_state_index(pr.nc, k, pair) * (N * P)) = cur;
+        state_put4<T, N, P>(zst + (int64_t)bwd_state_index(pr.nc, k, pair) * (N * P), e4, cur);
 #pragma unroll
       for (int e = 0; e < D; ++e)
         if (e == z) stk[e] = cur;
@@ -779,7 +866,7 @@ __global__ __launch_bounds__(256) void bwd_level_reduce_kernel(BwdParams pr) {
   float* dst = (REV ? pr.rst : pr.zst) + ((int64_t)bh * pr.nstate + sidx) * (N * P);
 #pragma unroll
   for (int q = 0; q < EPT; ++q)
-    if (q * 256 + tid < Q4) store4(dst + (q * 256 + tid) * 4, acc[q]);
+    if (q * 256 + tid < Q4) state_put4<T, N, P>(dst, (q * 256 + tid) * 4, acc[q]);
 }
 
 // ------------------------------------------------------------ launches 4, 5
@@ -856,22 +943,30 @@ __device__ inline void bwd_intra_scores(const T* csh, const T* bsh, const T* xsh
   }
 }
 
-// A level state (fp32 [N][P], row-major) prefetched into registers, then
-// stored to LDS as the hi / lo pair of rows_load_split.
+// A level state (the form of state_put4) prefetched into registers, then
+// stored to LDS as the hi and lo tiles the products read.
 template <class T, int N, int P, int NT>
 struct StateStage {
   using L = Rows<T, P>;
   static constexpr int PIECES = N * L::NBLK;  // 16-byte io-type pieces
   static constexpr int IT = (PIECES + NT - 1) / NT;
   static constexpr int F4 = L::VEC / 4;  // float4 per piece
+  // bf16: the hi and lo pieces of the level state's two planes; fp32: the
+  // values (see state_put4)
   f32x4 v[IT][F4];
   __device__ inline void load(const float* g, int tid) {  // unconditional: see RowsStage
 #pragma unroll
     for (int q = 0; q < IT; ++q) {
       const int i = PIECES % NT == 0 ? q * NT + tid : min(q * NT + tid, PIECES - 1);
-      const float* src = g + (int64_t)(i / L::NBLK) * P + (i % L::NBLK) * L::VEC;
+      if constexpr (sizeof(T) == 2) {
+        const bf16* hp = reinterpret_cast<const bf16*>(g) + (int64_t)i * L::VEC;
+        v[q][0] = *reinterpret_cast<const f32x4*>(hp);
+        v[q][1] = *reinterpret_cast<const f32x4*>(hp + N * P);
+      } else {
+        const float* src = g + (int64_t)(i / L::NBLK) * P + (i % L::NBLK) * L::VEC;
 #pragma unroll
-      for (int f = 0; f < F4; ++f) v[q][f] = *reinterpret_cast<const f32x4*>(src + 4 * f);
+        for (int f = 0; f < F4; ++f) v[q][f] = *reinterpret_cast<const f32x4*>(src + 4 * f);
+      }
     }
   }
   __device__ inline void store(T* hi, T* lo, int tid) const {
@@ -881,15 +976,8 @@ struct StateStage {
       if (i < PIECES) {
         const int o = L::at(i / L::NBLK, (i % L::NBLK) * L::VEC);
         if constexpr (sizeof(T) == 2) {
-          bf16x8 h, l;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = v[q][e >> 2][e & 3];
-            h[e] = (bf16)x;
-            l[e] = (bf16)(x - (float)h[e]);
-          }
-          store16(hi + o, h);
-          store16(lo + o, l);
+          store16(hi + o, __builtin_bit_cast(bf16x8, v[q][0]));
+          store16(lo + o, __builtin_bit_cast(bf16x8, v[q][1]));
         } else {
           store16(hi + o, v[q][0]);
         }
@@ -1699,7 +1787,7 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
     // 8 chunks, then the levels above from the groups' totals
     hipLaunchKernelGGL((bwd_zst_group_kernel<T, C, P, N>), dim3((pr.nc + 7) / 8, bh), dim3(Tl::NT), 0, st, pr);
     if (pr.kc >= 5)
-      hipLaunchKernelGGL((bwd_zst_up_kernel<P, N>), dim3((N * P + 1023) / 1024, bh), dim3(256), 0, st, pr);
+      hipLaunchKernelGGL((bwd_zst_up_kernel<T, P, N>), dim3((N * P + 1023) / 1024, bh), dim3(256), 0, st, pr);
     // reverse direction: per (level, pair, piece), the pieces then reduced
     constexpr bool LS2 = sizeof(T) == 2 && C == 64 && P == 64 && (N == 64 || N == 128);
     if (LS2 && (pr.nheads / pr.ngroups) % 2 == 0)  // the output pass's shape: its layouts, heads in pairs
