@@ -598,7 +598,7 @@ __global__ __launch_bounds__(256, 2) void output2_kernel(Params pr) {
 // [16 (w mod 4), +16), all N rows.  The heads share one copy of the B rows.
 // The segment's log-decays are copied once, up front, and each chunk's
 // decays are formed while the chunk before it is being reduced; the states
-// go out through LDS in whole rows, 16 bytes a lane.
+// go out through LDS, whole 128-byte lines at a time.
 // What it computes is state_kernel's (loglin_device.hpp): each segment's
 // state, decayed to the segment's end, in natural row order, and the
 // segment's log-decay.
