@@ -780,162 +780,6 @@ __global__ __launch_bounds__((Tiles<T, C, P, N>::NT)) void bwd_zst_group_kernel(
   }
 }
 
-// The same walk for the output pass's shape (bf16, 64-token chunks, P = 64,
-// N = 64 or 128) in that pass's LDS layouts, two heads of a group per
-// work-group sharing one copy of the B rows (as bwd_level_state2_kernel):
-// eight waves, wave w serving head w / 4 and its state columns
-// [16 (w mod 4), +16).  grid (ceil(nc / 8), batch*nheads / 2).
-template <int N>
-__global__ __launch_bounds__(512) void bwd_zst_group2_kernel(BwdParams pr) {
-  using O = Out2<N>;
-  using M = Mfma<bf16>;
-  constexpr int C = O::C, P = O::P, NB = O::NB, BROW = O::BROW, BBLK = O::BBLK, BINST = O::BINST;
-  constexpr int NWT = 8;
-  __shared__ __attribute__((aligned(16))) unsigned char bsh0[C * BROW];
-  __shared__ __attribute__((aligned(16))) unsigned char bsh1[C * BROW];
-  __shared__ __attribute__((aligned(16))) unsigned char xsh0[2][C * P * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char xsh1[2][C * P * 2];
-  // per head: the group's log-decays, and the chunk decays by chunk parity
-  __shared__ __attribute__((aligned(16))) float las[2][8 * C];
-  __shared__ __attribute__((aligned(16))) float cum[2][2][C], ecum[2][2][C], wst[2][2][C];
-  // per head: a level state on its way out, its hi and lo planes
-  __shared__ __attribute__((aligned(16))) bf16 zs[2][2][N * P];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __builtin_assume(wave >= 0 && wave < NWT);
-  const int hh = wave >> 2, wv = wave & 3;
-  const int g = lane >> 4, r = lane & 15;
-  const int H = pr.nheads, G = pr.ngroups;
-  const int b = blockIdx.y / (H / 2), h0 = 2 * (blockIdx.y % (H / 2));
-  const int h = h0 + hh, grp = h0 / (H / G);
-  const int bh = b * H + h;
-  const int64_t T_ = pr.seqlen;
-  const int g8 = blockIdx.x, c0 = 8 * g8, c1 = min(c0 + 8, pr.nc), n = c1 - c0;
-  const double* ca = pr.cuma + (int64_t)bh * (pr.nc + 1);
-  float* zst = pr.zst + (int64_t)bh * pr.nstate * (N * P);
-  const bf16* Bg = static_cast<const bf16*>(pr.Bm);
-  const bf16* Xg = static_cast<const bf16*>(pr.X);
-
-  // B^T and X^T transposing reads (as state2_kernel)
-  const unsigned o_bt = (8 * g + (r >> 2)) * BROW + 8 * (r & 3);
-  const int keyx = ((r >> 3) & 1) | ((g & 1) << 1);
-  const unsigned o_xt = (8 * g + (r >> 2)) * 128 + 16 * ((2 * wv + ((r & 3) >> 1)) ^ (2 * keyx)) +
-                        8 * (r & 1);
-  const unsigned rs_b = (unsigned)G * N * 2, rs_x = (unsigned)H * P * 2;
-  auto cb_off = [&](int inst) __attribute__((always_inline)) {
-    const unsigned pos = (unsigned)(inst * 64 + lane);
-    const unsigned rho = pos / BBLK;
-    const unsigned blk = min(pos - rho * BBLK, (unsigned)(BBLK - 2));
-    return __umul24(rho, rs_b) + 16u * blk;
-  };
-  auto cx_off = [&](int kx) __attribute__((always_inline)) {
-    const int pos = (wv + 4 * kx) * 64 + lane;
-    const int rho = pos >> 3, phys = pos & 7;
-    const int key = ((rho >> 1) & 1) | (((rho >> 3) & 1) << 1);
-    return __umul24((unsigned)rho, rs_x) + 16u * (phys ^ (2 * key));
-  };
-  auto issue = [&](int j, unsigned char* bs, unsigned char (*xs)[C * P * 2]) __attribute__((always_inline)) {
-    const int64_t r0 = (int64_t)b * T_ + (int64_t)j * C;
-    const bf16* bsrc = Bg + (r0 * G + grp) * N;
-    const bf16* xsrc = Xg + (r0 * H + h) * P;
-#pragma unroll
-    for (int kx = 0; kx < (BINST + NWT - 1) / NWT; ++kx)
-      if (BINST % NWT == 0 || wave + NWT * kx < BINST)
-        dma_16x64_at(bsrc, cb_off(wave + NWT * kx), lds_addr(bs) + (wave + NWT * kx) * 1024u);
-#pragma unroll
-    for (int kx = 0; kx < O::XINST_W; ++kx) dma_16x64_at(xsrc, cx_off(kx), lds_addr(xs[hh]) + (wv + 4 * kx) * 1024u);
-  };
-  if (wv == 0) {  // the group's log-decays of this head
-    const float* lsrc = pr.log_a + ((int64_t)b * T_ + (int64_t)c0 * C) * H + h;
-#pragma unroll
-    for (int kx = 0; kx < 8; ++kx)
-      if (kx < n) dma_4x64_at(lsrc, (unsigned)((kx * C + lane) * H) * 4u, lds_addr(&las[hh][kx * C]));
-  }
-  // a level state (uniform call: a barrier inside; at most one per chunk, and
-  // the loop's barriers separate one from the next)
-  auto put = [&](float* dst, const f32x4* S) __attribute__((always_inline)) {
-    state_tiles_to_lds<N, P, NB>(zs[hh][0], zs[hh][1], S, 16 * wv, g, r);
-    lds_barrier();
-    state_lds_out<N, P, 256>(dst, zs[hh][0], zs[hh][1], 64 * wv + lane);
-  };
-  auto put_f32 = [&](float* dst, const f32x4* S) __attribute__((always_inline)) {  // a group total
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * nb + 4 * g + i) * P + 16 * wv + r] = S[nb][i];
-  };
-
-  f32x4 stk[3][NB];  // left blocks of 1, 2 and 4 chunks waiting for their siblings
-  issue(c0, bsh0, xsh0);
-  auto step = [&](auto cur_c, int i) __attribute__((always_inline)) {
-    constexpr int CUR = decltype(cur_c)::value;
-    const int c = c0 + i;
-    const unsigned char* bs = CUR ? bsh1 : bsh0;
-    const unsigned char* xs = CUR ? xsh1[hh] : xsh0[hh];
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the chunk have landed
-    if (i == 0 && wv == 0) chunk_decays<bf16, C>(las[hh][lane], cum[hh][0], ecum[hh][0], wst[hh][0], lane);
-    lds_barrier();
-    if (i + 1 < n) issue(c + 1, CUR ? bsh0 : bsh1, CUR ? xsh0 : xsh1);
-    f32x4 cur[NB];  // this chunk's state, decayed to its end
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) cur[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // X rows scaled by the decay to the chunk end, split into hi and lo
-      const unsigned char* px = xs + o_xt + 32 * kt * 128;
-      const bf16x8 xt = cat8(lds_read8_tr(px), lds_read8_tr(px + 4 * 128));
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wst[hh][CUR][32 * kt + 8 * g]);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wst[hh][CUR][32 * kt + 8 * g + 4]);
-      bf16x8 vh, vl;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float v0 = (float)xt[jj] * w0[jj], v1 = (float)xt[jj + 4] * w1[jj];
-        vh[jj] = (bf16)v0;
-        vh[jj + 4] = (bf16)v1;
-        vl[jj] = (bf16)(v0 - (float)vh[jj]);
-        vl[jj + 4] = (bf16)(v1 - (float)vh[jj + 4]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const unsigned char* pb = bs + o_bt + 32 * kt * BROW + 32 * nb;
-        const bf16x8 af = cat8(lds_read8_tr(pb), lds_read8_tr(pb + 4 * BROW));
-        cur[nb] = M::mma(af, vh, cur[nb]);
-        cur[nb] = M::mma(af, vl, cur[nb]);
-      }
-    }
-    if (i + 1 < n && wv == 0)
-      chunk_decays<bf16, C>(las[hh][(i + 1) * C + lane], cum[hh][CUR ^ 1], ecum[hh][CUR ^ 1], wst[hh][CUR ^ 1],
-                            lane);
-    lds_barrier();  // the chunk's tiles are released; the next chunk's decays are in place
-    bool open = true;  // uniform
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!open) continue;
-      if (e == 3) {  // the whole group (i = 7): lower half of level 4 when even
-        if (pr.kc >= 5) put_f32(pr.part_f + ((int64_t)bh * ((pr.nc + 7) >> 3) + g8) * (N * P), cur);
-        if (!(g8 & 1) && (g8 >> 1) < bwd_pairs(pr.nc, 4))
-          put(zst + (int64_t)bwd_state_index(pr.nc, 4, g8 >> 1) * (N * P), cur);
-        open = false;
-      } else if (!((i >> e) & 1)) {  // a left block: lower half of level e + 1
-        const int k = e + 1, pair = c >> k;
-        if (pair < bwd_pairs(pr.nc, k)) put(zst + (int64_t)bwd_state_index(pr.nc, k, pair) * (N * P), cur);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) stk[e][nb] = cur[nb];
-        open = false;
-      } else {  // a right block: its left sibling, decayed across it, folds in
-        const float dec = __expf((float)(ca[c + 1] - ca[c + 1 - (1 << e)]));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) cur[nb] = dec * stk[e][nb] + cur[nb];
-      }
-    }
-  };
-  for (int i = 0; i < n; i += 2) {
-    step(std::integral_constant<int, 0>{}, i);
-    if (i + 1 < n) step(std::integral_constant<int, 1>{}, i + 1);
-  }
-}
-
 // grid (N P / 1024, batch*nheads), 256 threads: the lower halves of chunk
 // levels 5 and up, by the same walk over the full groups' totals (a block
 // of 2^z groups completed at group q is the lower half of level z + 4).
@@ -1941,12 +1785,7 @@ int launch_backward(const BwdParams& pr, hipStream_t st) {
   if (pr.npart > 0) {
     // forward direction: blocks of the chunk states, levels 1-4 per group of
     // 8 chunks, then the levels above from the groups' totals
-    constexpr bool OUT2S = sizeof(T) == 2 && C == 64 && P == 64 && (N == 64 || N == 128);
-    if (OUT2S && (pr.nheads / pr.ngroups) % 2 == 0)  // the output pass's shape: its layouts, heads in pairs
-      hipLaunchKernelGGL((bwd_zst_group2_kernel<OUT2S ? N : 128>), dim3((pr.nc + 7) / 8, bh / 2), dim3(512), 0, st,
-                         pr);
-    else
-      hipLaunchKernelGGL((bwd_zst_group_kernel<T, C, P, N>), dim3((pr.nc + 7) / 8, bh), dim3(Tl::NT), 0, st, pr);
+    hipLaunchKernelGGL((bwd_zst_group_kernel<T, C, P, N>), dim3((pr.nc + 7) / 8, bh), dim3(Tl::NT), 0, st, pr);
     if (pr.kc >= 5)
       hipLaunchKernelGGL((bwd_zst_up_kernel<T, P, N>), dim3((N * P + 1023) / 1024, bh), dim3(256), 0, st, pr);
     // reverse direction: per (level, pair, piece), the pieces then reduced
