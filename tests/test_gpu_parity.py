@@ -71,6 +71,13 @@ def test_batch_gt_one():
     check(small_cfg(T=512, H=4, G=2, Bt=3))
 
 
+@pytest.mark.parametrize("seg", [None, 0])
+def test_batch_segments(seg):
+    """Two sequences long enough for the state pass and the level scan
+    (5 segments of 8 chunks, or 40 one-chunk segments in three ranges)."""
+    check(small_cfg(T=64 * 40, H=4, G=2, Bt=2), seg_log2=seg, variant="slow_decay")
+
+
 @pytest.mark.parametrize("variant", ["slow_decay", "no_decay", "lam_intra", "lam_inter",
                                      "lam_ones"])
 def test_variants(variant):
