@@ -121,6 +121,12 @@ def test_group_of_four_heads_and_batch():
     check(small_cfg(T=512, H=8, G=2, Bt=2))
 
 
+def test_batch_long_levels():
+    """Two sequences of 40 chunks: chunk levels 1-6, the upper ones in
+    several pieces (the reduce) and above the groups of 8 (the group walk)."""
+    check(small_cfg(T=64 * 40, H=4, G=2, Bt=2), variant="slow_decay")
+
+
 def test_extra_levels_are_zero():
     check(small_cfg(T=320, H=2, G=1), extra_levels=3)
 
