@@ -70,6 +70,13 @@ def test_decode_variants(variant):
     check_decode(small_cfg(T=300, H=2, G=1), variant=variant)
 
 
+@pytest.mark.parametrize("variant", ["slow_decay", "slow_decay+lam_onehot_10"])
+def test_decode_long_context(variant):
+    """2100 steps: buckets up to level 12 occupied, with weight (slow decay),
+    and a deep level alone (one-hot level weights)."""
+    check_decode(small_cfg(T=2100, H=2, G=1), variant=variant)
+
+
 def test_decode_batch_and_matches_forward():
     """Batch of 3; the decode outputs agree with the chunked forward's."""
     cfg = small_cfg(T=256, H=4, G=2, Bt=3)
