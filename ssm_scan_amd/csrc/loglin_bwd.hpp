@@ -1300,7 +1300,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
       }
     }
     const int lv = c_log + k;
-    const float gk = gap_s[k];
+    const float egk = M::ex(gap_s[k]);  // e^(gap + Lambda_t) = e^gap e^(Lambda_t): one exponential per level
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       const int tw = 16 * (RPW * rg + rr);
@@ -1308,7 +1308,7 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = tw + 4 * g + i;
-        const float wt = M::ex(cum[t] + gk);
+        const float wt = ecum[t] * egk;
         float pt = 0.f;
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
@@ -1605,13 +1605,13 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dkv_kernel(BwdParams
         }
       }
     }
-    const float gk = gap_s[k];
+    const float egk = M::ex(gap_s[k]);  // e^(decay s -> chunk end + gap) as a product: one exponential per level
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * (RPW * rg + rr) + 4 * g + i;
-        const float w = M::ex(cum[C - 1] - cum[s] + gk);
+        const float w = wst[s] * egk;
 #pragma unroll
         for (int q = 0; q < PBW; ++q) dxe[rr][q][i] += w * tx[rr][q][i];
 #pragma unroll
