@@ -1097,8 +1097,10 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   const int H = pr.nheads, G = pr.ngroups, L = pr.nlevels;
   const int64_t T_ = pr.seqlen;
   const ChunkTiles ct(pr.batch * G * pr.nc);
-  // lambda rows: every level the sequence reaches (ll <= BWD_LMAX)
-  constexpr int LIT = (C * BWD_LMAX + NT - 1) / NT;
+  // lambda rows: every level the sequence reaches (ll <= BWD_LMAX), one
+  // register per (row, level slot) of the BWD_LMAX-wide rows (NT = 8 C)
+  constexpr int LIT = C * BWD_LMAX / NT;
+  static_assert(C * BWD_LMAX % NT == 0, "whole rows of level slots per thread");
   const int ll = pr.ll;
   RowsStage<T, C, N, NT> sc, sb;
   RowsStage<T, C, P, NT> sx, so;
@@ -1119,10 +1121,10 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
     so.load(static_cast<const T*>(pr.dO) + (((int64_t)b * T_ + t0) * H + h) * P, (int64_t)H * P, tid);
     const T* lg = static_cast<const T*>(pr.lam) + (((int64_t)b * T_ + t0) * H + h) * L;
 #pragma unroll
-    for (int q = 0; q < LIT; ++q) {
+    for (int q = 0; q < LIT; ++q) {  // element i: row i / BWD_LMAX, level i mod BWD_LMAX
       const int i = q * NT + tid;
-      const int ic = min(i, C * ll - 1);  // unconditional (see RowsStage)
-      lv_[q] = lg[(int64_t)(ic / ll) * H * L + ic % ll];
+      const int l = min(i % BWD_LMAX, ll - 1);  // unconditional (see RowsStage): levels past ll repeat the last
+      lv_[q] = lg[(int64_t)(i / BWD_LMAX) * H * L + l];
     }
     la = pr.log_a[((int64_t)b * T_ + t0 + min(tid, C - 1)) * H + h];
     // level k's gap (lane k - 1): log-decay from the end of the lower half
@@ -1153,10 +1155,10 @@ __global__ __launch_bounds__(bwd_chunk_threads(C)) void bwd_dq_kernel(BwdParams 
   so.store(osh, tid);
 #pragma unroll
   for (int q = 0; q < LIT; ++q) {
-    const int i = q * NT + tid;
-    if (i < C * ll) {
-      lam_s[i / ll][i % ll] = to_f(lv_[q]);
-      dlam_s[i / ll][i % ll] = 0.f;
+    const int i = q * NT + tid, row = i / BWD_LMAX, l = i % BWD_LMAX;
+    if (l < ll) {
+      lam_s[row][l] = to_f(lv_[q]);
+      dlam_s[row][l] = 0.f;
     }
   }
   if (tid < pr.kc) gap_s[tid + 1] = gap;
